@@ -1,0 +1,205 @@
+/*
+ * kvfp4.h - C ABI of the paged NVFP4 KV-cache library for AMD MI355X (gfx950).
+ *
+ * Four calls, all asynchronous on a caller-given HIP stream:
+ *   kv_quantize_append   fp16/bf16 K/V rows -> packed E2M1 + E4M3 block scales
+ *                        in paged NHD/HND caches addressed by a CSR page table
+ *   kv_dequantize_paged  paged NVFP4 -> contiguous [B, T, H, D] fp16/bf16
+ *   kv_materialize_fp8   active pages -> float8_e4m3fn page copy + block table
+ *   kv_global_scale      per-tensor global decode scale amax / (6 * e4m3_max)
+ *
+ * Sources (FlashInfer 0.7.4 documentation): the API pages
+ * flashinfer.page.nvfp4_quantize_append_paged_kv_cache,
+ * flashinfer.quantization.nvfp4_kv_dequantize_paged and
+ * flashinfer.quantization.kernels.nvfp4_kv_materialize.nvfp4_kv_materialize_fp8,
+ * and the flashinfer.quantization module page (sections "NVFP4 4over6
+ * Recipes", "FP4 KV Cache Quantization", "NVFP4 KV Cache Materialization" with
+ * NVFP4KVMaterializer.run()).
+ *
+ * Formats: E2M1 codes (OCP FP4: sign bit 3, magnitudes 0, .5, 1, 1.5, 2, 3, 4,
+ * 6), two per byte, the even element in the low nibble; E4M3 block scales
+ * (OCP float8_e4m3fn bytes), one per 16 consecutive elements of head_dim.
+ * A decoded value is e2m1 * block_scale * global_scale.
+ *
+ * Ownership and threading: every buffer pointer is device memory owned by the
+ * caller and must stay valid until the work queued on `stream` completes.
+ * The library never allocates, frees or synchronizes; it only launches
+ * kernels on `stream` (a hipStream_t passed as void*, NULL = the null
+ * stream), so every call can be captured in a HIP graph. Calls keep no state
+ * between them and may be made from several host threads.
+ *
+ * Errors: each call returns a status. Every argument check runs before any
+ * launch, so a call that returns an error has queued nothing and written
+ * nothing. Tensor *values* (page ids, positions, lengths, indptr entries) are
+ * not checked, as on the pages; out-of-range values are undefined behaviour.
+ * KVFP4_ELAUNCH reports a HIP launch failure (for instance a device that is
+ * not gfx950).
+ */
+#ifndef KVFP4_H
+#define KVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvfp4_status_t;
+enum {
+    KVFP4_OK = 0,
+    KVFP4_EINVAL = 1,        /* null pointer, bad enum, bad extent or scale */
+    KVFP4_EALIGN = 2,        /* a base pointer or stride is not 16-byte aligned */
+    KVFP4_EUNSUPPORTED = 3,  /* a valid request this build does not implement */
+    KVFP4_ELAUNCH = 4        /* the HIP runtime refused a launch */
+};
+
+enum { KVFP4_NHD = 0, KVFP4_HND = 1 };                /* cache layouts */
+enum { KVFP4_F16 = 0, KVFP4_BF16 = 1 };               /* 16-bit float types */
+enum { KVFP4_I32 = 0, KVFP4_I64 = 1 };                /* block-table index types */
+enum { KVFP4_ERR_MSE = 0, KVFP4_ERR_MAE = 1 };        /* 4over6 error metrics */
+
+/*
+ * 4over6 block-scale recipe (module page, "NVFP4 4over6 Recipes",
+ * NVFP44Over6Config): for every 16-element block the quantizer forms the
+ * amax/6 scale (clamped at e4m3_max) and the 1.5x tighter amax/4 scale
+ * (clamped at 448), quantizes and dequantizes with both, and keeps amax/4
+ * only when its summed error (err_mode: squared or absolute, evaluated in
+ * fp32, pairwise tree over the 16 elements) is strictly lower.
+ * A NULL recipe pointer selects standard NVFP4: amax/6 clamped at 448.
+ *   e4m3_max           a finite E4M3 value in (0, 448]; 256 is the page's knob
+ *   err_mode           KVFP4_ERR_MSE or KVFP4_ERR_MAE
+ *   err_use_fast_math  must be 0: the fp16 error recipe is not implemented
+ *                      (KVFP4_EUNSUPPORTED)
+ */
+typedef struct {
+    float e4m3_max;
+    int32_t err_mode;
+    int32_t err_use_fast_math;
+} kvfp4_recipe_t;
+
+/*
+ * A paged NVFP4 cache (append and dequantize pages: paged_kv_cache and
+ * kv_cache_sf, "tuple or stacked" format). Per page, the data holds
+ * [page_size, num_kv_heads, head_dim/2] bytes (NHD) or
+ * [num_kv_heads, page_size, head_dim/2] (HND), compact inside the page; the
+ * scales the same with head_dim/16 bytes per row. Page p of K data starts at
+ * k_data + p * k_page_stride, and likewise for the other three. A tuple cache
+ * passes two allocations; a stacked 5-D cache [pages, 2, ...] passes
+ * v = k + page bytes and strides of twice the page bytes. Strides are in bytes
+ * and may exceed the compact page (padded pages). The data bases and data
+ * page strides must be multiples of 16 bytes (the launchers on the pages check
+ * 16-byte alignment); scale bases and strides have no alignment requirement.
+ */
+typedef struct {
+    void *k_data, *v_data;            /* uint8 packed E2M1 */
+    void *k_sf, *v_sf;                /* uint8 E4M3 block scales, linear layout */
+    int64_t k_page_stride, v_page_stride;        /* bytes */
+    int64_t k_sf_page_stride, v_sf_page_stride;  /* bytes */
+    int32_t num_pages;                /* pages addressable through each base */
+    int32_t page_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;                 /* multiple of 16 */
+    int32_t layout;                   /* KVFP4_NHD or KVFP4_HND */
+} kvfp4_paged_cache_t;
+
+/*
+ * kv_quantize_append - nvfp4_quantize_append_paged_kv_cache.
+ * Quantizes nnz rows of append_key / append_value ([nnz, num_kv_heads,
+ * head_dim] contiguous, in_dtype KVFP4_F16/KVFP4_BF16, 16-byte aligned) and
+ * writes them in place into `cache`: row r belongs to request
+ * b = batch_indices[r] at logical position p = positions[r]; its page is
+ * kv_indices[kv_indptr[b] + p / page_size] and its slot p % page_size.
+ * kv_indptr has batch_size + 1 entries, kv_last_page_len batch_size entries
+ * (the space must already be reserved, as the page's note requires; the
+ * table is not modified). All index arrays are int32 device arrays.
+ * k_scale / v_scale are the positive finite global decode scales (host
+ * floats). Only the addressed code and scale bytes change. recipe: NULL for
+ * standard NVFP4, else a 4over6 recipe (the page lists no recipe argument for
+ * this call; every other NVFP4 entry point takes one, so it is accepted here).
+ * Rows with equal (b, p) race. nnz == 0 is a no-op.
+ * append_key / append_value must be 16-byte aligned.
+ */
+kvfp4_status_t kv_quantize_append(const kvfp4_paged_cache_t *cache,
+                                  const void *append_key, const void *append_value,
+                                  int32_t in_dtype, int64_t nnz,
+                                  const int32_t *batch_indices, const int32_t *positions,
+                                  const int32_t *kv_indices, const int32_t *kv_indptr,
+                                  const int32_t *kv_last_page_len, int32_t batch_size,
+                                  float k_scale, float v_scale,
+                                  const kvfp4_recipe_t *recipe, void *stream);
+
+/*
+ * kv_dequantize_paged - nvfp4_kv_dequantize_paged.
+ * For every request b < batch_size and position t < min(seq_lens[b],
+ * max_seq_len): page = block_tables[b * bt_row_stride + t / page_size]
+ * (int32 or int64 per bt_dtype), slot t % page_size, and for every head h and
+ * element e: output[b, t, h, e] = RNE_16(fp32(fp32(E4M3(s) * g) * e2m1(c)))
+ * with g = *k_scale for output_k and *v_scale for output_v (device fp32
+ * scalars). Outputs are caller-owned contiguous [batch_size, max_seq_len,
+ * num_kv_heads, head_dim] fp16/bf16 (out_dtype), 16-byte aligned. Positions
+ * t >= seq_lens[b] are left unchanged. bt_cols is the number of columns of
+ * the table (each row needs ceil(min(seq_len, max_seq_len) / page_size)).
+ */
+kvfp4_status_t kv_dequantize_paged(const kvfp4_paged_cache_t *cache,
+                                   const void *block_tables, int32_t bt_dtype,
+                                   int64_t bt_row_stride, int32_t bt_cols,
+                                   const int32_t *seq_lens, int32_t batch_size,
+                                   const float *k_scale, const float *v_scale,
+                                   void *output_k, void *output_v, int32_t out_dtype,
+                                   int32_t max_seq_len, void *stream);
+
+/*
+ * kv_materialize_fp8 - nvfp4_kv_materialize_fp8 / NVFP4KVMaterializer.run().
+ * cache must be HND with page_size % 4 == 0 and head_dim % 64 == 0 (the
+ * materializer's constraints); data page strides may exceed the compact
+ * page. For every request b and page j < ceil(seq_lens[b] / page_size):
+ *   dst = kv_page_indptr[b] + j + 1,
+ *   K page = block_tables[b * bt_row_stride + j],
+ *   V page = the same entry (uses_shared_paged_kv_idx != 0) or
+ *            block_tables[b * bt_row_stride + bt_kv_stride + j],
+ *   out[dst, 0 | 1, h, t, e] = E4M3_satfinite(E2M1(c) * E4M3(s)) for the
+ *   whole page (all page_size slots), K into half 0 and V into half 1,
+ *   fp8_block_tables[b * max_pages_per_seq + j] = dst.
+ * Page 0 of out (both halves) is set to zero. Only E2M1 and block scales are
+ * multiplied: the global scales belong to the consumer. The product is exact
+ * and rounds once to nearest-even, saturating at +-448 with its sign. K
+ * scales are linear; V scales are read 4-token interleaved when
+ * v_sf_interleaved != 0 (inside a (page, head) tile the scale of token t,
+ * block c sits at byte ((t / 4) * (head_dim / 16) + c) * 4 + t % 4), linear
+ * otherwise. out is float8_e4m3fn [num_out_pages, 2, num_kv_heads,
+ * page_size, head_dim], contiguous, 16-byte aligned, num_out_pages >=
+ * kv_page_indptr[batch_size] + 1; pages past kv_page_indptr[batch_size] and
+ * pages of a request past its length are neither written nor read, and no
+ * other table entry is written (zero the table first if a consumer reads
+ * them). Requests must satisfy seq_lens[b] <= max_pages_per_seq * page_size
+ * and reserve at least ceil(seq_lens[b] / page_size) pages.
+ * block_tables, seq_lens, kv_page_indptr and fp8_block_tables are int32.
+ */
+kvfp4_status_t kv_materialize_fp8(const kvfp4_paged_cache_t *cache, int32_t v_sf_interleaved,
+                                  const int32_t *block_tables, int32_t uses_shared_paged_kv_idx,
+                                  int64_t bt_row_stride, int64_t bt_kv_stride, int32_t bt_cols,
+                                  const int32_t *seq_lens, const int32_t *kv_page_indptr,
+                                  int32_t batch_size, void *out_fp8, int64_t num_out_pages,
+                                  int32_t *fp8_block_tables, int32_t max_pages_per_seq,
+                                  void *stream);
+
+/*
+ * kv_global_scale - make_nvfp4_global_scale(x, per_token_activation=False,
+ * recipe) (module page, "NVFP4 4over6 Recipes" and its precedence note): the
+ * per-tensor global decode scale g = amax|x| / fp32(6 * e4m3_max), one IEEE
+ * fp32 division, and 1 for an all-zero tensor. x is n contiguous fp16/bf16
+ * values (16-byte aligned); g_out is one device fp32, written in place (it is
+ * also used as the running maximum while the call runs). e4m3_max must match
+ * the quantizer's recipe: 448 for standard NVFP4, the recipe's value (256)
+ * for 4over6 - the page warns that a mismatch silently rescales the tensor.
+ */
+kvfp4_status_t kv_global_scale(const void *x, int32_t dtype, int64_t n, float e4m3_max,
+                               float *g_out, void *stream);
+
+/* Static description of a status code. */
+const char *kvfp4_status_string(kvfp4_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVFP4_H */

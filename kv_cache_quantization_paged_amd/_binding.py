@@ -1,0 +1,262 @@
+"""ctypes binding of ``libkvfp4.so`` (declared in ``include/kvfp4.h``).
+
+Argument marshalling only: the functions here take torch tensors that live on
+the GPU, check dtypes, shapes and devices, turn them into pointers and byte
+strides, and call the C entry point of the same name on torch's current
+stream. All computation happens in the HIP kernels. If the library has not
+been built, importing this module raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch  # loads the HIP runtime that the library then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libkvfp4.so")
+
+KVFP4_OK, KVFP4_EINVAL, KVFP4_EALIGN, KVFP4_EUNSUPPORTED, KVFP4_ELAUNCH = 0, 1, 2, 3, 4
+KVFP4_NHD, KVFP4_HND = 0, 1
+KVFP4_F16, KVFP4_BF16 = 0, 1
+KVFP4_I32, KVFP4_I64 = 0, 1
+KVFP4_ERR_MSE, KVFP4_ERR_MAE = 0, 1
+
+EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
+            "kvfp4_status_string")
+
+
+class PagedCacheDesc(C.Structure):
+    """``kvfp4_paged_cache_t``"""
+    _fields_ = [
+        ("k_data", C.c_void_p), ("v_data", C.c_void_p),
+        ("k_sf", C.c_void_p), ("v_sf", C.c_void_p),
+        ("k_page_stride", C.c_int64), ("v_page_stride", C.c_int64),
+        ("k_sf_page_stride", C.c_int64), ("v_sf_page_stride", C.c_int64),
+        ("num_pages", C.c_int32), ("page_size", C.c_int32),
+        ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("layout", C.c_int32),
+    ]
+
+
+class RecipeDesc(C.Structure):
+    """``kvfp4_recipe_t``"""
+    _fields_ = [("e4m3_max", C.c_float), ("err_mode", C.c_int32), ("err_use_fast_math", C.c_int32)]
+
+
+class KVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library():
+    """Load ``libkvfp4.so``; raises if it is missing (build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run kv_cache_quantization_paged_amd.build.build() "
+                          "(or __graft_entry__.build()) first")
+    lib = C.CDLL(LIB_PATH)
+    P, i32, i64, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_float
+    lib.kv_quantize_append.restype = i32
+    lib.kv_quantize_append.argtypes = [C.POINTER(PagedCacheDesc), P, P, i32, i64, P, P, P, P, P, i32,
+                                       f32, f32, C.POINTER(RecipeDesc), P]
+    lib.kv_dequantize_paged.restype = i32
+    lib.kv_dequantize_paged.argtypes = [C.POINTER(PagedCacheDesc), P, i32, i64, i32, P, i32, P, P,
+                                        P, P, i32, i32, P]
+    lib.kv_materialize_fp8.restype = i32
+    lib.kv_materialize_fp8.argtypes = [C.POINTER(PagedCacheDesc), i32, P, i32, i64, i64, i32, P, P, i32,
+                                       P, i64, P, i32, P]
+    lib.kv_global_scale.restype = i32
+    lib.kv_global_scale.argtypes = [P, i32, i64, f32, P, P]
+    lib.kvfp4_status_string.restype = C.c_char_p
+    lib.kvfp4_status_string.argtypes = [i32]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().kvfp4_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != KVFP4_OK:
+        raise KVFP4Error(status, where)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _half_enum(dtype) -> int:
+    if dtype == torch.float16:
+        return KVFP4_F16
+    if dtype == torch.bfloat16:
+        return KVFP4_BF16
+    raise TypeError(f"expected float16 or bfloat16, got {dtype}")
+
+
+def _need_i32(t, name):
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 CUDA tensor")
+
+
+# ---------------------------------------------------------------------------
+# cache descriptors
+# ---------------------------------------------------------------------------
+class PagedCache:
+    """Describes a paged NVFP4 cache held in four uint8 CUDA tensors.
+
+    ``k_data``/``v_data``: [num_pages, page_size, H, D/2] (NHD) or
+    [num_pages, H, page_size, D/2] (HND); ``k_sf``/``v_sf`` the same with D/16.
+    Any page stride is allowed (tuple, stacked 5-D views, padded pages) as long
+    as each page is compact inside.
+    """
+
+    def __init__(self, k_data, v_data, k_sf, v_sf, layout: int):
+        if layout not in (KVFP4_NHD, KVFP4_HND):
+            raise ValueError("layout must be NHD (0) or HND (1)")
+        for t, n in ((k_data, "k_data"), (v_data, "v_data"), (k_sf, "k_sf"), (v_sf, "v_sf")):
+            if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 4:
+                raise TypeError(f"{n} must be a 4-D uint8 CUDA tensor")
+            inner = t.shape[1:]
+            want = (inner[1] * inner[2], inner[2], 1)
+            if tuple(t.stride()[1:]) != want:
+                raise ValueError(f"{n}: each page must be compact (strides {t.stride()})")
+        if k_data.shape != v_data.shape or k_sf.shape != v_sf.shape or k_data.shape[:3] != k_sf.shape[:3]:
+            raise ValueError("K/V data and scale shapes disagree")
+        self.layout = layout
+        if layout == KVFP4_NHD:
+            _, self.page_size, self.num_kv_heads, half = k_data.shape
+        else:
+            _, self.num_kv_heads, self.page_size, half = k_data.shape
+        self.head_dim = 2 * half
+        if k_sf.shape[3] * 16 != self.head_dim:
+            raise ValueError("scale tensors must have head_dim // 16 in the last dimension")
+        self.tensors = (k_data, v_data, k_sf, v_sf)
+        self.num_pages = min(k_data.shape[0], v_data.shape[0])
+        self.desc = PagedCacheDesc(k_data.data_ptr(), v_data.data_ptr(), k_sf.data_ptr(), v_sf.data_ptr(),
+                                   k_data.stride(0), v_data.stride(0), k_sf.stride(0), v_sf.stride(0),
+                                   self.num_pages, self.page_size, self.num_kv_heads, self.head_dim, layout)
+
+
+class Recipe:
+    """4over6 recipe (``kvfp4_recipe_t``); ``None`` everywhere means standard NVFP4."""
+
+    def __init__(self, e4m3_max: float = 256.0, err_mode: int = KVFP4_ERR_MSE, err_use_fast_math: bool = False):
+        self.e4m3_max = float(e4m3_max)
+        self.err_mode = int(err_mode)
+        self.err_use_fast_math = bool(err_use_fast_math)
+
+    def desc(self):
+        return RecipeDesc(self.e4m3_max, self.err_mode, int(self.err_use_fast_math))
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, one Python function each
+# ---------------------------------------------------------------------------
+def kv_quantize_append(cache: PagedCache, append_key, append_value, batch_indices, positions,
+                       kv_indices, kv_indptr, kv_last_page_len, k_scale: float, v_scale: float,
+                       recipe: Recipe | None = None, stream=None):
+    lib = load_library()
+    if append_key.shape != append_value.shape or append_key.dtype != append_value.dtype:
+        raise ValueError("append_key and append_value must match")
+    if append_key.dim() != 3 or tuple(append_key.shape[1:]) != (cache.num_kv_heads, cache.head_dim):
+        raise ValueError("append rows must be [nnz, num_kv_heads, head_dim]")
+    if not (append_key.is_cuda and append_key.is_contiguous() and append_value.is_contiguous()):
+        raise ValueError("append rows must be contiguous CUDA tensors")
+    for t, n in ((batch_indices, "batch_indices"), (positions, "positions"), (kv_indices, "kv_indices"),
+                 (kv_indptr, "kv_indptr"), (kv_last_page_len, "kv_last_page_len")):
+        _need_i32(t, n)
+    nnz = append_key.shape[0]
+    if batch_indices.numel() != nnz or positions.numel() != nnz:
+        raise ValueError("batch_indices / positions must have nnz entries")
+    batch = kv_indptr.numel() - 1
+    if kv_last_page_len.numel() != batch:
+        raise ValueError("kv_last_page_len must have batch_size entries")
+    rd = recipe.desc() if recipe is not None else None
+    st = lib.kv_quantize_append(C.byref(cache.desc), _ptr(append_key), _ptr(append_value),
+                                _half_enum(append_key.dtype), nnz, _ptr(batch_indices), _ptr(positions),
+                                _ptr(kv_indices), _ptr(kv_indptr), _ptr(kv_last_page_len), batch,
+                                float(k_scale), float(v_scale), C.byref(rd) if rd is not None else None,
+                                _stream(stream))
+    _check(st, "kv_quantize_append")
+
+
+def kv_dequantize_paged(cache: PagedCache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v,
+                        stream=None):
+    lib = load_library()
+    if block_tables.dtype not in (torch.int32, torch.int64) or block_tables.dim() != 2 or not block_tables.is_cuda:
+        raise TypeError("block_tables must be a 2-D int32/int64 CUDA tensor")
+    if block_tables.stride(1) != 1:
+        raise ValueError("block_tables rows must be contiguous")
+    _need_i32(seq_lens, "seq_lens")
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.dtype != torch.float32 or not t.is_cuda or t.numel() < 1:
+            raise TypeError(f"{n} must be a float32 CUDA tensor")
+    if output_k.shape != output_v.shape or output_k.dtype != output_v.dtype:
+        raise ValueError("output_k and output_v must match")
+    if output_k.dim() != 4 or tuple(output_k.shape[2:]) != (cache.num_kv_heads, cache.head_dim):
+        raise ValueError("outputs must be [batch, max_seq_len, num_heads, head_dim]")
+    if not (output_k.is_cuda and output_k.is_contiguous() and output_v.is_contiguous()):
+        raise ValueError("outputs must be contiguous CUDA tensors")
+    B, T = output_k.shape[0], output_k.shape[1]
+    if block_tables.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_tables / seq_lens batch size disagrees with the outputs")
+    st = lib.kv_dequantize_paged(C.byref(cache.desc), _ptr(block_tables),
+                                 KVFP4_I64 if block_tables.dtype == torch.int64 else KVFP4_I32,
+                                 block_tables.stride(0), block_tables.shape[1], _ptr(seq_lens), B,
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(output_k), _ptr(output_v),
+                                 _half_enum(output_k.dtype), T, _stream(stream))
+    _check(st, "kv_dequantize_paged")
+
+
+def kv_materialize_fp8(cache: PagedCache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
+                       uses_shared_paged_kv_idx: bool = True, v_sf_interleaved: bool = True, stream=None):
+    lib = load_library()
+    _need_i32(seq_lens, "seq_lens")
+    _need_i32(kv_page_indptr, "kv_page_indptr")
+    _need_i32(fp8_block_tables, "fp8_block_tables")
+    if block_tables.dtype != torch.int32 or not block_tables.is_cuda or block_tables.stride(-1) != 1:
+        raise TypeError("block_tables must be an int32 CUDA tensor with contiguous rows")
+    B = seq_lens.numel()
+    if uses_shared_paged_kv_idx:
+        if block_tables.dim() != 2:
+            raise ValueError("shared block_tables are [batch, max_num_pages]")
+        cols, row, kvs = block_tables.shape[1], block_tables.stride(0), 0
+    else:
+        if block_tables.dim() != 3 or block_tables.shape[1] != 2:
+            raise ValueError("separate block_tables are [batch, 2, max_num_pages]")
+        cols, row, kvs = block_tables.shape[2], block_tables.stride(0), block_tables.stride(1)
+    if block_tables.shape[0] != B or kv_page_indptr.numel() != B + 1 or fp8_block_tables.shape[0] != B:
+        raise ValueError("batch sizes disagree")
+    if out.dim() != 5 or out.shape[1:] != (2, cache.num_kv_heads, cache.page_size, cache.head_dim):
+        raise ValueError("out must be [num_out_pages, 2, num_kv_heads, page_size, head_dim]")
+    if out.element_size() != 1 or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous one-byte (float8_e4m3fn) CUDA tensor")
+    st = lib.kv_materialize_fp8(C.byref(cache.desc), int(bool(v_sf_interleaved)), _ptr(block_tables),
+                                int(bool(uses_shared_paged_kv_idx)), row, kvs, cols, _ptr(seq_lens),
+                                _ptr(kv_page_indptr), B, _ptr(out), out.shape[0], _ptr(fp8_block_tables),
+                                fp8_block_tables.shape[1], _stream(stream))
+    _check(st, "kv_materialize_fp8")
+
+
+def kv_global_scale(x, e4m3_max: float, g_out, stream=None):
+    lib = load_library()
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous CUDA tensor")
+    if g_out.dtype != torch.float32 or not g_out.is_cuda:
+        raise TypeError("g_out must be a float32 CUDA tensor")
+    st = lib.kv_global_scale(_ptr(x), _half_enum(x.dtype), x.numel(), float(e4m3_max), _ptr(g_out),
+                             _stream(stream))
+    _check(st, "kv_global_scale")

@@ -1,0 +1,170 @@
+"""Torch-facing API with the signatures of the FlashInfer KV-cache pages.
+
+* ``nvfp4_quantize_append_paged_kv_cache``  (flashinfer.page API page)
+* ``nvfp4_kv_dequantize_paged``             (flashinfer.quantization API page)
+* ``nvfp4_kv_materialize_fp8`` and ``NVFP4KVMaterializer`` (the
+  nvfp4_kv_materialize API page and the materializer class on the
+  flashinfer.quantization module page)
+* ``NVFP44Over6Config``, ``make_nvfp4_global_scale``, ``nvfp4_e4m3_max``
+  (module page, "NVFP4 4over6 Recipes")
+
+Caches are given as on the pages: a (K, V) tuple of uint8 tensors or one
+stacked 5-D tensor with K/V on dimension 1, in "NHD" or "HND" layout. This
+module only reshapes arguments into the C ABI's descriptors; the work runs in
+the library's kernels on torch's current stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Tuple, Union
+
+import torch
+
+from . import _binding as B
+
+CacheArg = Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]
+
+
+# ---------------------------------------------------------------------------
+# recipe
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class NVFP44Over6Config:
+    """4over6 block-scale recipe: e4m3_max (256 by default), err_mode "MSE"
+    or "MAE". ``err_use_fast_math=True`` (fp16 error evaluation, a distinct
+    recipe on the page) is rejected by the library."""
+    e4m3_max: float = 256.0
+    err_mode: str = "MSE"
+    err_use_fast_math: bool = False
+
+    def _recipe(self) -> B.Recipe:
+        mode = {"MSE": B.KVFP4_ERR_MSE, "MAE": B.KVFP4_ERR_MAE}.get(str(self.err_mode).upper())
+        if mode is None:
+            raise ValueError(f"err_mode must be 'MSE' or 'MAE', got {self.err_mode!r}")
+        return B.Recipe(self.e4m3_max, mode, self.err_use_fast_math)
+
+
+def nvfp4_e4m3_max(nvfp4_4over6_config: Optional[NVFP44Over6Config] = None) -> float:
+    """E4M3 block-scale clamp implied by a resolved recipe (448 when None)."""
+    return 448.0 if nvfp4_4over6_config is None else float(nvfp4_4over6_config.e4m3_max)
+
+
+def make_nvfp4_global_scale(x: torch.Tensor, per_token_activation: bool = False,
+                            nvfp4_4over6_config: Optional[NVFP44Over6Config] = None,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-tensor global decode scale amax|x| / (6 * e4m3_max) as a 1-element
+    float32 CUDA tensor. Use the same recipe as the quantize call."""
+    if per_token_activation:
+        raise NotImplementedError("per-token global scales are not part of the KV-cache path")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    B.kv_global_scale(x.contiguous(), nvfp4_e4m3_max(nvfp4_4over6_config), out)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# cache arguments
+# ---------------------------------------------------------------------------
+def _layout(kv_layout: str) -> int:
+    if kv_layout == "NHD":
+        return B.KVFP4_NHD
+    if kv_layout == "HND":
+        return B.KVFP4_HND
+    raise ValueError(f"kv_layout must be 'NHD' or 'HND', got {kv_layout!r}")
+
+
+def _split(cache: CacheArg, name: str):
+    if isinstance(cache, (tuple, list)):
+        if len(cache) != 2:
+            raise ValueError(f"{name}: a tuple cache has two tensors (K, V)")
+        return cache[0], cache[1]
+    if cache.dim() != 5 or cache.shape[1] != 2:
+        raise ValueError(f"{name}: a stacked cache is 5-D with K/V on dimension 1")
+    return cache[:, 0], cache[:, 1]
+
+
+def paged_cache(paged_kv_cache: CacheArg, kv_cache_sf: CacheArg, kv_layout: str = "NHD") -> B.PagedCache:
+    k, v = _split(paged_kv_cache, "paged_kv_cache")
+    ks, vs = _split(kv_cache_sf, "kv_cache_sf")
+    return B.PagedCache(k, v, ks, vs, _layout(kv_layout))
+
+
+# ---------------------------------------------------------------------------
+# the three calls
+# ---------------------------------------------------------------------------
+def nvfp4_quantize_append_paged_kv_cache(append_key, append_value, batch_indices, positions,
+                                         paged_kv_cache: CacheArg, kv_cache_sf: CacheArg, kv_indices,
+                                         kv_indptr, kv_last_page_len, k_scale: float, v_scale: float,
+                                         kv_layout: str = "NHD",
+                                         nvfp4_4over6: Optional[NVFP44Over6Config] = None) -> None:
+    """Quantize and append K/V rows in place (standard NVFP4, or the given
+    4over6 recipe)."""
+    cache = paged_cache(paged_kv_cache, kv_cache_sf, kv_layout)
+    recipe = nvfp4_4over6._recipe() if nvfp4_4over6 is not None else None
+    B.kv_quantize_append(cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                         kv_last_page_len, k_scale, v_scale, recipe)
+
+
+def nvfp4_kv_dequantize_paged(paged_kv_cache: CacheArg, kv_cache_sf: CacheArg, block_tables, seq_lens,
+                              k_scale: torch.Tensor, v_scale: torch.Tensor, output_k, output_v,
+                              kv_layout: str = "NHD") -> None:
+    """Dequantize into caller-owned [batch, max_seq_len, H, D] outputs;
+    positions >= seq_lens[b] are left unchanged."""
+    cache = paged_cache(paged_kv_cache, kv_cache_sf, kv_layout)
+    B.kv_dequantize_paged(cache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v)
+
+
+def _hnd_cache(k_cache, v_cache, k_block_scales, v_block_scales) -> B.PagedCache:
+    return B.PagedCache(k_cache, v_cache, k_block_scales, v_block_scales, B.KVFP4_HND)
+
+
+def nvfp4_kv_materialize_fp8(k_cache, v_cache, k_block_scales, v_block_scales, block_tables, seq_lens,
+                             max_kv_len: int, uses_shared_paged_kv_idx: bool = True,
+                             out: Optional[torch.Tensor] = None, kv_page_indptr: Optional[torch.Tensor] = None,
+                             num_pages: Optional[int] = None, v_sf_interleaved: bool = True):
+    """Functional form: validates, allocates what is not given, returns
+    (kv_cache_fp8, fp8_block_tables) with padded table entries 0."""
+    cache = _hnd_cache(k_cache, v_cache, k_block_scales, v_block_scales)
+    batch = seq_lens.numel()
+    ps = cache.page_size
+    m = (int(max_kv_len) + ps - 1) // ps
+    dev = k_cache.device
+    if kv_page_indptr is None:
+        kv_page_indptr = torch.arange(0, (batch + 1) * m, m, dtype=torch.int32, device=dev)
+        num_pages = batch * m
+    elif num_pages is None:
+        raise ValueError("kv_page_indptr requires num_pages (its last element, known on the host)")
+    if out is None:
+        out = torch.empty((num_pages + 1, 2, cache.num_kv_heads, ps, cache.head_dim),
+                          dtype=torch.float8_e4m3fn, device=dev)
+    table = torch.zeros((batch, m), dtype=torch.int32, device=dev)
+    B.kv_materialize_fp8(cache, block_tables, seq_lens, kv_page_indptr, out, table,
+                         uses_shared_paged_kv_idx, v_sf_interleaved)
+    return out, table
+
+
+class NVFP4KVMaterializer:
+    """Validate once, launch many times. ``run()`` allocates nothing, does
+    not synchronize, and launches on the current stream."""
+
+    def __init__(self, num_kv_heads: int, page_size: int, head_dim: int, device="cuda",
+                 uses_shared_paged_kv_idx: bool = True, v_sf_interleaved: bool = True):
+        if page_size % 4 != 0:
+            raise ValueError("page_size must be divisible by 4")
+        if head_dim % 64 != 0:
+            raise ValueError("head_dim must be divisible by 64")
+        self.num_kv_heads, self.page_size, self.head_dim = num_kv_heads, page_size, head_dim
+        self.device = torch.device(device)
+        self.shared = bool(uses_shared_paged_kv_idx)
+        self.v_sf_interleaved = bool(v_sf_interleaved)
+        B.load_library()
+
+    def run(self, k_cache, v_cache, k_block_scales, v_block_scales, block_tables, seq_lens, kv_page_indptr,
+            *, out: torch.Tensor, fp8_block_tables: torch.Tensor):
+        cache = _hnd_cache(k_cache, v_cache, k_block_scales, v_block_scales)
+        if (cache.num_kv_heads, cache.page_size, cache.head_dim) != (self.num_kv_heads, self.page_size,
+                                                                     self.head_dim):
+            raise ValueError("cache geometry differs from the materializer's")
+        B.kv_materialize_fp8(cache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
+                             self.shared, self.v_sf_interleaved)
+        return out, fp8_block_tables

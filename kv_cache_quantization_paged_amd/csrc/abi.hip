@@ -1,0 +1,186 @@
+// abi.hip - the extern "C" boundary: argument checks, then one launch
+// sequence on the caller's stream. Every check runs before anything is
+// queued, so a rejected call has no effect. Tensor values are not read on the
+// host (that would need a synchronization); see include/kvfp4.h.
+#include <math.h>
+#include <string.h>
+
+#include "kvfp4_internal.h"
+
+using namespace kvfp4;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned16(int64_t v) { return (v & 15) == 0; }
+
+// host-side E4M3 decode, used only to check that a recipe clamp is an E4M3 value
+float e4m3_value_host(uint32_t b)
+{
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 0)
+        return (float)m * 0x1p-9f;
+    return ldexpf(1.0f + (float)m / 8.0f, (int)e - 7);
+}
+
+bool is_finite_e4m3_value(float v)
+{
+    for (uint32_t b = 0; b < 0x7F; ++b)
+        if (e4m3_value_host(b) == v)
+            return true;
+    return false;
+}
+
+kvfp4_status_t check_cache(const kvfp4_paged_cache_t *c)
+{
+    if (!c || !c->k_data || !c->v_data || !c->k_sf || !c->v_sf)
+        return KVFP4_EINVAL;
+    if (c->num_pages <= 0 || c->page_size <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
+        return KVFP4_EINVAL;
+    if (c->head_dim % 16 != 0)
+        return KVFP4_EINVAL;
+    if (c->layout != KVFP4_NHD && c->layout != KVFP4_HND)
+        return KVFP4_EINVAL;
+    const int64_t elems = (int64_t)c->page_size * c->num_kv_heads * c->head_dim;
+    if (elems > (int64_t)1 << 30)
+        return KVFP4_EINVAL;
+    if (c->k_page_stride < elems / 2 || c->v_page_stride < elems / 2)
+        return KVFP4_EINVAL;
+    if (c->k_sf_page_stride < elems / 16 || c->v_sf_page_stride < elems / 16)
+        return KVFP4_EINVAL;
+    if (!aligned16(c->k_data) || !aligned16(c->v_data) || !aligned16(c->k_page_stride) ||
+        !aligned16(c->v_page_stride))
+        return KVFP4_EALIGN;
+    return KVFP4_OK;
+}
+
+kvfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? KVFP4_OK : KVFP4_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+kvfp4_status_t kv_quantize_append(const kvfp4_paged_cache_t *cache, const void *append_key,
+                                  const void *append_value, int32_t in_dtype, int64_t nnz,
+                                  const int32_t *batch_indices, const int32_t *positions,
+                                  const int32_t *kv_indices, const int32_t *kv_indptr,
+                                  const int32_t *kv_last_page_len, int32_t batch_size, float k_scale,
+                                  float v_scale, const kvfp4_recipe_t *recipe, void *stream)
+{
+    kvfp4_status_t s = check_cache(cache);
+    if (s != KVFP4_OK)
+        return s;
+    if (in_dtype != KVFP4_F16 && in_dtype != KVFP4_BF16)
+        return KVFP4_EINVAL;
+    if (nnz < 0 || batch_size < 0)
+        return KVFP4_EINVAL;
+    if (!(k_scale > 0.0f) || !isfinite(k_scale) || !(v_scale > 0.0f) || !isfinite(v_scale))
+        return KVFP4_EINVAL;
+    if (recipe) {
+        if (!(recipe->e4m3_max > 0.0f && recipe->e4m3_max <= 448.0f) || !is_finite_e4m3_value(recipe->e4m3_max))
+            return KVFP4_EINVAL;
+        if (recipe->err_mode != KVFP4_ERR_MSE && recipe->err_mode != KVFP4_ERR_MAE)
+            return KVFP4_EINVAL;
+        if (recipe->err_use_fast_math != 0)
+            return KVFP4_EUNSUPPORTED;
+    }
+    if (nnz == 0)
+        return KVFP4_OK;
+    if (batch_size == 0 || !append_key || !append_value || !batch_indices || !positions || !kv_indices ||
+        !kv_indptr || !kv_last_page_len)
+        return KVFP4_EINVAL;
+    if (!aligned16(append_key) || !aligned16(append_value))
+        return KVFP4_EALIGN;
+    return from_hip(launch_quantize_append(*cache, append_key, append_value, in_dtype == KVFP4_BF16, nnz,
+                                           batch_indices, positions, kv_indices, kv_indptr, k_scale, v_scale,
+                                           recipe, (hipStream_t)stream));
+}
+
+kvfp4_status_t kv_dequantize_paged(const kvfp4_paged_cache_t *cache, const void *block_tables, int32_t bt_dtype,
+                                   int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
+                                   int32_t batch_size, const float *k_scale, const float *v_scale,
+                                   void *output_k, void *output_v, int32_t out_dtype, int32_t max_seq_len,
+                                   void *stream)
+{
+    kvfp4_status_t s = check_cache(cache);
+    if (s != KVFP4_OK)
+        return s;
+    if (bt_dtype != KVFP4_I32 && bt_dtype != KVFP4_I64)
+        return KVFP4_EINVAL;
+    if (out_dtype != KVFP4_F16 && out_dtype != KVFP4_BF16)
+        return KVFP4_EINVAL;
+    if (batch_size < 0 || max_seq_len < 0 || bt_cols < 0 || bt_row_stride < bt_cols)
+        return KVFP4_EINVAL;
+    if (batch_size == 0 || max_seq_len == 0)
+        return KVFP4_OK;
+    // each row needs ceil(min(seq_len, max_seq_len) / page_size) columns: a value, not checked
+    if (bt_cols < 1 || !block_tables || !seq_lens || !k_scale || !v_scale || !output_k || !output_v)
+        return KVFP4_EINVAL;
+    if (!aligned16(output_k) || !aligned16(output_v))
+        return KVFP4_EALIGN;
+    return from_hip(launch_dequantize_paged(*cache, block_tables, bt_dtype == KVFP4_I64, bt_row_stride, seq_lens,
+                                            batch_size, k_scale, v_scale, output_k, output_v,
+                                            out_dtype == KVFP4_BF16, max_seq_len, (hipStream_t)stream));
+}
+
+kvfp4_status_t kv_materialize_fp8(const kvfp4_paged_cache_t *cache, int32_t v_sf_interleaved,
+                                  const int32_t *block_tables, int32_t uses_shared_paged_kv_idx,
+                                  int64_t bt_row_stride, int64_t bt_kv_stride, int32_t bt_cols,
+                                  const int32_t *seq_lens, const int32_t *kv_page_indptr, int32_t batch_size,
+                                  void *out_fp8, int64_t num_out_pages, int32_t *fp8_block_tables,
+                                  int32_t max_pages_per_seq, void *stream)
+{
+    kvfp4_status_t s = check_cache(cache);
+    if (s != KVFP4_OK)
+        return s;
+    if (cache->layout != KVFP4_HND || cache->page_size % 4 != 0 || cache->head_dim % 64 != 0)
+        return KVFP4_EINVAL;
+    if (batch_size < 0 || num_out_pages < 1 || !out_fp8 || max_pages_per_seq < 0)
+        return KVFP4_EINVAL;
+    if (!aligned16(out_fp8))
+        return KVFP4_EALIGN;
+    if (batch_size > 0) {
+        if (!block_tables || !seq_lens || !kv_page_indptr || !fp8_block_tables)
+            return KVFP4_EINVAL;
+        if (bt_cols < max_pages_per_seq)
+            return KVFP4_EINVAL;
+        if (uses_shared_paged_kv_idx) {
+            if (bt_row_stride < bt_cols)
+                return KVFP4_EINVAL;
+        } else if (bt_kv_stride < bt_cols || bt_row_stride < bt_kv_stride + bt_cols) {
+            return KVFP4_EINVAL;
+        }
+    }
+    return from_hip(launch_materialize_fp8(*cache, v_sf_interleaved != 0, block_tables, uses_shared_paged_kv_idx != 0,
+                                           bt_row_stride, bt_kv_stride, seq_lens, kv_page_indptr, batch_size,
+                                           out_fp8, fp8_block_tables, max_pages_per_seq, (hipStream_t)stream));
+}
+
+kvfp4_status_t kv_global_scale(const void *x, int32_t dtype, int64_t n, float e4m3_max, float *g_out, void *stream)
+{
+    if (dtype != KVFP4_F16 && dtype != KVFP4_BF16)
+        return KVFP4_EINVAL;
+    if (n < 0 || !g_out || (n > 0 && !x))
+        return KVFP4_EINVAL;
+    if (!(e4m3_max > 0.0f && e4m3_max <= 448.0f) || !is_finite_e4m3_value(e4m3_max))
+        return KVFP4_EINVAL;
+    if (n > 0 && !aligned16(x))
+        return KVFP4_EALIGN;
+    if (((uintptr_t)g_out & 3u) != 0)
+        return KVFP4_EALIGN;
+    return from_hip(launch_global_scale(x, dtype == KVFP4_BF16, n, e4m3_max, g_out, (hipStream_t)stream));
+}
+
+const char *kvfp4_status_string(kvfp4_status_t status)
+{
+    switch (status) {
+    case KVFP4_OK: return "ok";
+    case KVFP4_EINVAL: return "invalid argument (null pointer, enum, extent, stride or scale)";
+    case KVFP4_EALIGN: return "misaligned pointer or stride (16-byte alignment required)";
+    case KVFP4_EUNSUPPORTED: return "unsupported request (fp16 4over6 error evaluation is not implemented)";
+    case KVFP4_ELAUNCH: return "HIP kernel launch failed (is the device gfx950?)";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

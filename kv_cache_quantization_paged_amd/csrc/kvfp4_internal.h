@@ -1,0 +1,34 @@
+// kvfp4_internal.h - launchers shared between the C-ABI layer and the kernel
+// translation units. Arguments reaching these functions are already checked.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvfp4.h"
+
+namespace kvfp4 {
+
+// Persistent grids: 256 CUs x 8 resident 256-thread workgroups.
+constexpr int kPersistentWorkgroups = 2048;
+
+hipError_t launch_quantize_append(const kvfp4_paged_cache_t &c, const void *key, const void *value,
+                                  bool in_bf16, int64_t nnz, const int32_t *batch_indices,
+                                  const int32_t *positions, const int32_t *kv_indices,
+                                  const int32_t *kv_indptr, float k_scale, float v_scale,
+                                  const kvfp4_recipe_t *recipe, hipStream_t st);
+
+hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *block_tables, bool bt64,
+                                   int64_t bt_row_stride, const int32_t *seq_lens, int32_t batch,
+                                   const float *k_scale, const float *v_scale, void *out_k, void *out_v,
+                                   bool out_bf16, int32_t max_seq_len, hipStream_t st);
+
+hipError_t launch_materialize_fp8(const kvfp4_paged_cache_t &c, bool v_interleaved, const int32_t *bt,
+                                  bool shared, int64_t bt_row_stride, int64_t bt_kv_stride,
+                                  const int32_t *seq_lens, const int32_t *indptr, int32_t batch,
+                                  void *out, int32_t *table, int32_t maxp, hipStream_t st);
+
+hipError_t launch_global_scale(const void *x, bool bf16, int64_t n, float e4m3_max, float *g_out,
+                               hipStream_t st);
+
+}  // namespace kvfp4

@@ -1,0 +1,111 @@
+// nvfp4_device.h - device-side number-format helpers for the gfx950 kernels.
+//
+// E2M1 (OCP FP4): sign bit 3, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for
+// codes 0..7. E4M3 (OCP float8_e4m3fn): bias 7, subnormal step 2^-9, largest
+// finite 448, 0x7F/0xFF NaN. Rounding is always to nearest, ties to even,
+// as the FlashInfer KV-cache pages' formats require of a quantizer; every
+// helper here is exact integer or single-rounding fp32 work so that the
+// results are reproducible bit for bit. Build with -ffp-contract=off: no step
+// below may be fused with a neighbouring multiply or add.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- E4M3 ----
+// byte -> fp32 (exact; NaN bytes give NaN).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b)
+{
+    const uint32_t mag = b & 0x7Fu;
+    float v = (mag >= 8u) ? __uint_as_float((mag << 20) + (120u << 23))   // (1+m/8) 2^(e-7)
+                          : (float)mag * 0x1p-9f;                          // m 2^-9
+    v = (mag == 0x7Fu) ? __uint_as_float(0x7FC00000u) : v;
+    return (b & 0x80u) ? -v : v;
+}
+
+// x in [0, 448] -> nearest E4M3 byte (ties to the even code).
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float x)
+{
+    if (x < 0x1p-6f)                                          // subnormal range: step 2^-9
+        return (uint32_t)__builtin_rintf(x * 512.0f);         // 8 here is 2^-6, the first normal
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);       // keep 3 mantissa bits, RNE
+    return (r >> 20) - (120u << 3);
+}
+
+// |p| of an exact product, any magnitude -> E4M3 byte with saturation to 448;
+// the sign comes from `sign` (0 or 0x80). NaN -> 0x7F | sign.
+__device__ __forceinline__ uint32_t f32_to_e4m3_satfinite(float a, uint32_t sign)
+{
+    if (!(a == a))
+        return 0x7Fu | sign;
+    return f32_to_e4m3_rne(fminf(a, 448.0f)) | sign;
+}
+
+// ---------------------------------------------------------------- E2M1 ----
+// |v| (finite) -> nearest E2M1 magnitude as fp32, ties to even, saturating at
+// 6. The grid has step 0.5 below 2 and doubles every binade above, so adding
+// c = 2^(E+22), whose ulp is that step (E = exponent of max(|v|, 1)), lets
+// the fp32 adder do the round-to-nearest-even; subtracting c gives the value.
+__device__ __forceinline__ float e2m1_round_mag(float a)
+{
+    const uint32_t u = __float_as_uint(a);
+    // exponent of |v| clamped to [1, 8]: below 1 the step stays 0.5, above 8
+    // everything saturates anyway (and c stays a finite power of two)
+    const uint32_t clamped = u < 0x3F800000u ? 0x3F800000u : (u > 0x41000000u ? 0x41000000u : u);
+    const float c = __uint_as_float((clamped & 0x7F800000u) + (22u << 23));
+    const float q = (a + c) - c;
+    return fminf(q, 6.0f);
+}
+
+// nearest-E2M1 magnitude (0, 0.5, 1, ..., 6) -> its 3-bit code.
+__device__ __forceinline__ uint32_t e2m1_mag_to_code(float q)
+{
+    const uint32_t hi = (__float_as_uint(q) >> 22);          // 252 for 0.5, 254.. for >= 1
+    const uint32_t k = hi >= 254u ? hi - 252u : 0u;
+    return q == 0.5f ? 1u : k;
+}
+
+// E2M1 magnitude code 0..7 -> value (exact).
+__device__ __forceinline__ float e2m1_code_to_mag(uint32_t k)
+{
+    const uint32_t bits = (k >= 2u) ? ((k + 252u) << 22) : (k ? 0x3F000000u : 0u);
+    return __uint_as_float(bits);
+}
+
+// ------------------------------------------------------- 16-bit floats ----
+// RNE fp32 -> bf16 / fp16 bit patterns, two at a time (gfx950 converts with
+// round-to-nearest-even; fp16 keeps subnormals).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const f32x2 v = {lo, hi};
+    const bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    const f32x2 v = {lo, hi};
+    const f16x2 r = __builtin_convertvector(v, f16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// bf16 / fp16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+}  // namespace kvfp4

@@ -1,0 +1,141 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function ``include/kvfp4.h`` declares, and rejects invalid arguments
+with the documented status before anything is launched."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from kv_cache_quantization_paged_amd import _binding
+    _binding.load_library()
+    return _binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
+                            "kvfp4_status_string"])
+
+
+def test_library_exports_every_declared_symbol(B):
+    lib = C.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(B.EXPORTED) == set(declared_functions())
+
+
+def test_status_strings(B):
+    for s in range(5):
+        assert B.status_string(s)
+    assert B.status_string(99) == "unknown status"
+
+
+def _cache(B, **kw):
+    d = dict(k_data=16, v_data=32, k_sf=48, v_sf=64, k_page_stride=8192, v_page_stride=8192,
+             k_sf_page_stride=1024, v_sf_page_stride=1024, num_pages=4, page_size=16, num_kv_heads=8,
+             head_dim=128, layout=0)
+    d.update(kw)
+    return B.PagedCacheDesc(**d)
+
+
+def _append(B, cache, **kw):
+    a = dict(key=C.c_void_p(4096), value=C.c_void_p(8192), dtype=1, nnz=1, bi=C.c_void_p(64), pos=C.c_void_p(64),
+             ind=C.c_void_p(64), ptr=C.c_void_p(64), last=C.c_void_p(64), batch=1, ks=1.0, vs=1.0, recipe=None)
+    a.update(kw)
+    lib = B.load_library()
+    return lib.kv_quantize_append(C.byref(cache), a["key"], a["value"], a["dtype"], a["nnz"], a["bi"], a["pos"],
+                                  a["ind"], a["ptr"], a["last"], a["batch"], a["ks"], a["vs"], a["recipe"], None)
+
+
+def test_append_rejects_bad_arguments(B):
+    assert _append(B, _cache(B, k_data=None)) == B.KVFP4_EINVAL
+    assert _append(B, _cache(B, head_dim=40)) == B.KVFP4_EINVAL
+    assert _append(B, _cache(B, layout=2)) == B.KVFP4_EINVAL
+    assert _append(B, _cache(B, k_page_stride=100)) == B.KVFP4_EINVAL            # smaller than a page
+    assert _append(B, _cache(B, k_page_stride=8200)) == B.KVFP4_EALIGN
+    assert _append(B, _cache(B, v_data=40)) == B.KVFP4_EALIGN
+    assert _append(B, _cache(B), dtype=7) == B.KVFP4_EINVAL
+    assert _append(B, _cache(B), ks=0.0) == B.KVFP4_EINVAL
+    assert _append(B, _cache(B), vs=float("inf")) == B.KVFP4_EINVAL
+    assert _append(B, _cache(B), ks=float("nan")) == B.KVFP4_EINVAL
+    assert _append(B, _cache(B), key=C.c_void_p(4100)) == B.KVFP4_EALIGN
+    assert _append(B, _cache(B), bi=None) == B.KVFP4_EINVAL
+    assert _append(B, _cache(B), nnz=-1) == B.KVFP4_EINVAL
+    bad = B.RecipeDesc(300.0, 0, 0)                                              # not an E4M3 value
+    assert _append(B, _cache(B), recipe=C.byref(bad)) == B.KVFP4_EINVAL
+    bad = B.RecipeDesc(256.0, 5, 0)
+    assert _append(B, _cache(B), recipe=C.byref(bad)) == B.KVFP4_EINVAL
+    fm = B.RecipeDesc(256.0, 0, 1)
+    assert _append(B, _cache(B), recipe=C.byref(fm)) == B.KVFP4_EUNSUPPORTED
+    # nnz == 0 is a no-op that launches nothing, even with null row pointers
+    assert _append(B, _cache(B), nnz=0, key=None, value=None, bi=None) == B.KVFP4_OK
+
+
+def test_dequant_rejects_bad_arguments(B):
+    lib = B.load_library()
+    P = C.c_void_p
+
+    def call(cache, bt=P(64), bt_dtype=0, row=4, cols=4, sl=P(64), batch=1, ks=P(64), vs=P(64), ok=P(4096),
+             ov=P(8192), out_dtype=1, T=16):
+        return lib.kv_dequantize_paged(C.byref(cache), bt, bt_dtype, row, cols, sl, batch, ks, vs, ok, ov,
+                                       out_dtype, T, None)
+    assert call(_cache(B, v_sf=None)) == B.KVFP4_EINVAL
+    assert call(_cache(B), bt_dtype=3) == B.KVFP4_EINVAL
+    assert call(_cache(B), out_dtype=3) == B.KVFP4_EINVAL
+    assert call(_cache(B), row=2, cols=4) == B.KVFP4_EINVAL
+    assert call(_cache(B), ks=None) == B.KVFP4_EINVAL
+    assert call(_cache(B), ok=P(4104)) == B.KVFP4_EALIGN
+    assert call(_cache(B), batch=-1) == B.KVFP4_EINVAL
+    assert call(_cache(B), batch=0, bt=None, sl=None) == B.KVFP4_OK
+    assert call(_cache(B), T=0) == B.KVFP4_OK
+
+
+def test_materialize_rejects_bad_arguments(B):
+    lib = B.load_library()
+    P = C.c_void_p
+
+    def call(cache, inter=1, bt=P(64), shared=1, row=8, kvs=0, cols=8, sl=P(64), ip=P(64), batch=1, out=P(4096),
+             n_out=4, tab=P(64), maxp=8):
+        return lib.kv_materialize_fp8(C.byref(cache), inter, bt, shared, row, kvs, cols, sl, ip, batch, out, n_out,
+                                      tab, maxp, None)
+    hnd = dict(layout=1)
+    assert call(_cache(B)) == B.KVFP4_EINVAL                                   # NHD is not accepted
+    assert call(_cache(B, page_size=6, k_page_stride=3072, v_page_stride=3072, **hnd)) == B.KVFP4_EINVAL
+    assert call(_cache(B, head_dim=96, k_page_stride=6144, v_page_stride=6144, **hnd)) == B.KVFP4_EINVAL
+    assert call(_cache(B, **hnd), n_out=0) == B.KVFP4_EINVAL
+    assert call(_cache(B, **hnd), out=P(4100)) == B.KVFP4_EALIGN
+    assert call(_cache(B, **hnd), cols=4, maxp=8) == B.KVFP4_EINVAL             # fewer columns than the FP8 table
+    assert call(_cache(B, **hnd), shared=0, row=8, kvs=8) == B.KVFP4_EINVAL     # row stride too small for [B,2,m]
+    assert call(_cache(B, **hnd), tab=None) == B.KVFP4_EINVAL
+
+
+def test_global_scale_rejects_bad_arguments(B):
+    lib = B.load_library()
+    P = C.c_void_p
+    assert lib.kv_global_scale(P(64), 5, 10, 448.0, P(64), None) == B.KVFP4_EINVAL
+    assert lib.kv_global_scale(P(64), 1, 10, 300.0, P(64), None) == B.KVFP4_EINVAL
+    assert lib.kv_global_scale(P(64), 1, 10, 448.0, None, None) == B.KVFP4_EINVAL
+    assert lib.kv_global_scale(P(72), 1, 10, 448.0, P(64), None) == B.KVFP4_EALIGN
+    assert lib.kv_global_scale(None, 1, 10, 448.0, P(64), None) == B.KVFP4_EINVAL
+
+
+def test_package_refuses_to_run_without_library(tmp_path, monkeypatch):
+    """No fallback: with the library missing, loading raises."""
+    from kv_cache_quantization_paged_amd import _binding
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(ImportError):
+        _binding.load_library()

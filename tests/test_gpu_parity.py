@@ -1,0 +1,334 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on
+seeded inputs that span many tiles and end in ragged tails. Codes, scales,
+page tables, FP8 pages and dequantized 16-bit values must match bit for bit
+(the dequant bar of 0 ulp holds because both sides use the same fp32 order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import DeviceCache, bits_tensor, first_mismatch, i32, oracle_threads, same_bytes, tensor_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_quantization_paged_amd as K
+    return K
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------- inputs
+def align_pad(ps, H, D):
+    """bytes that make a data page stride a multiple of 16 (the ABI's rule)"""
+    return (-(ps * H * D // 2)) % 16
+
+
+def append_values(rng, nnz, H, D, kind):
+    if kind == "normal":
+        x = W.head_scaled_normal(rng, nnz, W.head_scales(rng, H), D)
+    elif kind == "student_t":
+        x = W.student_t_with_outliers(rng, (nnz, H, D), frac=0.01)
+    else:   # "special": zero, -0, tiny, huge, grid-valued blocks mixed with normal ones
+        x = rng.standard_normal((nnz, H, D)).astype(np.float32)
+        blocks = x.reshape(-1, 16)
+        n = blocks.shape[0]
+        sel = rng.integers(0, 6, n)
+        blocks[sel == 0] = 0.0
+        blocks[sel == 1] = -0.0
+        blocks[sel == 2] *= 1e-6
+        blocks[sel == 3] *= 3e3
+        grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6], np.float32)
+        g4 = grid[rng.integers(0, 16, (int((sel == 4).sum()), 16))]
+        g4[:, 0] = 6.0
+        blocks[sel == 4] = g4 * np.float32(0.125)
+    return x
+
+
+def append_case(seed, layout, ps, H, D, in_bf16, kind="normal", stacked=False, data_pad=0, sf_pad=0,
+                B=6, pool=None):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, 5 * ps, B)
+    lens[0] = 1
+    start = np.array([rng.integers(0, l) for l in lens])
+    start[-1] = 0
+    n_pages = int(((lens + ps - 1) // ps).sum())
+    pool = pool or n_pages + 5
+    perm = rng.permutation(pool)
+    indices, indptr, last = W.csr_for_lengths(lens, ps, perm)
+    data_pad += align_pad(ps, H, D)
+    cache = W.make_cache(rng, pool, ps, H, D, layout, stacked=stacked, data_pad=data_pad, sf_pad=sf_pad)
+    bi, pos = W.rows_for_positions(start, lens)
+    order = rng.permutation(len(bi))                 # rows in any order
+    bi, pos = bi[order], pos[order]
+    nnz = len(bi)
+    key = W.f32_to_bits(append_values(rng, nnz, H, D, kind), in_bf16)
+    val = W.f32_to_bits(append_values(rng, nnz, H, D, kind) * np.float32(0.5), in_bf16)
+    return cache, key, val, bi, pos, indices, indptr, last, lens
+
+
+def run_append_both(K, orc, seed, layout, ps, H, D, in_bf16, recipe_o, recipe_k, kind="normal", stacked=False,
+                    data_pad=0, sf_pad=0, scale_mult=1.0):
+    cache, key, val, bi, pos, indices, indptr, last, _ = append_case(seed, layout, ps, H, D, in_bf16, kind,
+                                                                     stacked, data_pad, sf_pad)
+    emax = recipe_o.e4m3_max if recipe_o.four_over_six else 448.0
+    gk = orc.global_scale(key, in_bf16, emax) * scale_mult
+    gv = orc.global_scale(val, in_bf16, emax) * scale_mult
+    gk, gv = float(np.float32(gk)), float(np.float32(gv))
+    dev = DeviceCache(cache)
+    host = cache.copy()
+    say(f"append seed={seed} layout={layout} ps={ps} H={H} D={D} bf16={in_bf16} nnz={len(bi)} "
+        f"recipe={recipe_o} kind={kind} stacked={stacked} pad={data_pad}/{sf_pad}")
+    K.kv_quantize_append(dev.cache, bits_tensor(key, in_bf16), bits_tensor(val, in_bf16), i32(bi), i32(pos),
+                         i32(indices), i32(indptr), i32(last), gk, gv, recipe_k)
+    torch.cuda.synchronize()
+    orc.quantize_append(host, key, val, in_bf16, bi, pos, indices, indptr, last, gk, gv, recipe_o,
+                        threads=oracle_threads())
+    got = dev.to_host()
+    for name, a, b in zip(("k_data", "v_data", "k_sf", "v_sf"), (got.k_data, got.v_data, got.k_sf, got.v_sf),
+                          (host.k_data, host.v_data, host.k_sf, host.v_sf)):
+        assert np.array_equal(a, b), (name, first_mismatch(a, b))
+    assert same_bytes(got, host)          # padding and untouched bytes too
+
+
+def recipes(K, orc, name):
+    if name == "standard":
+        return orc.STANDARD, None
+    mode = orc.MSE if name == "mse" else orc.MAE
+    return orc.four_over_six(mode), K.Recipe(256.0, K.KVFP4_ERR_MSE if mode == orc.MSE else K.KVFP4_ERR_MAE)
+
+
+# --------------------------------------------------------------------------- append
+@pytest.mark.parametrize("layout", [W.NHD, W.HND])
+@pytest.mark.parametrize("recipe", ["standard", "mse", "mae"])
+@pytest.mark.parametrize("in_bf16", [True, False])
+def test_append_parity(K, orc, layout, recipe, in_bf16):
+    ro, rk = recipes(K, orc, recipe)
+    run_append_both(K, orc, 100 + layout * 10 + in_bf16, layout, 16, 8, 128, in_bf16, ro, rk, kind="student_t")
+
+
+@pytest.mark.parametrize("geom", [(1, 1, 16), (4, 2, 64), (64, 4, 256), (8, 3, 80), (32, 32, 256), (16, 5, 48)])
+@pytest.mark.parametrize("recipe", ["standard", "mse"])
+def test_append_geometries(K, orc, geom, recipe):
+    ps, H, D = geom
+    ro, rk = recipes(K, orc, recipe)
+    run_append_both(K, orc, 200 + ps + H + D, W.HND if D % 32 else W.NHD, ps, H, D, True, ro, rk)
+
+
+@pytest.mark.parametrize("kind", ["special", "normal"])
+@pytest.mark.parametrize("recipe", ["standard", "mse", "mae"])
+def test_append_special_values_and_clamp(K, orc, kind, recipe):
+    ro, rk = recipes(K, orc, recipe)
+    # scale_mult < 1 pushes block scales past the clamps (mismatched global scale)
+    for mult in (1.0, 0.1):
+        run_append_both(K, orc, 300, W.NHD, 16, 4, 128, False, ro, rk, kind=kind, scale_mult=mult)
+
+
+@pytest.mark.parametrize("stacked,data_pad,sf_pad", [(True, 0, 0), (False, 48, 5), (True, 32, 0)])
+def test_append_stacked_and_padded(K, orc, stacked, data_pad, sf_pad):
+    ro, rk = recipes(K, orc, "mae")
+    run_append_both(K, orc, 400, W.HND, 16, 8, 128, True, ro, rk, stacked=stacked, data_pad=data_pad, sf_pad=sf_pad)
+    ro, rk = recipes(K, orc, "standard")
+    run_append_both(K, orc, 401, W.NHD, 16, 8, 128, True, ro, rk, stacked=stacked, data_pad=data_pad, sf_pad=sf_pad)
+
+
+def test_append_empty_is_noop(K, orc):
+    cache, key, val, bi, pos, indices, indptr, last, _ = append_case(5, W.NHD, 16, 2, 64, True)
+    dev = DeviceCache(cache)
+    e = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    K.kv_quantize_append(dev.cache, e, e, i32(bi[:0]), i32(pos[:0]), i32(indices), i32(indptr), i32(last), 1.0, 1.0)
+    torch.cuda.synchronize()
+    assert same_bytes(dev.to_host(), cache)
+
+
+# --------------------------------------------------------------------------- dequant
+def dequant_case(seed, layout, ps, H, D, B=7, pool=60, neg_scales=True, stacked=False, data_pad=0):
+    rng = np.random.default_rng(seed)
+    data_pad += align_pad(ps, H, D)
+    cache = W.make_cache(rng, pool, ps, H, D, layout, stacked=stacked, data_pad=data_pad)
+    for a in (cache.k_sf, cache.v_sf):
+        a[...] = rng.integers(0, 256 if neg_scales else 0x7F, a.shape, dtype=np.uint8)
+        a[(a & 0x7F) == 0x7F] = 0x7E
+    T = 3 * ps + 5
+    lens = rng.integers(0, T + 6, B).astype(np.int32)
+    lens[0] = 0
+    lens[1] = T + 9                 # longer than max_seq_len: clamped
+    lens[2] = 1
+    cols = (T + ps - 1) // ps + 1
+    bt = rng.integers(0, pool, (B, cols)).astype(np.int32)
+    return cache, bt, lens, T
+
+
+@pytest.mark.parametrize("layout", [W.NHD, W.HND])
+@pytest.mark.parametrize("out_bf16", [True, False])
+@pytest.mark.parametrize("bt64", [False, True])
+@pytest.mark.parametrize("geom", [(16, 8, 128), (32, 2, 64), (5, 3, 48), (1, 16, 256)])
+def test_dequant_parity(K, orc, layout, out_bf16, bt64, geom):
+    ps, H, D = geom
+    seed = 500 + layout + 2 * out_bf16 + 4 * bt64 + ps
+    cache, bt, lens, T = dequant_case(seed, layout, ps, H, D)
+    bt = bt.astype(np.int64 if bt64 else np.int32)
+    B = len(lens)
+    gk, gv = 0.0137, 2.7e-4
+    ok = np.full((B, T, H, D), W.SENTINEL_16, np.uint16)
+    ov = ok.copy()
+    orc.dequantize_paged(cache, bt, lens, gk, gv, ok, ov, out_bf16, threads=oracle_threads())
+    dev = DeviceCache(cache)
+    tdt = torch.bfloat16 if out_bf16 else torch.float16
+    dk = torch.full((B, T, H, D), W.SENTINEL_16 - 65536, dtype=torch.int16, device="cuda").view(tdt)
+    dv = dk.clone()
+    say(f"dequant seed={seed} layout={layout} geom={geom} bf16={out_bf16} bt64={bt64} B={B} T={T}")
+    K.kv_dequantize_paged(dev.cache, torch.from_numpy(bt).cuda(), i32(lens),
+                          torch.tensor([gk], dtype=torch.float32, device="cuda"),
+                          torch.tensor([gv], dtype=torch.float32, device="cuda"), dk, dv)
+    torch.cuda.synchronize()
+    gk_bits, gv_bits = tensor_bits(dk), tensor_bits(dv)
+    assert np.array_equal(gk_bits, ok), first_mismatch(gk_bits, ok)
+    assert np.array_equal(gv_bits, ov), first_mismatch(gv_bits, ov)
+
+
+def test_dequant_stacked_padded_and_empty(K, orc):
+    cache, bt, lens, T = dequant_case(77, W.HND, 16, 4, 128, stacked=True, data_pad=64)
+    B, H, D = len(lens), 4, 128
+    ok = np.full((B, T, H, D), W.SENTINEL_16, np.uint16)
+    ov = ok.copy()
+    orc.dequantize_paged(cache, bt, lens, 0.5, 0.25, ok, ov, True)
+    dev = DeviceCache(cache)
+    dk = torch.full((B, T, H, D), W.SENTINEL_16 - 65536, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dv = dk.clone()
+    one = lambda v: torch.tensor([v], dtype=torch.float32, device="cuda")  # noqa: E731
+    K.kv_dequantize_paged(dev.cache, i32(bt), i32(lens), one(0.5), one(0.25), dk, dv)
+    # all-zero lengths: nothing may be written
+    zk = torch.full_like(dk.view(torch.int16), 7).view(torch.bfloat16)
+    zv = zk.clone()
+    K.kv_dequantize_paged(dev.cache, i32(bt), i32(np.zeros(B)), one(0.5), one(0.25), zk, zv)
+    torch.cuda.synchronize()
+    assert np.array_equal(tensor_bits(dk), ok) and np.array_equal(tensor_bits(dv), ov)
+    assert np.all(tensor_bits(zk) == 7) and np.all(tensor_bits(zv) == 7)
+
+
+def test_append_then_dequant_round_trip(K, orc):
+    """Tiny round trip workload: append every token, then dequantize into
+    sentinel-filled outputs; both stages bit-exact against the oracle."""
+    wl = W.tiny_round_trip()
+    gk, gv = orc.global_scale(wl.key, True), orc.global_scale(wl.value, True)
+    host = wl.cache.copy()
+    dev = DeviceCache(wl.cache)
+    K.kv_quantize_append(dev.cache, bits_tensor(wl.key, True), bits_tensor(wl.value, True), i32(wl.batch_indices),
+                         i32(wl.positions), i32(wl.kv_indices), i32(wl.kv_indptr), i32(wl.kv_last_page_len), gk, gv)
+    orc.quantize_append(host, wl.key, wl.value, True, wl.batch_indices, wl.positions, wl.kv_indices, wl.kv_indptr,
+                        wl.kv_last_page_len, gk, gv)
+    B, T, H, D = 2, wl.max_seq_len, 2, 64
+    dk = torch.full((B, T, H, D), W.SENTINEL_16 - 65536, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dv = dk.clone()
+    K.kv_dequantize_paged(dev.cache, i32(wl.block_tables), i32(wl.seq_lens),
+                          torch.tensor([gk], dtype=torch.float32, device="cuda"),
+                          torch.tensor([gv], dtype=torch.float32, device="cuda"), dk, dv)
+    torch.cuda.synchronize()
+    assert same_bytes(dev.to_host(), host)
+    ok = np.full((B, T, H, D), W.SENTINEL_16, np.uint16)
+    ov = ok.copy()
+    orc.dequantize_paged(host, wl.block_tables, wl.seq_lens, gk, gv, ok, ov, True)
+    assert np.array_equal(tensor_bits(dk), ok) and np.array_equal(tensor_bits(dv), ov)
+    assert np.all(ok[0, 5:] == W.SENTINEL_16)
+
+
+# --------------------------------------------------------------------------- materialize
+def mat_case(seed, shared, compact, ps=16, H=4, D=128, B=6, data_pad=256, extra_out=3):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 8 * ps, B)
+    lens[0] = 0
+    lens[1] = 1
+    lens[2] = 3 * ps
+    need = (lens + ps - 1) // ps
+    P = int(need.sum()) + 4
+    maxp = int(need.max()) + 2
+    cache = W.make_cache(rng, P, ps, H, D, W.HND, data_pad=data_pad)
+    for a in (cache.k_sf, cache.v_sf):
+        a[...] = rng.integers(0, 256, a.shape, dtype=np.uint8)
+        a[(a & 0x7F) == 0x7F] = 0x7E
+    res = need if compact else need + rng.integers(0, 3, B)
+    indptr = np.zeros(B + 1, np.int32)
+    indptr[1:] = np.cumsum(res)
+    if shared:
+        bt = rng.integers(0, P, (B, maxp + 1)).astype(np.int32)
+    else:
+        bt = rng.integers(0, P, (B, 2, maxp + 1)).astype(np.int32)
+    n_out = int(indptr[-1]) + 1 + extra_out
+    return cache, bt, lens.astype(np.int32), indptr, maxp, n_out
+
+
+@pytest.mark.parametrize("shared", [True, False])
+@pytest.mark.parametrize("compact", [True, False])
+@pytest.mark.parametrize("interleaved", [True, False])
+@pytest.mark.parametrize("geom", [(16, 4, 128), (4, 2, 64), (32, 8, 256), (8, 1, 192)])
+def test_materialize_parity(K, orc, shared, compact, interleaved, geom):
+    ps, H, D = geom
+    seed = 600 + shared + 2 * compact + 4 * interleaved + ps
+    cache, bt, lens, indptr, maxp, n_out = mat_case(seed, shared, compact, ps, H, D)
+    B = len(lens)
+    out = np.full((n_out, 2, H, ps, D), W.SENTINEL_FP8, np.uint8)
+    tab = np.full((B, maxp), -1, np.int32)
+    orc.materialize_fp8(cache, bt, lens, indptr, out, tab, shared=shared, v_sf_interleaved=interleaved,
+                        threads=oracle_threads())
+    dev = DeviceCache(cache)
+    d_out = torch.full((n_out, 2, H, ps, D), W.SENTINEL_FP8, dtype=torch.uint8, device="cuda")
+    d_tab = torch.full((B, maxp), -1, dtype=torch.int32, device="cuda")
+    say(f"materialize seed={seed} geom={geom} shared={shared} compact={compact} interleaved={interleaved}")
+    K.kv_materialize_fp8(dev.cache, torch.from_numpy(bt).cuda(), i32(lens), i32(indptr),
+                         d_out.view(torch.float8_e4m3fn), d_tab, shared, interleaved)
+    torch.cuda.synchronize()
+    got = d_out.cpu().numpy()
+    assert np.array_equal(got, out), first_mismatch(got, out)
+    assert np.array_equal(d_tab.cpu().numpy(), tab)
+
+
+def test_materialize_empty_batch_zeroes_page0(K, orc):
+    cache, bt, lens, indptr, maxp, n_out = mat_case(9, True, True)
+    dev = DeviceCache(cache)
+    d_out = torch.full((3, 2, 4, 16, 128), 0x33, dtype=torch.uint8, device="cuda")
+    d_tab = torch.full((1, 1), -1, dtype=torch.int32, device="cuda")
+    K.kv_materialize_fp8(dev.cache, i32(bt[:0]), i32(lens[:0]), i32(np.zeros(1)), d_out.view(torch.float8_e4m3fn),
+                         d_tab[:0], True, True)
+    torch.cuda.synchronize()
+    got = d_out.cpu().numpy()
+    assert np.all(got[0] == 0) and np.all(got[1:] == 0x33)
+
+
+def test_materializer_class_matches_functional(K, orc):
+    cache, bt, lens, indptr, maxp, n_out = mat_case(11, True, True)
+    dev = DeviceCache(cache)
+    m = (int(lens.max()) + 15) // 16
+    out_f, tab_f = K.nvfp4_kv_materialize_fp8(dev.k_data, dev.v_data, dev.k_sf, dev.v_sf, i32(bt), i32(lens),
+                                              int(lens.max()), True, kv_page_indptr=i32(indptr),
+                                              num_pages=int(indptr[-1]))
+    mat = K.NVFP4KVMaterializer(4, 16, 128)
+    out_r = torch.zeros_like(out_f)
+    tab_r = torch.zeros((len(lens), m), dtype=torch.int32, device="cuda")
+    mat.run(dev.k_data, dev.v_data, dev.k_sf, dev.v_sf, i32(bt), i32(lens), i32(indptr), out=out_r,
+            fp8_block_tables=tab_r)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f.view(torch.uint8), out_r.view(torch.uint8))
+    assert torch.equal(tab_f, tab_r)
+
+
+# --------------------------------------------------------------------------- global scale
+@pytest.mark.parametrize("n", [0, 1, 7, 4096, 1_000_003])
+@pytest.mark.parametrize("is_bf16", [True, False])
+@pytest.mark.parametrize("emax", [448.0, 256.0])
+def test_global_scale_parity(K, orc, n, is_bf16, emax):
+    rng = np.random.default_rng(n + 7 * is_bf16)
+    x = W.f32_to_bits((rng.standard_normal(n) * 3).astype(np.float32), is_bf16)
+    want = orc.global_scale(x, is_bf16, emax)
+    g = torch.full((1,), -5.0, dtype=torch.float32, device="cuda")
+    K.kv_global_scale(bits_tensor(x, is_bf16) if n else torch.empty(0, dtype=torch.bfloat16 if is_bf16 else
+                                                                    torch.float16, device="cuda"), emax, g)
+    torch.cuda.synchronize()
+    assert g.item() == want
