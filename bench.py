@@ -1,0 +1,430 @@
+"""Benchmark of the paged NVFP4 KV-cache path on one MI355X.
+
+Headline step (the decode workload): quantize-append one new token for each
+of 64 requests (bf16 K/V, 8 KV heads, head_dim 128, page_size 16, NHD pages
+shuffled across a 20,000-page pool), then gather-dequantize every request's
+full context (lengths U{1..4096} + 1) into bf16 [64, max_len, 8, 128].
+value = algorithmic bytes of the step / wall time of the step, with all
+inputs resident in HBM; two replicas of the workload alternate so that
+consecutive steps touch disjoint memory.
+
+Legs (same JSON line, each kernel timed alone, median of HIP-event times with
+a 1 GiB write between iterations so nothing is served from the 256 MB
+Infinity Cache): prefill dequantize (16 x 8192 tokens, HND, int64 table, fp16
+out), materialize-FP8 (32 requests, log-uniform lengths, padded pages,
+separate K/V tables), 4over6 quantize-append (65,536 rows, Student-t(3) with
+0.1% outliers x20, MSE and MAE) and its dequantize, and a plain
+device-to-device copy as the achievable-bandwidth context line.
+
+The CPU oracle is timed on a bounded sample of the decode step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+METRIC = "effective HBM GB/s and % of MI355X peak for paged NVFP4 KV append/dequant/FP8"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (what the method must move)
+# ---------------------------------------------------------------------------
+def dequant_bytes(lens, ps, H, D, bt_elem_bytes):
+    tokens = int(np.sum(lens))
+    pages = int(np.sum((np.asarray(lens) + ps - 1) // ps))
+    return 2 * tokens * H * (D // 2 + D // 16 + 2 * D) + pages * bt_elem_bytes + 4 * len(lens)
+
+
+def append_bytes(nnz, H, D):
+    return 2 * nnz * H * (2 * D + D // 2 + D // 16) + 8 * nnz
+
+
+def materialize_bytes(lens, ps, H, D, B):
+    pages = int(np.sum((np.asarray(lens) + ps - 1) // ps))
+    per_page = 2 * H * ps * (D // 2 + D // 16) + 2 * H * ps * D
+    return pages * per_page + 2 * H * ps * D + 12 * pages + 4 * (B + 1) + 4 * B
+
+
+# ---------------------------------------------------------------------------
+# device workloads
+# ---------------------------------------------------------------------------
+class Env:
+    def __init__(self):
+        import torch
+        import kv_cache_quantization_paged_amd as K
+        self.torch, self.K = torch, K
+        self.dev = torch.device("cuda:0")
+        self.flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
+
+    def i32(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.dev)
+
+    def gen(self, seed):
+        g = self.torch.Generator(device=self.dev)
+        g.manual_seed(seed)
+        return g
+
+    def cache(self, pages, ps, H, D, layout, seed, data_pad=0):
+        """Pool of pages filled with random bytes; returns (PagedCache, tensors)."""
+        torch = self.torch
+        g = self.gen(seed)
+        dbytes, sbytes = ps * H * D // 2, ps * H * D // 16
+        bufs = [torch.randint(0, 256, (pages * (dbytes + data_pad),), generator=g, device=self.dev,
+                              dtype=torch.uint8) for _ in range(2)]
+        sfs = [torch.randint(0, 0x7F, (pages * sbytes,), generator=g, device=self.dev, dtype=torch.uint8)
+               for _ in range(2)]
+        inner_d = (ps, H, D // 2) if layout == self.K.KVFP4_NHD else (H, ps, D // 2)
+        inner_s = (ps, H, D // 16) if layout == self.K.KVFP4_NHD else (H, ps, D // 16)
+        dview = [b.as_strided((pages,) + inner_d, (dbytes + data_pad, inner_d[1] * inner_d[2], inner_d[2], 1))
+                 for b in bufs]
+        sview = [b.view((pages,) + inner_s) for b in sfs]
+        return self.K.PagedCache(dview[0], dview[1], sview[0], sview[1], layout), (bufs, sfs, dview, sview)
+
+    def flush(self):
+        self.flush_buf.zero_()
+
+    def time_leg(self, fn, iters, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        times = []
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(iters):
+            self.flush()
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return statistics.median(times)
+
+
+def student_t3(env, shape, gen):
+    """Student-t with 3 degrees of freedom from four normals, then exactly
+    0.1% of the entries (without replacement) multiplied by 20."""
+    torch = env.torch
+    z = torch.randn(shape, generator=gen, device=env.dev)
+    c = torch.zeros(shape, device=env.dev)
+    for _ in range(3):
+        w = torch.randn(shape, generator=gen, device=env.dev)
+        c += w * w
+    x = z / torch.sqrt(c / 3.0)
+    n = x.numel()
+    k = int(round(0.001 * n))
+    idx = torch.randperm(n, generator=gen, device=env.dev)[:k]
+    x.view(-1)[idx] *= 20.0
+    return x
+
+
+class Decode:
+    """The decode workload on the device (one replica)."""
+
+    def __init__(self, env, ps=16, H=8, D=128, pool=20000, seed=1002):
+        import workloads as W
+        torch, K = env.torch, env.K
+        self.env = env
+        rng = np.random.default_rng(seed)
+        old, new_len, indices, indptr, last, bt = W.decode_append_tables(rng, 64, 4096, pool, ps)
+        a_k, a_v = W.head_scales(rng, H), W.head_scales(rng, H)
+        self.lens = new_len
+        self.B, self.T, self.H, self.D, self.ps = 64, int(new_len.max()), H, D, ps
+        self.cache, self._keep = env.cache(pool, ps, H, D, K.KVFP4_NHD, seed)
+        g = env.gen(seed)
+        n_hist = int(old.sum())
+        ak = torch.from_numpy(a_k).to(env.dev)[None, :, None]
+        av = torch.from_numpy(a_v).to(env.dev)[None, :, None]
+        hk = (torch.randn((n_hist, H, D), generator=g, device=env.dev) * ak).to(torch.bfloat16)
+        hv = (torch.randn((n_hist, H, D), generator=g, device=env.dev) * av).to(torch.bfloat16)
+        self.key = (torch.randn((64, H, D), generator=g, device=env.dev) * ak).to(torch.bfloat16)
+        self.value = (torch.randn((64, H, D), generator=g, device=env.dev) * av).to(torch.bfloat16)
+        gk = torch.empty(1, dtype=torch.float32, device=env.dev)
+        gv = torch.empty(1, dtype=torch.float32, device=env.dev)
+        K.kv_global_scale(torch.cat([hk.view(-1), self.key.view(-1)]), 448.0, gk)
+        K.kv_global_scale(torch.cat([hv.view(-1), self.value.view(-1)]), 448.0, gv)
+        self.gk_t, self.gv_t = gk, gv
+        self.gk, self.gv = float(gk.item()), float(gv.item())
+        self.indices, self.indptr, self.last = env.i32(indices), env.i32(indptr), env.i32(last)
+        hb = np.concatenate([np.full(o, b, np.int32) for b, o in enumerate(old)])
+        hp = np.concatenate([np.arange(o, dtype=np.int32) for o in old])
+        K.kv_quantize_append(self.cache, hk, hv, env.i32(hb), env.i32(hp), self.indices, self.indptr, self.last,
+                             self.gk, self.gv)
+        del hk, hv
+        self.bi = env.i32(np.arange(64))
+        self.pos = env.i32(old)
+        self.bt = env.i32(bt)
+        self.seq_lens = env.i32(new_len)
+        self.out_k = torch.empty((64, self.T, H, D), dtype=torch.bfloat16, device=env.dev)
+        self.out_v = torch.empty_like(self.out_k)
+        self.append_bytes = append_bytes(64, H, D)
+        self.dequant_bytes = dequant_bytes(new_len, ps, H, D, 4)
+
+    def append(self):
+        self.env.K.kv_quantize_append(self.cache, self.key, self.value, self.bi, self.pos, self.indices,
+                                      self.indptr, self.last, self.gk, self.gv)
+
+    def dequant(self):
+        self.env.K.kv_dequantize_paged(self.cache, self.bt, self.seq_lens, self.gk_t, self.gv_t, self.out_k,
+                                       self.out_v)
+
+
+# ---------------------------------------------------------------------------
+# legs
+# ---------------------------------------------------------------------------
+def leg_prefill_dequant(env, iters, warmup):
+    torch, K = env.torch, env.K
+    B, T, ps, H, D = 16, 8192, 32, 8, 128
+    rng = np.random.default_rng(1003)
+    n_pages = B * T // ps
+    perm = rng.permutation(n_pages)
+    cache, keep = env.cache(n_pages, ps, H, D, K.KVFP4_HND, 1003)
+    g = env.gen(1003)
+    lens = np.full(B, T)
+    indptr = env.i32(np.arange(B + 1) * (T // ps))
+    gks = []
+    rows_b = env.i32(np.repeat(np.arange(B), T))
+    rows_p = env.i32(np.tile(np.arange(T), B))
+    kv = []
+    for _ in range(2):
+        x = torch.randn((B * T, H, D), generator=g, device=env.dev).to(torch.bfloat16)
+        gt = torch.empty(1, dtype=torch.float32, device=env.dev)
+        K.kv_global_scale(x, 448.0, gt)
+        kv.append(x)
+        gks.append(gt)
+    K.kv_quantize_append(cache, kv[0], kv[1], rows_b, rows_p, env.i32(perm), indptr,
+                         env.i32(np.full(B, ps)), gks[0].item(), gks[1].item())
+    del kv
+    bt = torch.from_numpy(perm.reshape(B, T // ps).astype(np.int64)).to(env.dev)
+    ok = torch.empty((B, T, H, D), dtype=torch.float16, device=env.dev)
+    ov = torch.empty_like(ok)
+    sl = env.i32(lens)
+    ms = env.time_leg(lambda: K.kv_dequantize_paged(cache, bt, sl, gks[0], gks[1], ok, ov), iters, warmup)
+    nbytes = dequant_bytes(lens, ps, H, D, 8)
+    return {"kernel": "kv_dequantize_paged", "workload": "prefill_dequantize: 16 x 8192 tokens, page_size 32, "
+            "8 heads, head_dim 128, HND, int64 block table, fp16 out", "bytes": nbytes, "us": ms * 1e3,
+            "GBps": nbytes / (ms * 1e6), "frac": nbytes / (ms * 1e6) / PEAK_GBS}
+
+
+def leg_materialize(env, iters, warmup):
+    torch, K = env.torch, env.K
+    import workloads as W
+    ps, H, D = 16, 8, 128
+    rng = np.random.default_rng(1004)
+    lens, P, maxp, bt, indptr = W.materialize_tables(rng, 32, 128, 32768, ps, shared=False, compact=True)
+    cache, keep = env.cache(P, ps, H, D, K.KVFP4_HND, 1004, data_pad=256)
+    out = torch.empty((P + 1, 2, H, ps, D), dtype=torch.float8_e4m3fn, device=env.dev)
+    tab = torch.zeros((32, maxp), dtype=torch.int32, device=env.dev)
+    bt_t, sl, ip = env.i32(bt), env.i32(lens), env.i32(indptr)
+    mat = K.NVFP4KVMaterializer(H, ps, D, env.dev, uses_shared_paged_kv_idx=False)
+    kd, vd, ks, vs = cache.tensors
+    ms = env.time_leg(lambda: mat.run(kd, vd, ks, vs, bt_t, sl, ip, out=out, fp8_block_tables=tab), iters, warmup)
+    nbytes = materialize_bytes(lens, ps, H, D, 32)
+    return {"kernel": "kv_materialize_fp8", "workload": "materialize_fp8: 32 requests, lengths log-uniform "
+            "[128, 32768], page_size 16, 8 heads, head_dim 128, HND, data page stride 8448 B, separate K/V "
+            "tables, compact kv_page_indptr, interleaved V scales", "bytes": nbytes, "us": ms * 1e3,
+            "GBps": nbytes / (ms * 1e6), "frac": nbytes / (ms * 1e6) / PEAK_GBS}
+
+
+def leg_four_over_six(env, iters, warmup):
+    torch, K = env.torch, env.K
+    B, T, ps, H, D = 16, 4096, 64, 8, 128
+    rng = np.random.default_rng(1005)
+    n_pages = B * T // ps
+    perm = rng.permutation(n_pages)
+    cache, keep = env.cache(n_pages, ps, H, D, K.KVFP4_NHD, 1005)
+    g = env.gen(1005)
+    key = student_t3(env, (B * T, H, D), g).to(torch.bfloat16)
+    val = student_t3(env, (B * T, H, D), g).to(torch.bfloat16)
+    gk = torch.empty(1, dtype=torch.float32, device=env.dev)
+    gv = torch.empty(1, dtype=torch.float32, device=env.dev)
+    K.kv_global_scale(key, 256.0, gk)
+    K.kv_global_scale(val, 256.0, gv)
+    bi = env.i32(np.repeat(np.arange(B), T))
+    pos = env.i32(np.tile(np.arange(T), B))
+    ind = env.i32(perm)
+    ptr = env.i32(np.arange(B + 1) * (T // ps))
+    last = env.i32(np.full(B, ps))
+    res = {}
+    gkf, gvf = gk.item(), gv.item()
+    nbytes = append_bytes(B * T, H, D)
+    for name, mode in (("mse", K.KVFP4_ERR_MSE), ("mae", K.KVFP4_ERR_MAE)):
+        r = K.Recipe(256.0, mode)
+        ms = env.time_leg(lambda: K.kv_quantize_append(cache, key, val, bi, pos, ind, ptr, last, gkf, gvf, r),
+                          iters, warmup)
+        res["append_" + name] = {"kernel": "kv_quantize_append", "recipe": f"4over6 e4m3_max=256 {name.upper()}",
+                                 "bytes": nbytes, "us": ms * 1e3, "GBps": nbytes / (ms * 1e6),
+                                 "frac": nbytes / (ms * 1e6) / PEAK_GBS}
+    ms = env.time_leg(lambda: K.kv_quantize_append(cache, key, val, bi, pos, ind, ptr, last, gkf, gvf, None),
+                      iters, warmup)
+    res["append_standard"] = {"kernel": "kv_quantize_append", "recipe": "standard amax/6", "bytes": nbytes,
+                              "us": ms * 1e3, "GBps": nbytes / (ms * 1e6), "frac": nbytes / (ms * 1e6) / PEAK_GBS}
+    bt = env.i32(perm.reshape(B, T // ps))
+    ok = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=env.dev)
+    ov = torch.empty_like(ok)
+    sl = env.i32(np.full(B, T))
+    ms = env.time_leg(lambda: K.kv_dequantize_paged(cache, bt, sl, gk, gv, ok, ov), iters, warmup)
+    db = dequant_bytes(np.full(B, T), ps, H, D, 4)
+    res["dequant"] = {"kernel": "kv_dequantize_paged", "bytes": db, "us": ms * 1e3, "GBps": db / (ms * 1e6),
+                      "frac": db / (ms * 1e6) / PEAK_GBS}
+    res["workload"] = ("four_over_six_quantize: 65,536 rows (16 x 4096), 8 heads, head_dim 128, bf16 Student-t(3) "
+                       "with 0.1% entries x20, page_size 64 NHD, recipe-matched global scale")
+    return res
+
+
+def leg_copy(env, nbytes, iters, warmup):
+    torch = env.torch
+    src = torch.empty(nbytes // 2, dtype=torch.uint8, device=env.dev).fill_(1)
+    dst = torch.empty_like(src)
+    ms = env.time_leg(lambda: dst.copy_(src), iters, warmup)
+    moved = 2 * src.numel()
+    return {"kernel": "torch copy_ (device to device)", "bytes": moved, "us": ms * 1e3, "GBps": moved / (ms * 1e6),
+            "frac": moved / (ms * 1e6) / PEAK_GBS}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the decode step
+# ---------------------------------------------------------------------------
+def cpu_baseline(sample_requests: int, ps=16, H=8, D=128, pool=20000, seed=1002):
+    import oracle
+    import workloads as W
+    rng = np.random.default_rng(seed)
+    old, new_len, indices, indptr, last, bt = W.decode_append_tables(rng, 64, 4096, pool, ps)
+    a_k, a_v = W.head_scales(rng, H), W.head_scales(rng, H)
+    R = sample_requests
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    cache = W.make_cache(rng, pool, ps, H, D, W.NHD, fill="zero")
+    hist = int(old[:R].sum())
+    hk = W.f32_to_bits(W.head_scaled_normal(rng, hist, a_k, D), True)
+    hv = W.f32_to_bits(W.head_scaled_normal(rng, hist, a_v, D), True)
+    nk = W.f32_to_bits(W.head_scaled_normal(rng, R, a_k, D), True)
+    nv = W.f32_to_bits(W.head_scaled_normal(rng, R, a_v, D), True)
+    gk = oracle.global_scale(np.concatenate([hk.ravel(), nk.ravel()]), True)
+    gv = oracle.global_scale(np.concatenate([hv.ravel(), nv.ravel()]), True)
+    hb, hp = W.rows_for_positions(np.zeros(R, np.int64), old[:R])
+    # only the first R requests: truncate the CSR table to them
+    ind_r, ptr_r, last_r = indices[:indptr[R]], indptr[:R + 1], last[:R]
+    oracle.quantize_append(cache, hk, hv, True, hb, hp, ind_r, ptr_r, last_r, gk, gv, threads=threads)
+    T = int(new_len[:R].max())
+    ok = np.zeros((R, T, H, D), np.uint16)
+    ov = np.zeros_like(ok)
+    t0 = time.perf_counter()
+    oracle.quantize_append(cache, nk, nv, True, np.arange(R, dtype=np.int32), old[:R].astype(np.int32),
+                           ind_r, ptr_r, last_r, gk, gv, threads=threads)
+    oracle.dequantize_paged(cache, np.ascontiguousarray(bt[:R]), new_len[:R].astype(np.int32), gk, gv, ok, ov, True,
+                            threads=threads)
+    dt = time.perf_counter() - t0
+    nbytes = append_bytes(R, H, D) + dequant_bytes(new_len[:R], ps, H, D, 4)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"decode step restricted to the first {R} of 64 requests ({int(new_len[:R].sum())} context "
+                      f"tokens of 124,503): oracle quantize-append of their new tokens + dequantize of their "
+                      f"full context, {threads} threads"}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--leg-iters", type=int, default=50)
+    ap.add_argument("--no-legs", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged NVFP4 path needs no collectives and this build has no "
+              "multi-GPU step (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    env = Env()
+    log("bench: building the decode workload (2 replicas)")
+    reps = [Decode(env), Decode(env)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        r = reps[i % 2]
+        r.append()
+        r.dequant()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        r = reps[i % 2]
+        r.append()
+        evs[i][0].record()
+        r.dequant()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    deq_ms = [a.elapsed_time(b) for a, b in evs]
+    deq_avg = sum(deq_ms) / len(deq_ms)
+    step_bytes = reps[0].append_bytes + reps[0].dequant_bytes
+    value = step_bytes / (ms_step * 1e6)
+    achieved = reps[0].dequant_bytes / (deq_avg * 1e6)
+
+    # append latency of the decode step, timed alone
+    app_ms = env.time_leg(reps[0].append, 50, 5)
+    legs = {"decode_append_us": app_ms * 1e3,
+            "decode_dequant": {"kernel": "kv_dequantize_paged", "bytes": reps[0].dequant_bytes,
+                               "us_avg": deq_avg * 1e3, "us_median": statistics.median(deq_ms) * 1e3,
+                               "GBps": achieved, "frac": achieved / PEAK_GBS}}
+    del reps
+    torch.cuda.empty_cache()
+    if not args.no_legs:
+        log("bench: legs")
+        legs["prefill_dequantize"] = leg_prefill_dequant(env, args.leg_iters, 5)
+        torch.cuda.empty_cache()
+        legs["materialize_fp8"] = leg_materialize(env, args.leg_iters, 5)
+        torch.cuda.empty_cache()
+        legs["four_over_six_quantize"] = leg_four_over_six(env, args.leg_iters, 5)
+        torch.cuda.empty_cache()
+        legs["copy_context"] = leg_copy(env, 1 << 29, args.leg_iters, 5)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(args.cpu_sample_requests)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode_append: 64 requests x 1 new bf16 token (append) + dequantize of the full "
+                               "context (124,503 tokens, bf16 out); page_size 16, 8 KV heads, head_dim 128, NHD, "
+                               "20,000-page shuffled pool, lengths U{1..4096}+1, seed 1002",
+                   "batch": 64, "page_size": 16, "num_kv_heads": 8, "head_dim": 128, "layout": "NHD",
+                   "step_bytes": step_bytes, "peak_GBps": PEAK_GBS},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_GBS, "traffic": None,
+                     "kernel": "kv_dequantize_paged (dequant_kernel<NHD, bf16, int32 table>)"},
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

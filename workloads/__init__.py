@@ -226,6 +226,47 @@ def tiny_round_trip(seed: int = 1001) -> AppendDequant:
                          lens.astype(np.int32), int(lens.max()), True, name="tiny_round_trip")
 
 
+def decode_append_tables(rng, B: int = 64, max_old: int = 4096, pool: int = 20000, ps: int = 16):
+    """Lengths and page tables of the decode workload (first draws of its
+    seed): old lengths U{1..max_old}, one new token each, pages of a shuffled
+    pool taken in request order."""
+    old = rng.integers(1, max_old + 1, size=B).astype(np.int64)
+    new_len = old + 1
+    perm = rng.permutation(pool)
+    indices, indptr, last = csr_for_lengths(new_len, ps, perm)
+    cols = int(((new_len.max() + ps - 1) // ps))
+    bt = block_table_from_csr(indices, indptr, cols, np.int32)
+    return old, new_len, indices, indptr, last, bt
+
+
+def materialize_tables(rng, B: int = 32, lo: int = 128, hi: int = 32768, ps: int = 16, shared: bool = False,
+                       compact: bool = True):
+    """Lengths, page tables and kv_page_indptr of the materialize workload
+    (first draws of its seed): lengths log-uniform in [lo, hi], K and V pages
+    from independent permutations of the pool."""
+    lens = np.clip(np.floor(np.exp(rng.uniform(np.log(lo), np.log(hi), size=B))), lo, hi).astype(np.int64)
+    need = (lens + ps - 1) // ps
+    P = int(need.sum())
+    maxp = int(need.max())
+    permk = rng.permutation(P)
+    permv = rng.permutation(P)
+    if compact:
+        indptr = np.zeros(B + 1, np.int32)
+        indptr[1:] = np.cumsum(need)
+    else:
+        indptr = (np.arange(B + 1) * maxp).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(need)])
+    bt = np.zeros((B, maxp), np.int32) if shared else np.zeros((B, 2, maxp), np.int32)
+    for b in range(B):
+        n = need[b]
+        if shared:
+            bt[b, :n] = permk[off[b]:off[b] + n]
+        else:
+            bt[b, 0, :n] = permk[off[b]:off[b] + n]
+            bt[b, 1, :n] = permv[off[b]:off[b] + n]
+    return lens, P, maxp, bt, indptr
+
+
 def decode_append(seed: int = 1002, B: int = 64, max_old: int = 4096, pool: int = 20000,
                   ps: int = 16, H: int = 8, D: int = 128) -> AppendDequant:
     """B requests with old lengths U{1..max_old}, one new token each at
@@ -233,12 +274,7 @@ def decode_append(seed: int = 1002, B: int = 64, max_old: int = 4096, pool: int 
     times a per-head log-uniform [0.1, 10] scale (independent for K and V).
     ``history_*`` hold the rows already in the cache (quantized untimed)."""
     rng = np.random.default_rng(seed)
-    old = rng.integers(1, max_old + 1, size=B).astype(np.int64)
-    new_len = old + 1
-    perm = rng.permutation(pool)
-    indices, indptr, last = csr_for_lengths(new_len, ps, perm)
-    cols = int(((new_len.max() + ps - 1) // ps))
-    bt = block_table_from_csr(indices, indptr, cols, np.int32)
+    old, new_len, indices, indptr, last, bt = decode_append_tables(rng, B, max_old, pool, ps)
     cache = make_cache(rng, pool, ps, H, D, NHD)
     a_k, a_v = head_scales(rng, H), head_scales(rng, H)
     n_hist = int(old.sum())
@@ -332,29 +368,7 @@ def materialize_fp8(seed: int = 1004, B: int = 32, lo: int = 128, hi: int = 3276
     0x00..0x7E; K and V pages drawn from independent permutations of the
     pool (separate tables) unless ``shared``; compact kv_page_indptr."""
     rng = np.random.default_rng(seed)
-    lens = np.clip(np.floor(np.exp(rng.uniform(np.log(lo), np.log(hi), size=B))), lo, hi).astype(np.int64)
-    need = (lens + ps - 1) // ps
-    P = int(need.sum())
-    maxp = int(need.max())
-    permk = rng.permutation(P)
-    permv = rng.permutation(P)
-    if compact:
-        indptr = np.zeros(B + 1, np.int32)
-        indptr[1:] = np.cumsum(need)
-    else:
-        indptr = (np.arange(B + 1) * maxp).astype(np.int32)
-    off = np.concatenate([[0], np.cumsum(need)])
-    if shared:
-        bt = np.zeros((B, maxp), np.int32)
-    else:
-        bt = np.zeros((B, 2, maxp), np.int32)
-    for b in range(B):
-        n = need[b]
-        if shared:
-            bt[b, :n] = permk[off[b]:off[b] + n]
-        else:
-            bt[b, 0, :n] = permk[off[b]:off[b] + n]
-            bt[b, 1, :n] = permv[off[b]:off[b] + n]
+    lens, P, maxp, bt, indptr = materialize_tables(rng, B, lo, hi, ps, shared, compact)
     cache = make_cache(rng, P, ps, H, D, HND, data_pad=data_pad, fill="zero")
     for a in (cache.k_data, cache.v_data):
         a[...] = rng.integers(0, 256, size=a.shape, dtype=np.uint8)
