@@ -8,9 +8,9 @@ value = algorithmic bytes of the step / wall time of the step, with all
 inputs resident in HBM; two replicas of the workload alternate so that
 consecutive steps touch disjoint memory.
 
-Legs (same JSON line, each kernel timed alone, median of HIP-event times with
-a 1 GiB write between iterations so nothing is served from the 256 MB
-Infinity Cache): prefill dequantize (16 x 8192 tokens, HND, int64 table, fp16
+Legs (same JSON line; each kernel launched back to back on two replicas of
+its workload in disjoint memory, mean of the per-launch HIP-event times, the
+same steady state as the headline step): prefill dequantize (16 x 8192 tokens, HND, int64 table, fp16
 out), materialize-FP8 (32 requests, log-uniform lengths, padded pages,
 separate K/V tables), 4over6 quantize-append (65,536 rows, Student-t(3) with
 0.1% outliers x20, MSE and MAE) and its dequantize, and a plain
@@ -69,7 +69,6 @@ class Env:
         import kv_cache_quantization_paged_amd as K
         self.torch, self.K = torch, K
         self.dev = torch.device("cuda:0")
-        self.flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
 
     def i32(self, a):
         return self.torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.dev)
@@ -95,24 +94,26 @@ class Env:
         sview = [b.view((pages,) + inner_s) for b in sfs]
         return self.K.PagedCache(dview[0], dview[1], sview[0], sview[1], layout), (bufs, sfs, dview, sview)
 
-    def flush(self):
-        self.flush_buf.zero_()
-
-    def time_leg(self, fn, iters, warmup):
+    def steady(self, fns, iters, warmup):
+        """Launch fns[i % len(fns)] back to back (replicas in disjoint memory,
+        so nothing is reused from the 256 MB Infinity Cache) and return the
+        (mean, median) in ms of the per-launch HIP-event times. In this
+        steady state each launch also pays the write-back its predecessor left
+        dirty in the cache, as a serving loop does; a kernel timed alone after
+        a flush would leave up to 256 MB of its own output unwritten when its
+        end event fires."""
         torch = self.torch
-        for _ in range(warmup):
-            fn()
-        times = []
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(iters):
-            self.flush()
-            e0.record()
-            fn()
-            e1.record()
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
-        return statistics.median(times)
+        for i in range(warmup):
+            fns[i % len(fns)]()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            evs[i][0].record()
+            fns[i % len(fns)]()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in evs]
+        return statistics.mean(ts), statistics.median(ts)
 
 
 def student_t3(env, shape, gen):
@@ -184,70 +185,83 @@ class Decode:
 
 
 # ---------------------------------------------------------------------------
-# legs
+# legs: each kernel in steady state, alternating two replicas of its workload
 # ---------------------------------------------------------------------------
-def leg_prefill_dequant(env, iters, warmup):
+def prefill_replica(env, seed=1003):
     torch, K = env.torch, env.K
     B, T, ps, H, D = 16, 8192, 32, 8, 128
-    rng = np.random.default_rng(1003)
+    rng = np.random.default_rng(seed)
     n_pages = B * T // ps
     perm = rng.permutation(n_pages)
-    cache, keep = env.cache(n_pages, ps, H, D, K.KVFP4_HND, 1003)
-    g = env.gen(1003)
-    lens = np.full(B, T)
-    indptr = env.i32(np.arange(B + 1) * (T // ps))
-    gks = []
+    cache, keep = env.cache(n_pages, ps, H, D, K.KVFP4_HND, seed)
+    g = env.gen(seed)
     rows_b = env.i32(np.repeat(np.arange(B), T))
     rows_p = env.i32(np.tile(np.arange(T), B))
-    kv = []
+    kv, gks = [], []
     for _ in range(2):
         x = torch.randn((B * T, H, D), generator=g, device=env.dev).to(torch.bfloat16)
         gt = torch.empty(1, dtype=torch.float32, device=env.dev)
         K.kv_global_scale(x, 448.0, gt)
         kv.append(x)
         gks.append(gt)
-    K.kv_quantize_append(cache, kv[0], kv[1], rows_b, rows_p, env.i32(perm), indptr,
+    K.kv_quantize_append(cache, kv[0], kv[1], rows_b, rows_p, env.i32(perm), env.i32(np.arange(B + 1) * (T // ps)),
                          env.i32(np.full(B, ps)), gks[0].item(), gks[1].item())
     del kv
     bt = torch.from_numpy(perm.reshape(B, T // ps).astype(np.int64)).to(env.dev)
     ok = torch.empty((B, T, H, D), dtype=torch.float16, device=env.dev)
     ov = torch.empty_like(ok)
-    sl = env.i32(lens)
-    ms = env.time_leg(lambda: K.kv_dequantize_paged(cache, bt, sl, gks[0], gks[1], ok, ov), iters, warmup)
-    nbytes = dequant_bytes(lens, ps, H, D, 8)
-    return {"kernel": "kv_dequantize_paged", "workload": "prefill_dequantize: 16 x 8192 tokens, page_size 32, "
-            "8 heads, head_dim 128, HND, int64 block table, fp16 out", "bytes": nbytes, "us": ms * 1e3,
-            "GBps": nbytes / (ms * 1e6), "frac": nbytes / (ms * 1e6) / PEAK_GBS}
+    sl = env.i32(np.full(B, T))
+    nbytes = dequant_bytes(np.full(B, T), ps, H, D, 8)
+    return (lambda: K.kv_dequantize_paged(cache, bt, sl, gks[0], gks[1], ok, ov)), nbytes, (cache, keep, ok, ov)
 
 
-def leg_materialize(env, iters, warmup):
+def leg_prefill_dequant(env, iters, warmup):
+    fns, keep = [], []
+    for _ in range(2):
+        fn, nbytes, k = prefill_replica(env)
+        fns.append(fn)
+        keep.append(k)
+    r = env.steady(fns, iters, warmup)
+    return dict(kernel="kv_dequantize_paged", workload="prefill_dequantize: 16 x 8192 tokens, page_size 32, "
+                "8 heads, head_dim 128, HND, int64 block table, fp16 out", bytes=nbytes, **rates(nbytes, r))
+
+
+def materialize_replica(env, seed=1004):
     torch, K = env.torch, env.K
     import workloads as W
     ps, H, D = 16, 8, 128
-    rng = np.random.default_rng(1004)
+    rng = np.random.default_rng(seed)
     lens, P, maxp, bt, indptr = W.materialize_tables(rng, 32, 128, 32768, ps, shared=False, compact=True)
-    cache, keep = env.cache(P, ps, H, D, K.KVFP4_HND, 1004, data_pad=256)
+    cache, keep = env.cache(P, ps, H, D, K.KVFP4_HND, seed, data_pad=256)
     out = torch.empty((P + 1, 2, H, ps, D), dtype=torch.float8_e4m3fn, device=env.dev)
     tab = torch.zeros((32, maxp), dtype=torch.int32, device=env.dev)
     bt_t, sl, ip = env.i32(bt), env.i32(lens), env.i32(indptr)
     mat = K.NVFP4KVMaterializer(H, ps, D, env.dev, uses_shared_paged_kv_idx=False)
     kd, vd, ks, vs = cache.tensors
-    ms = env.time_leg(lambda: mat.run(kd, vd, ks, vs, bt_t, sl, ip, out=out, fp8_block_tables=tab), iters, warmup)
     nbytes = materialize_bytes(lens, ps, H, D, 32)
-    return {"kernel": "kv_materialize_fp8", "workload": "materialize_fp8: 32 requests, lengths log-uniform "
-            "[128, 32768], page_size 16, 8 heads, head_dim 128, HND, data page stride 8448 B, separate K/V "
-            "tables, compact kv_page_indptr, interleaved V scales", "bytes": nbytes, "us": ms * 1e3,
-            "GBps": nbytes / (ms * 1e6), "frac": nbytes / (ms * 1e6) / PEAK_GBS}
+    return (lambda: mat.run(kd, vd, ks, vs, bt_t, sl, ip, out=out, fp8_block_tables=tab)), nbytes, (cache, keep, out)
 
 
-def leg_four_over_six(env, iters, warmup):
+def leg_materialize(env, iters, warmup):
+    fns, keep = [], []
+    for _ in range(2):
+        fn, nbytes, k = materialize_replica(env)
+        fns.append(fn)
+        keep.append(k)
+    r = env.steady(fns, iters, warmup)
+    return dict(kernel="kv_materialize_fp8", workload="materialize_fp8: 32 requests, lengths log-uniform "
+                "[128, 32768], page_size 16, 8 heads, head_dim 128, HND, data page stride 8448 B, separate K/V "
+                "tables, compact kv_page_indptr, interleaved V scales", bytes=nbytes, **rates(nbytes, r))
+
+
+def four_over_six_replica(env, seed=1005):
     torch, K = env.torch, env.K
     B, T, ps, H, D = 16, 4096, 64, 8, 128
-    rng = np.random.default_rng(1005)
+    rng = np.random.default_rng(seed)
     n_pages = B * T // ps
     perm = rng.permutation(n_pages)
-    cache, keep = env.cache(n_pages, ps, H, D, K.KVFP4_NHD, 1005)
-    g = env.gen(1005)
+    cache, keep = env.cache(n_pages, ps, H, D, K.KVFP4_NHD, seed)
+    g = env.gen(seed)
     key = student_t3(env, (B * T, H, D), g).to(torch.bfloat16)
     val = student_t3(env, (B * T, H, D), g).to(torch.bfloat16)
     gk = torch.empty(1, dtype=torch.float32, device=env.dev)
@@ -259,41 +273,54 @@ def leg_four_over_six(env, iters, warmup):
     ind = env.i32(perm)
     ptr = env.i32(np.arange(B + 1) * (T // ps))
     last = env.i32(np.full(B, ps))
-    res = {}
     gkf, gvf = gk.item(), gv.item()
-    nbytes = append_bytes(B * T, H, D)
-    for name, mode in (("mse", K.KVFP4_ERR_MSE), ("mae", K.KVFP4_ERR_MAE)):
-        r = K.Recipe(256.0, mode)
-        ms = env.time_leg(lambda: K.kv_quantize_append(cache, key, val, bi, pos, ind, ptr, last, gkf, gvf, r),
-                          iters, warmup)
-        res["append_" + name] = {"kernel": "kv_quantize_append", "recipe": f"4over6 e4m3_max=256 {name.upper()}",
-                                 "bytes": nbytes, "us": ms * 1e3, "GBps": nbytes / (ms * 1e6),
-                                 "frac": nbytes / (ms * 1e6) / PEAK_GBS}
-    ms = env.time_leg(lambda: K.kv_quantize_append(cache, key, val, bi, pos, ind, ptr, last, gkf, gvf, None),
-                      iters, warmup)
-    res["append_standard"] = {"kernel": "kv_quantize_append", "recipe": "standard amax/6", "bytes": nbytes,
-                              "us": ms * 1e3, "GBps": nbytes / (ms * 1e6), "frac": nbytes / (ms * 1e6) / PEAK_GBS}
     bt = env.i32(perm.reshape(B, T // ps))
     ok = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=env.dev)
     ov = torch.empty_like(ok)
     sl = env.i32(np.full(B, T))
-    ms = env.time_leg(lambda: K.kv_dequantize_paged(cache, bt, sl, gk, gv, ok, ov), iters, warmup)
+    fns = {}
+    for name, recipe in (("mse", K.Recipe(256.0, K.KVFP4_ERR_MSE)), ("mae", K.Recipe(256.0, K.KVFP4_ERR_MAE)),
+                         ("standard", None)):
+        fns["append_" + name] = (lambda r=recipe: K.kv_quantize_append(cache, key, val, bi, pos, ind, ptr, last,
+                                                                       gkf, gvf, r))
+    fns["dequant"] = lambda: K.kv_dequantize_paged(cache, bt, sl, gk, gv, ok, ov)
+    return fns, (cache, keep, key, val, ok, ov, bi, pos, ind, ptr, last, bt, sl, gk, gv)
+
+
+def leg_four_over_six(env, iters, warmup):
+    torch = env.torch
+    reps = [four_over_six_replica(env) for _ in range(2)]
+    B, T, H, D, ps = 16, 4096, 8, 128, 64
+    res = {}
+    ab = append_bytes(B * T, H, D)
+    for name, recipe in (("mse", "4over6 e4m3_max=256 MSE"), ("mae", "4over6 e4m3_max=256 MAE"),
+                         ("standard", "standard amax/6")):
+        r = env.steady([rep[0]["append_" + name] for rep in reps], iters, warmup)
+        res["append_" + name] = dict(kernel="kv_quantize_append", recipe=recipe, bytes=ab, **rates(ab, r))
     db = dequant_bytes(np.full(B, T), ps, H, D, 4)
-    res["dequant"] = {"kernel": "kv_dequantize_paged", "bytes": db, "us": ms * 1e3, "GBps": db / (ms * 1e6),
-                      "frac": db / (ms * 1e6) / PEAK_GBS}
+    r = env.steady([rep[0]["dequant"] for rep in reps], iters, warmup)
+    res["dequant"] = dict(kernel="kv_dequantize_paged", bytes=db, **rates(db, r))
     res["workload"] = ("four_over_six_quantize: 65,536 rows (16 x 4096), 8 heads, head_dim 128, bf16 Student-t(3) "
                        "with 0.1% entries x20, page_size 64 NHD, recipe-matched global scale")
+    del reps
+    torch.cuda.empty_cache()
     return res
 
 
 def leg_copy(env, nbytes, iters, warmup):
     torch = env.torch
-    src = torch.empty(nbytes // 2, dtype=torch.uint8, device=env.dev).fill_(1)
-    dst = torch.empty_like(src)
-    ms = env.time_leg(lambda: dst.copy_(src), iters, warmup)
-    moved = 2 * src.numel()
-    return {"kernel": "torch copy_ (device to device)", "bytes": moved, "us": ms * 1e3, "GBps": moved / (ms * 1e6),
-            "frac": moved / (ms * 1e6) / PEAK_GBS}
+    pairs = []
+    for _ in range(2):
+        src = torch.ones(nbytes // 2, dtype=torch.uint8, device=env.dev)
+        pairs.append((src, torch.empty_like(src)))
+    r = env.steady([(lambda s=s, d=d: d.copy_(s)) for s, d in pairs], iters, warmup)
+    return dict(kernel="torch copy_ (device to device)", bytes=nbytes, **rates(nbytes, r))
+
+
+def rates(nbytes, r):
+    avg, med = r
+    return {"us_avg": avg * 1e3, "us_median": med * 1e3, "GBps": nbytes / (avg * 1e6),
+            "frac": nbytes / (avg * 1e6) / PEAK_GBS}
 
 
 # ---------------------------------------------------------------------------
@@ -385,8 +412,8 @@ def main():
     value = step_bytes / (ms_step * 1e6)
     achieved = reps[0].dequant_bytes / (deq_avg * 1e6)
 
-    # append latency of the decode step, timed alone
-    app_ms = env.time_leg(reps[0].append, 50, 5)
+    # append latency of the decode step, back to back
+    app_ms = env.steady([r.append for r in reps], 50, 5)[0]
     legs = {"decode_append_us": app_ms * 1e3,
             "decode_dequant": {"kernel": "kv_dequantize_paged", "bytes": reps[0].dequant_bytes,
                                "us_avg": deq_avg * 1e3, "us_median": statistics.median(deq_ms) * 1e3,

@@ -3,19 +3,22 @@
 // the "NVFP4 4over6 Recipes" section of the flashinfer.quantization page).
 //
 // One lane owns one 16-element block of one (row, head) of K or V: it loads
-// the block's 32 input bytes (two 16-byte loads, consecutive lanes read
-// consecutive blocks of a row), reduces amax in registers, derives the E4M3
+// the block's 32 input bytes, reduces amax in registers, derives the E4M3
 // block scale, encodes 16 E2M1 codes and stores 8 packed bytes plus the scale
 // byte at (page, slot) from the CSR table. The 4over6 recipe evaluates both
-// candidates in the same lane: no cross-lane traffic at all.
+// candidates in the same lane: no cross-lane traffic.
 //
 // fp32 order (bit-exact with the reference reading):
 //   sf  = amax / fp32(C * g)                 (IEEE division)
 //   s   = E4M3_RNE(min(sf, clamp_C))
 //   dec = fp32(E4M3(s) * g),  inv = dec ? fp32(1 / dec) : 0
-//   q_i = nearest E2M1 magnitude of |x_i| * inv, sign from x_i
-//   4over6: d_i = |x_i| - fp32(dec * q_i); MSE d_i*d_i or MAE |d_i|; pairwise
-//   tree over the 16 terms; amax/4 kept only when strictly lower.
+//   c_i = E2M1_RNE_sat(fp32(x_i * inv))
+//   4over6: d_i = x_i - fp32(dec * e2m1(c_i)); MSE d_i*d_i or MAE |d_i|;
+//   pairwise tree over the 16 terms; amax/4 kept only when strictly lower.
+// dec and inv depend only on (tensor, scale byte): each workgroup tabulates
+// them for the 127 finite non-negative scale bytes in LDS at start, so a block
+// pays one IEEE division (for sf) per candidate and two LDS reads. The E2M1
+// encode / decode and the E4M3 encode use gfx950's conversion instructions.
 #include "kvfp4_internal.h"
 #include "nvfp4_device.h"
 
@@ -39,6 +42,11 @@ struct AppendArgs {
     int32_t err_mode;  // 0 MSE, 1 MAE
 };
 
+struct ScaleTables {
+    float dec[2][128];
+    float inv[2][128];
+};
+
 template <bool BF16>
 __device__ __forceinline__ void load_block(const uint8_t *p, float x[16])
 {
@@ -52,35 +60,42 @@ __device__ __forceinline__ void load_block(const uint8_t *p, float x[16])
     }
 }
 
-struct Candidate {
-    uint32_t s;
-    float dec, inv;
-};
-
-__device__ __forceinline__ Candidate make_candidate(float amax, float t, float clamp, float g)
+// E2M1 codes of fp32(x_i * inv), packed two per byte, element 0 lowest
+__device__ __forceinline__ uint2 encode16(const float x[16], float inv)
 {
-    Candidate c;
-    const float sf = amax / t;
-    c.s = f32_to_e4m3_rne(fminf(sf, clamp));
-    c.dec = e4m3_to_f32(c.s) * g;
-    c.inv = (c.dec == 0.0f) ? 0.0f : 1.0f / c.dec;
-    return c;
+    uint32_t w0 = 0u, w1 = 0u;
+    w0 = f32x2_to_fp4x2<0>(w0, x[0] * inv, x[1] * inv);
+    w0 = f32x2_to_fp4x2<1>(w0, x[2] * inv, x[3] * inv);
+    w0 = f32x2_to_fp4x2<2>(w0, x[4] * inv, x[5] * inv);
+    w0 = f32x2_to_fp4x2<3>(w0, x[6] * inv, x[7] * inv);
+    w1 = f32x2_to_fp4x2<0>(w1, x[8] * inv, x[9] * inv);
+    w1 = f32x2_to_fp4x2<1>(w1, x[10] * inv, x[11] * inv);
+    w1 = f32x2_to_fp4x2<2>(w1, x[12] * inv, x[13] * inv);
+    w1 = f32x2_to_fp4x2<3>(w1, x[14] * inv, x[15] * inv);
+    return make_uint2(w0, w1);
 }
 
-// 16 magnitudes + the signs of x -> two packed code dwords
-__device__ __forceinline__ uint2 pack_codes(const float q[16], const float x[16])
+// terms of one packed dword (8 elements starting at x[0])
+template <bool MSE>
+__device__ __forceinline__ void terms8(const float *x, uint32_t w, float dec, float t[8])
 {
-    uint32_t w[2] = {0u, 0u};
+    const f32x2 v0 = fp4x2_to_f32x2<0>(w), v1 = fp4x2_to_f32x2<1>(w);
+    const f32x2 v2 = fp4x2_to_f32x2<2>(w), v3 = fp4x2_to_f32x2<3>(w);
+    const float v[8] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t k = e2m1_mag_to_code(q[i]) | ((__float_as_uint(x[i]) >> 28) & 8u);
-        w[i >> 3] |= k << (4 * (i & 7));
+    for (int i = 0; i < 8; ++i) {
+        const float d = x[i] - dec * v[i];
+        t[i] = MSE ? d * d : fabsf(d);
     }
-    return make_uint2(w[0], w[1]);
 }
 
-__device__ __forceinline__ float tree16(float t[16])
+// summed error of a candidate: pairwise tree over the 16 terms in index order
+template <bool MSE>
+__device__ __forceinline__ float block_error(const float x[16], uint2 codes, float dec)
 {
+    float t[16];
+    terms8<MSE>(x, codes.x, dec, t);
+    terms8<MSE>(x + 8, codes.y, dec, t + 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i) t[i] = t[2 * i] + t[2 * i + 1];
 #pragma unroll
@@ -90,9 +105,10 @@ __device__ __forceinline__ float tree16(float t[16])
     return t[0] + t[1];
 }
 
-template <bool BF16, bool FOUR_OVER_SIX>
-__device__ __forceinline__ void quantize_one(const AppendArgs &a, int kv, int64_t r, int h, int c,
-                                             int64_t page, int slot, bool hnd, int err_mode)
+// RECIPE: 0 standard, 1 4over6 MSE, 2 4over6 MAE
+template <bool BF16, int RECIPE>
+__device__ __forceinline__ void quantize_one(const AppendArgs &a, const ScaleTables &tab, int kv, int64_t r, int h,
+                                             int c, int64_t page, int slot, bool hnd)
 {
     const int nb = a.D >> 4;
     float x[16];
@@ -102,45 +118,46 @@ __device__ __forceinline__ void quantize_one(const AppendArgs &a, int kv, int64_
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
     const float g = a.g[kv];
 
-    uint32_t s;
-    float q[16];
-    const Candidate c6 = make_candidate(amax, 6.0f * g, a.clamp6, g);
-    if (!FOUR_OVER_SIX) {
-        s = c6.s;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) q[i] = e2m1_round_mag(fabsf(x[i]) * c6.inv);
-    } else {
-        const Candidate c4 = make_candidate(amax, 4.0f * g, 448.0f, g);
-        float q6[16], q4[16], t6[16], t4[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float ax = fabsf(x[i]);
-            q6[i] = e2m1_round_mag(ax * c6.inv);
-            q4[i] = e2m1_round_mag(ax * c4.inv);
-            const float d6 = ax - c6.dec * q6[i];
-            const float d4 = ax - c4.dec * q4[i];
-            t6[i] = err_mode == 0 ? d6 * d6 : fabsf(d6);
-            t4[i] = err_mode == 0 ? d4 * d4 : fabsf(d4);
+    const float sf6 = amax / (6.0f * g);
+    uint32_t s = f32_to_e4m3_hw(fminf(sf6, a.clamp6));
+    float dec = tab.dec[kv][s];
+    uint2 codes = encode16(x, tab.inv[kv][s]);
+    if (RECIPE != 0) {
+        const float sf4 = amax / (4.0f * g);
+        const uint32_t s4 = f32_to_e4m3_hw(fminf(sf4, 448.0f));
+        const float dec4 = tab.dec[kv][s4];
+        const uint2 codes4 = encode16(x, tab.inv[kv][s4]);
+        const float e6 = block_error<RECIPE == 1>(x, codes, dec);
+        const float e4 = block_error<RECIPE == 1>(x, codes4, dec4);
+        if (e4 < e6) {
+            s = s4;
+            codes = codes4;
         }
-        const float e6 = tree16(t6);
-        const float e4 = tree16(t4);
-        const bool take4 = e4 < e6;
-        s = take4 ? c4.s : c6.s;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) q[i] = take4 ? q4[i] : q6[i];
     }
-    const uint2 packed = pack_codes(q, x);
     const int64_t row = hnd ? ((int64_t)h * a.ps + slot) : ((int64_t)slot * a.H + h);
-    *(uint2 *)(a.data[kv] + page * a.stride[kv] + row * (a.D >> 1) + c * 8) = packed;
+    *(uint2 *)(a.data[kv] + page * a.stride[kv] + row * (a.D >> 1) + c * 8) = codes;
     a.sf[kv][page * a.sf_stride[kv] + row * nb + c] = (uint8_t)s;
 }
 
-template <bool BF16, bool FOUR_OVER_SIX, bool HND>
-__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a)
+// At least 6 workgroups (24 waves) per CU: caps the 4over6 kernels at 80
+// VGPRs without spilling, which hides more memory latency than the default
+// allocation (98 VGPRs, 4 waves per SIMD) does.
+template <bool BF16, int RECIPE, bool HND>
+__global__ __launch_bounds__(kThreads, 6) void append_kernel(AppendArgs a)
 {
+    __shared__ ScaleTables tab;
+    const int tid = threadIdx.x;
+    {
+        // decode factor and its reciprocal for (tensor, scale byte)
+        const int kv = tid >> 7, s = tid & 127;
+        const float dec = e4m3_byte_to_f32((uint32_t)s) * a.g[kv];
+        tab.dec[kv][s] = dec;
+        tab.inv[kv][s] = (dec == 0.0f) ? 0.0f : 1.0f / dec;
+    }
+    __syncthreads();
+
     const int nb = a.D >> 4;
     const int bpr = a.H * nb;                         // blocks per row (all heads)
-    const int tid = threadIdx.x;
     if (bpr <= kThreads) {
         const int rows_per_iter = kThreads / bpr;
         const int row_off = tid / bpr;
@@ -154,8 +171,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a)
             const int p = a.positions[r];
             const int64_t page = a.kv_indices[a.kv_indptr[b] + p / a.ps];
             const int slot = p % a.ps;
-            quantize_one<BF16, FOUR_OVER_SIX>(a, 0, r, h, c, page, slot, HND, a.err_mode);
-            quantize_one<BF16, FOUR_OVER_SIX>(a, 1, r, h, c, page, slot, HND, a.err_mode);
+            quantize_one<BF16, RECIPE>(a, tab, 0, r, h, c, page, slot, HND);
+            quantize_one<BF16, RECIPE>(a, tab, 1, r, h, c, page, slot, HND);
         }
     } else {
         for (int64_t r = blockIdx.x; r < a.nnz; r += gridDim.x) {
@@ -165,21 +182,31 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a)
             const int slot = p % a.ps;
             for (int hc = tid; hc < bpr; hc += kThreads) {
                 const int h = hc / nb, c = hc - (hc / nb) * nb;
-                quantize_one<BF16, FOUR_OVER_SIX>(a, 0, r, h, c, page, slot, HND, a.err_mode);
-                quantize_one<BF16, FOUR_OVER_SIX>(a, 1, r, h, c, page, slot, HND, a.err_mode);
+                quantize_one<BF16, RECIPE>(a, tab, 0, r, h, c, page, slot, HND);
+                quantize_one<BF16, RECIPE>(a, tab, 1, r, h, c, page, slot, HND);
             }
         }
     }
 }
 
-template <bool BF16, bool F46>
+template <bool BF16, int RECIPE>
 hipError_t launch2(bool hnd, const AppendArgs &a, int grid, hipStream_t st)
 {
     if (hnd)
-        hipLaunchKernelGGL((append_kernel<BF16, F46, true>), dim3(grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((append_kernel<BF16, RECIPE, true>), dim3(grid), dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((append_kernel<BF16, F46, false>), dim3(grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((append_kernel<BF16, RECIPE, false>), dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch1(int recipe, bool hnd, const AppendArgs &a, int grid, hipStream_t st)
+{
+    if (recipe == 1)
+        return launch2<BF16, 1>(hnd, a, grid, st);
+    if (recipe == 2)
+        return launch2<BF16, 2>(hnd, a, grid, st);
+    return launch2<BF16, 0>(hnd, a, grid, st);
 }
 
 }  // namespace
@@ -220,10 +247,8 @@ hipError_t launch_quantize_append(const kvfp4_paged_cache_t &c, const void *key,
     const int64_t wgs = (nnz + rows_per_wg - 1) / rows_per_wg;
     const int grid = (int)(wgs < kPersistentWorkgroups ? wgs : kPersistentWorkgroups);
     const bool hnd = c.layout == KVFP4_HND;
-    const bool f46 = recipe != nullptr;
-    if (in_bf16)
-        return f46 ? launch2<true, true>(hnd, a, grid, st) : launch2<true, false>(hnd, a, grid, st);
-    return f46 ? launch2<false, true>(hnd, a, grid, st) : launch2<false, false>(hnd, a, grid, st);
+    const int rk = recipe == nullptr ? 0 : (recipe->err_mode == KVFP4_ERR_MSE ? 1 : 2);
+    return in_bf16 ? launch1<true>(rk, hnd, a, grid, st) : launch1<false>(rk, hnd, a, grid, st);
 }
 
 }  // namespace kvfp4

@@ -1,17 +1,24 @@
 // dequant.hip - paged NVFP4 gather-dequantize for gfx950
 // (FlashInfer page flashinfer.quantization.nvfp4_kv_dequantize_paged).
 //
-// Work item ("tile"): one logical page j of one request b for K or for V.
-// Its output rows out[b, j*ps + t, h, :] (t < tokens of the page, every head)
-// are one contiguous run of n_tok*H*D 16-bit values, so every wavefront store
-// is a coalesced 16-byte-per-lane stream whatever the cache layout; the NHD/HND
-// difference is only where a lane reads its 8 code bytes and scale byte.
-// A persistent grid walks the B * ceil(T/ps) * 2 tiles; tiles past a request's
-// length cost a few scalar instructions and are skipped.
+// Work item: one logical page j of one request b, K and V together (one
+// block-table lookup for both). The page's output rows out[b, j*ps + t, h, :]
+// (t < tokens of the page, every head) are one contiguous run of n_tok*H*D
+// 16-bit values, so lane l of a wavefront always stores the 16 bytes right
+// after lane l-1: each store instruction writes 1 KiB of contiguous HBM
+// whatever the cache layout. A lane owns 8 consecutive outputs per chunk:
+// 4 code bytes and its block's scale byte in, 16 bytes out. NHD vs HND only
+// changes where a chunk's code bytes are read. The grid has one workgroup per
+// (request, page) pair of the B * ceil(T/ps) table; workgroups past a
+// request's length exit at once. Active pages are scattered through that
+// table when lengths differ, and a persistent loop over it leaves some
+// workgroups with several times the work of others; one workgroup per pair
+// lets the dispatcher keep every CU busy.
 //
-// Per lane and per 16-element block: 8 code bytes + 1 scale byte in, 32 bytes
-// out. value = RNE16(fp32(fp32(E4M3(s) * g) * e2m1(c))); the product order is
-// the one the oracle states (scale times global first).
+// value = RNE16(fp32(fp32(E4M3(s) * g) * e2m1(c))): the scale and the codes
+// are decoded by gfx950's conversion instructions (exact: E4M3 -> fp32, and
+// FP4 -> fp32 with a unit scale), then two fp32 multiplies in that order and
+// one round-to-nearest-even conversion per value.
 #include "kvfp4_internal.h"
 #include "nvfp4_device.h"
 
@@ -20,7 +27,8 @@ namespace kvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kBatch = 8;            // chunks in flight per lane
+constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid size in work-items stays below 2^32)
 
 struct DequantArgs {
     const uint8_t *data[2];
@@ -34,46 +42,49 @@ struct DequantArgs {
     uint16_t *out[2];
     int32_t ps, H, D, T;
     int32_t pages_per_req;   // ceil(T / ps)
-    int64_t num_tiles;       // B * pages_per_req * 2
+    int32_t num_pairs;       // B * pages_per_req
 };
 
-// 8 code bytes (16 elements) -> 8 packed 16-bit pairs
+// 4 code bytes (8 values) -> 4 packed 16-bit pairs
 template <bool BF16>
-__device__ __forceinline__ void decode_block(uint32_t c0, uint32_t c1, float dec, uint32_t out[8])
+__device__ __forceinline__ uint4 decode_chunk(uint32_t codes, float dec)
 {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const uint32_t c = w ? c1 : c0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = (c >> (8 * i)) & 0xFu;
-            const uint32_t hi = (c >> (8 * i + 4)) & 0xFu;
-            float ylo = dec * e2m1_code_to_mag(lo & 7u);
-            float yhi = dec * e2m1_code_to_mag(hi & 7u);
-            ylo = __uint_as_float(__float_as_uint(ylo) ^ ((lo & 8u) << 28));
-            yhi = __uint_as_float(__float_as_uint(yhi) ^ ((hi & 8u) << 28));
-            out[w * 4 + i] = BF16 ? pack_bf16x2(ylo, yhi) : pack_f16x2(ylo, yhi);
-        }
+    const f32x2 v0 = fp4x2_to_f32x2<0>(codes);
+    const f32x2 v1 = fp4x2_to_f32x2<1>(codes);
+    const f32x2 v2 = fp4x2_to_f32x2<2>(codes);
+    const f32x2 v3 = fp4x2_to_f32x2<3>(codes);
+    uint4 r;
+    if (BF16) {
+        r.x = pack_bf16x2(dec * v0.x, dec * v0.y);
+        r.y = pack_bf16x2(dec * v1.x, dec * v1.y);
+        r.z = pack_bf16x2(dec * v2.x, dec * v2.y);
+        r.w = pack_bf16x2(dec * v3.x, dec * v3.y);
+    } else {
+        r.x = pack_f16x2(dec * v0.x, dec * v0.y);
+        r.y = pack_f16x2(dec * v1.x, dec * v1.y);
+        r.z = pack_f16x2(dec * v2.x, dec * v2.y);
+        r.w = pack_f16x2(dec * v3.x, dec * v3.y);
     }
+    return r;
 }
 
 template <bool HND, bool BF16, bool BT64>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a)
 {
-    const int nb = a.D >> 4;                       // blocks per (token, head) row
-    const int rows_per_iter = kThreads / nb;       // rows the workgroup covers per step
+    const int cpr = a.D >> 3;                  // chunks per (token, head) row
+    const int nb = a.D >> 4;
     const int tid = threadIdx.x;
-    const bool lane_active = tid < rows_per_iter * nb;
-    const int c = tid % nb;
-    const int row0 = tid / nb;
-    const int t_step = rows_per_iter / a.H, h_step = rows_per_iter % a.H;
-    const float g0 = *a.scale[0], g1 = *a.scale[1];
+    // mixed-radix position of chunk (tid + 256 k): row advances by r_step (+1
+    // on a carry from cc), and the row's (t, h) follow
+    const int r_step = kThreads / cpr, c_step = kThreads - r_step * cpr;
+    const int rt_step = r_step / a.H, rh_step = r_step - rt_step * a.H;
+    const float g[2] = {*a.scale[0], *a.scale[1]};
 
-    for (int64_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
-        const int kv = (int)(tile & 1);
-        const int64_t bj = tile >> 1;
-        const int b = (int)(bj / a.pages_per_req);
-        const int j = (int)(bj - (int64_t)b * a.pages_per_req);
+    // one pair per workgroup (the loop only repeats for tables of more than
+    // kMaxGrid pairs)
+    for (int pair = blockIdx.x; pair < a.num_pairs; pair += gridDim.x) {
+        const int b = pair / a.pages_per_req;
+        const int j = pair - b * a.pages_per_req;
         const int len = min(a.seq_lens[b], a.T);
         const int t_first = j * a.ps;
         if (t_first >= len)
@@ -81,44 +92,45 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a)
         const int n_tok = min(a.ps, len - t_first);
         const int64_t page = BT64 ? ((const int64_t *)a.block_tables)[b * a.bt_row_stride + j]
                                   : (int64_t)((const int32_t *)a.block_tables)[b * a.bt_row_stride + j];
-        const uint8_t *src = a.data[kv] + page * a.stride[kv];
-        const uint8_t *sfs = a.sf[kv] + page * a.sf_stride[kv];
-        uint16_t *dst = a.out[kv] + ((int64_t)b * a.T + t_first) * a.H * a.D;
-        const float g = kv ? g1 : g0;
-        const int n_rows = n_tok * a.H;
-        if (!lane_active)
-            continue;
-
-        // (t, h) of this lane's first row, advanced incrementally
-        int t = row0 / a.H, h = row0 - (row0 / a.H) * a.H;
-        for (int row = row0; row < n_rows; row += kUnroll * rows_per_iter) {
-            uint2 codes[kUnroll];
-            uint32_t sbyte[kUnroll];
-            int rows[kUnroll];
+        const int n_chunks = n_tok * a.H * cpr;
+        const int64_t out_off = ((int64_t)b * a.T + t_first) * a.H * a.D;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                rows[u] = row + u * rows_per_iter;
-                const int in_row = HND ? (h * a.ps + t) : rows[u];
-                if (rows[u] < n_rows) {
-                    codes[u] = *(const uint2 *)(src + (int64_t)in_row * (a.D >> 1) + c * 8);
-                    sbyte[u] = sfs[(int64_t)in_row * nb + c];
-                }
-                h += h_step;
-                t += t_step;
-                if (h >= a.H) {
-                    h -= a.H;
-                    t += 1;
-                }
-            }
+        for (int kv = 0; kv < 2; ++kv) {
+            const uint8_t *src = a.data[kv] + page * a.stride[kv];
+            const uint8_t *sfs = a.sf[kv] + page * a.sf_stride[kv];
+            uint4 *dst = (uint4 *)(a.out[kv] + out_off);
+            const float gk = g[kv];
+            int row = tid / cpr, cc = tid - (tid / cpr) * cpr;
+            int t = row / a.H, h = row - (row / a.H) * a.H;
+            for (int base = 0; base < n_chunks; base += kBatch * kThreads) {
+                uint32_t code[kBatch], sbyte[kBatch];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                if (rows[u] < n_rows) {
-                    const float dec = e4m3_to_f32(sbyte[u]) * g;
-                    uint32_t o[8];
-                    decode_block<BF16>(codes[u].x, codes[u].y, dec, o);
-                    uint4 *p = (uint4 *)(dst + (int64_t)rows[u] * a.D + c * 16);
-                    p[0] = make_uint4(o[0], o[1], o[2], o[3]);
-                    p[1] = make_uint4(o[4], o[5], o[6], o[7]);
+                for (int u = 0; u < kBatch; ++u) {
+                    const int ci = base + u * kThreads + tid;
+                    if (ci < n_chunks) {
+                        const int in_row = HND ? (h * a.ps + t) : row;
+                        code[u] = *(const uint32_t *)(src + (int64_t)in_row * (a.D >> 1) + cc * 4);
+                        sbyte[u] = sfs[(int64_t)in_row * nb + (cc >> 1)];
+                    }
+                    // advance (row, cc, t, h) by kThreads chunks
+                    cc += c_step;
+                    int carry = cc >= cpr;
+                    cc -= carry ? cpr : 0;
+                    row += r_step + carry;
+                    h += rh_step + carry;
+                    t += rt_step;
+                    if (h >= a.H) {
+                        h -= a.H;
+                        t += 1;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int ci = base + u * kThreads + tid;
+                    if (ci < n_chunks) {
+                        const float dec = e4m3_byte_to_f32(sbyte[u]) * gk;
+                        dst[ci] = decode_chunk<BF16>(code[u], dec);
+                    }
                 }
             }
         }
@@ -163,10 +175,13 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
     a.D = c.head_dim;
     a.T = max_seq_len;
     a.pages_per_req = (max_seq_len + c.page_size - 1) / c.page_size;
-    a.num_tiles = (int64_t)batch * a.pages_per_req * 2;
-    if (a.num_tiles == 0)
+    const int64_t pairs = (int64_t)batch * a.pages_per_req;
+    if (pairs == 0)
         return hipSuccess;
-    const int grid = (int)(a.num_tiles < (int64_t)kPersistentWorkgroups ? a.num_tiles : kPersistentWorkgroups);
+    if (pairs > INT32_MAX)
+        return hipErrorInvalidValue;
+    a.num_pairs = (int32_t)pairs;
+    const int grid = (int)(pairs < kMaxGrid ? pairs : kMaxGrid);
     const bool hnd = c.layout == KVFP4_HND;
     if (hnd)
         return out_bf16 ? launch3<true, true>(bt64, a, grid, st) : launch3<true, false>(bt64, a, grid, st);

@@ -13,10 +13,15 @@
 // once, saturating at 448); a block then needs one 8-byte LDS read and a few
 // v_perm byte selects per 8 elements. The sign is code sign XOR scale sign.
 //
-// Work list: the B x max_pages_per_seq (request, page) pairs, walked by a
-// persistent grid; pairs past a request's ceil(seq_len / ps) pages are
-// skipped, so no page beyond kv_page_indptr[B] is touched. Workgroup 0 also
-// zeroes output page 0.
+// Work list: the output pages 1 .. kv_page_indptr[B] the requests reserve,
+// walked by a persistent grid (the table above is built once per workgroup).
+// Output page p + 1 belongs to the request b with indptr[b] <= p <
+// indptr[b + 1] (a binary search over the indptr, in scalar registers) and is
+// its page j = p - indptr[b]; it is written only when j < ceil(seq_len / ps),
+// so reserved-but-unused pages and everything past kv_page_indptr[B] stay
+// untouched. Walking reserved pages rather than the B x max_pages_per_seq
+// table keeps the work per workgroup even when lengths differ widely.
+// Workgroup 0 also zeroes output page 0.
 #include "kvfp4_internal.h"
 #include "nvfp4_device.h"
 
@@ -38,7 +43,7 @@ struct MatArgs {
     int32_t *table;
     int32_t ps, H, D;
     int32_t maxp;          // max_pages_per_seq: columns of the FP8 block table
-    int64_t num_pairs;     // B * maxp
+    int32_t batch;
 };
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
@@ -77,8 +82,7 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a)
     __syncthreads();
 
     const int nb = a.D >> 4;
-    const int blocks_per_head = a.ps * nb;
-    const int blocks_per_half = a.H * blocks_per_head;
+    const int blocks_per_half = a.H * a.ps * nb;
     const int64_t half_bytes = (int64_t)a.H * a.ps * a.D;
 
     if (blockIdx.x == 0) {
@@ -87,17 +91,29 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a)
             z[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 
-    // per-thread (h, t, c) of block q = tid + k * kThreads, advanced incrementally
-    const int q_step_h = kThreads / blocks_per_head;
-    const int q_step_r = kThreads - q_step_h * blocks_per_head;
+    // block q = tid + k * kThreads of a half page is (h, t, c) with
+    // q = (h * ps + t) * nb + c; the thread advances it by kThreads blocks
+    const int c_step = kThreads % nb;
+    const int t_all = kThreads / nb;
+    const int t_step = t_all % a.ps, h_step = t_all / a.ps;
+    const int c0 = tid % nb, t0 = (tid / nb) % a.ps, h0 = tid / (nb * a.ps);
 
-    for (int64_t pair = blockIdx.x; pair < a.num_pairs; pair += gridDim.x) {
-        const int b = (int)(pair / a.maxp);
-        const int j = (int)(pair - (int64_t)b * a.maxp);
+    const int n_work = a.batch > 0 ? a.indptr[a.batch] : 0;
+    for (int p = blockIdx.x; p < n_work; p += gridDim.x) {
+        int lo = 0, hi = a.batch;              // indptr[lo] <= p < indptr[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.indptr[mid] <= p)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        const int b = lo;
+        const int j = p - a.indptr[b];
         const int n_pages = (a.seq_lens[b] + a.ps - 1) / a.ps;
-        if (j >= n_pages)
+        if (j < 0 || j >= n_pages || j >= a.maxp)
             continue;
-        const int64_t dst = (int64_t)a.indptr[b] + j + 1;
+        const int64_t dst = (int64_t)p + 1;
         const int32_t *row = a.bt + b * a.bt_row_stride;
         const int64_t pk = row[j];
         const int64_t pv = SHARED ? pk : row[a.bt_kv_stride + j];
@@ -108,27 +124,25 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a)
             const int64_t page = kv ? pv : pk;
             const uint8_t *src = a.data[kv] + page * a.stride[kv];
             const uint8_t *sfs = a.sf[kv] + page * a.sf_stride[kv];
-            uint8_t *o = a.out + (dst * 2 + kv) * half_bytes;
-            int hh = tid / blocks_per_head;
-            int rem = tid - hh * blocks_per_head;
+            uint4 *o = (uint4 *)(a.out + (dst * 2 + kv) * half_bytes);
+            int c = c0, t = t0, h = h0;
             for (int q = tid; q < blocks_per_half; q += kThreads) {
                 const uint2 codes = *(const uint2 *)(src + (int64_t)q * 8);
-                uint32_t sidx = (uint32_t)q;
-                if (INTERLEAVED && kv == 1) {
-                    const int t = rem / nb, c = rem - (rem / nb) * nb;
-                    sidx = (uint32_t)(hh * blocks_per_head + ((t >> 2) * nb + c) * 4 + (t & 3));
-                }
-                const uint32_t s = sfs[sidx];
-                const uint2 l = lut[s];
-                const uint32_t smask = (s & 0x80u) ? 0x80808080u : 0u;
+                const int sidx = (INTERLEAVED && kv == 1) ? (h * a.ps + (t & ~3)) * nb + c * 4 + (t & 3) : q;
+                const uint32_t sb = sfs[sidx];
+                const uint2 l = lut[sb];
+                const uint32_t smask = (sb & 0x80u) ? 0x80808080u : 0u;
                 const uint2 lo = convert8(codes.x, l, smask);
                 const uint2 hi = convert8(codes.y, l, smask);
-                *(uint4 *)(o + (int64_t)q * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                hh += q_step_h;
-                rem += q_step_r;
-                if (rem >= blocks_per_head) {
-                    rem -= blocks_per_head;
-                    hh += 1;
+                o[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                c += c_step;
+                int carry = c >= nb;
+                c -= carry ? nb : 0;
+                t += t_step + carry;
+                h += h_step;
+                if (t >= a.ps) {
+                    t -= a.ps;
+                    h += 1;
                 }
             }
         }
@@ -162,9 +176,11 @@ hipError_t launch_materialize_fp8(const kvfp4_paged_cache_t &c, bool v_interleav
     a.H = c.num_kv_heads;
     a.D = c.head_dim;
     a.maxp = maxp;
-    a.num_pairs = (int64_t)batch * maxp;
-    // at least one workgroup, which zeroes page 0 even for an empty batch
-    const int64_t want = a.num_pairs > 0 ? a.num_pairs : 1;
+    a.batch = batch;
+    // the number of reserved pages lives on the device: a fixed persistent
+    // grid (at least one workgroup, which zeroes page 0 for an empty batch)
+    const int64_t pairs = (int64_t)batch * maxp;
+    const int64_t want = pairs > 0 ? pairs : 1;
     const int grid = (int)(want < kPersistentWorkgroups ? want : kPersistentWorkgroups);
     if (v_interleaved) {
         if (shared)

@@ -79,6 +79,42 @@ __device__ __forceinline__ float e2m1_code_to_mag(uint32_t k)
     return __uint_as_float(bits);
 }
 
+// ------------------------------------------------ gfx950 conversions ----
+// These conversion instructions are used only in the forms that reproduce
+// the definitions above bit for bit (checked exhaustively per input class on
+// the device): the FP4 and FP8 decodes are exact; the FP4 encode with a unit
+// scale rounds to nearest-even onto the E2M1 grid, saturates at +-6 and keeps
+// the sign of zero; the FP8 encode rounds to nearest-even for |x| <= 448 (it
+// is only given clamped values). Their scale operand applies only its
+// exponent, so it is always 1.0 here.
+
+// byte SEL of `packed` (two E2M1 codes, low nibble first) -> two fp32 values
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4x2_to_f32x2(uint32_t packed)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
+}
+
+// two fp32 -> two E2M1 codes written into byte SEL of `old`, `lo` in the low
+// nibble; the other bytes of `old` are kept
+template <int SEL>
+__device__ __forceinline__ uint32_t f32x2_to_fp4x2(uint32_t old, float lo, float hi)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, 1.0f, SEL);
+}
+
+// E4M3 byte (low 8 bits) -> fp32, exact
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t b)
+{
+    return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+}
+
+// x in [0, 448] -> nearest E4M3 byte, ties to even
+__device__ __forceinline__ uint32_t f32_to_e4m3_hw(float x)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xFFu;
+}
+
 // ------------------------------------------------------- 16-bit floats ----
 // RNE fp32 -> bf16 / fp16 bit patterns, two at a time (gfx950 converts with
 // round-to-nearest-even; fp16 keeps subnormals).

@@ -332,3 +332,42 @@ def test_global_scale_parity(K, orc, n, is_bf16, emax):
                                                                     torch.float16, device="cuda"), emax, g)
     torch.cuda.synchronize()
     assert g.item() == want
+
+
+@pytest.mark.parametrize("in_bf16", [True, False])
+@pytest.mark.parametrize("recipe", ["standard", "mse", "mae"])
+def test_append_encoder_sweeps_every_16bit_value(K, orc, in_bf16, recipe):
+    """Every bf16 / fp16 value in [-6, 6] passes through the E2M1 encoder
+    with a unit decode factor (g = 1 and a block amax of 6 give s = 1.0), so
+    the device encoder meets every tie and every subnormal input; the 4over6
+    recipes also run the amax/4 candidate (decode factor 1.5) on them."""
+    ro, rk = recipes(K, orc, recipe)
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = W.bits_to_f32(bits, in_bf16)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 6.0)
+    sweep = bits[keep]
+    n_rows = (sweep.size + 14) // 15
+    pad = np.zeros(n_rows * 15, np.uint16)
+    pad[:sweep.size] = sweep
+    six = W.f32_to_bits(np.array([6.0], np.float32), in_bf16)[0]
+    rows = np.concatenate([np.full((n_rows, 1), six, np.uint16), pad.reshape(n_rows, 15)], axis=1)
+    key = rows.reshape(n_rows, 1, 16)
+    val = key[::-1].copy()
+    ps = 16
+    lens = np.array([n_rows])
+    pool = (n_rows + ps - 1) // ps + 2
+    rng = np.random.default_rng(77)
+    indices, indptr, last = W.csr_for_lengths(lens, ps, rng.permutation(pool))
+    cache = W.make_cache(rng, pool, ps, 1, 16, W.NHD)
+    bi, pos = W.rows_for_positions(np.zeros(1, np.int64), lens)
+    host = cache.copy()
+    dev = DeviceCache(cache)
+    say(f"encoder sweep bf16={in_bf16} recipe={recipe} rows={n_rows}")
+    K.kv_quantize_append(dev.cache, bits_tensor(key, in_bf16), bits_tensor(val, in_bf16), i32(bi), i32(pos),
+                         i32(indices), i32(indptr), i32(last), 1.0, 1.0, rk)
+    torch.cuda.synchronize()
+    orc.quantize_append(host, key, val, in_bf16, bi, pos, indices, indptr, last, 1.0, 1.0, ro,
+                        threads=oracle_threads())
+    got = dev.to_host()
+    for a, b in zip((got.k_data, got.v_data, got.k_sf, got.v_sf), (host.k_data, host.v_data, host.k_sf, host.v_sf)):
+        assert np.array_equal(a, b), first_mismatch(a, b)
