@@ -5,12 +5,12 @@ of 64 requests (bf16 K/V, 8 KV heads, head_dim 128, page_size 16, NHD pages
 shuffled across a 20,000-page pool), then gather-dequantize every request's
 full context (lengths U{1..4096} + 1) into bf16 [64, max_len, 8, 128].
 value = algorithmic bytes of the step / wall time of the step, with all
-inputs resident in HBM; two replicas of the workload alternate so that
-consecutive steps touch disjoint memory.
+inputs resident in HBM; replicas of the workload in disjoint memory rotate so
+that no step finds its inputs in the 256 MB Infinity Cache.
 
-Legs (same JSON line; each kernel launched back to back on two replicas of
-its workload in disjoint memory, mean of the per-launch HIP-event times, the
-same steady state as the headline step): prefill dequantize (16 x 8192 tokens, HND, int64 table, fp16
+Legs (same JSON line; each kernel launched back to back over rotating
+replicas of its workload in disjoint memory, mean of the per-launch HIP-event
+times, the same steady state as the headline step): prefill dequantize (16 x 8192 tokens, HND, int64 table, fp16
 out), materialize-FP8 (32 requests, log-uniform lengths, padded pages,
 separate K/V tables), 4over6 quantize-append (65,536 rows, Student-t(3) with
 0.1% outliers x20, MSE and MAE) and its dequantize, and a plain
@@ -217,7 +217,7 @@ def prefill_replica(env, seed=1003):
 
 def leg_prefill_dequant(env, iters, warmup):
     fns, keep = [], []
-    for _ in range(2):
+    for _ in range(replicas_for(151_000_000)):
         fn, nbytes, k = prefill_replica(env)
         fns.append(fn)
         keep.append(k)
@@ -244,7 +244,7 @@ def materialize_replica(env, seed=1004):
 
 def leg_materialize(env, iters, warmup):
     fns, keep = [], []
-    for _ in range(2):
+    for _ in range(replicas_for(222_000_000)):
         fn, nbytes, k = materialize_replica(env)
         fns.append(fn)
         keep.append(k)
@@ -289,7 +289,8 @@ def four_over_six_replica(env, seed=1005):
 
 def leg_four_over_six(env, iters, warmup):
     torch = env.torch
-    reps = [four_over_six_replica(env) for _ in range(2)]
+    # the append reads 268 MB of rows, the dequant 75 MB of cache per replica
+    reps = [four_over_six_replica(env) for _ in range(replicas_for(75_000_000))]
     B, T, H, D, ps = 16, 4096, 8, 128, 64
     res = {}
     ab = append_bytes(B * T, H, D)
@@ -310,11 +311,53 @@ def leg_four_over_six(env, iters, warmup):
 def leg_copy(env, nbytes, iters, warmup):
     torch = env.torch
     pairs = []
-    for _ in range(2):
+    for _ in range(replicas_for(nbytes // 2)):
         src = torch.ones(nbytes // 2, dtype=torch.uint8, device=env.dev)
         pairs.append((src, torch.empty_like(src)))
     r = env.steady([(lambda s=s, d=d: d.copy_(s)) for s, d in pairs], iters, warmup)
     return dict(kernel="torch copy_ (device to device)", bytes=nbytes, **rates(nbytes, r))
+
+
+DEQUANT_SOURCES = ("kv_cache_quantization_paged_amd/csrc/dequant.hip",
+                   "kv_cache_quantization_paged_amd/csrc/nvfp4_device.h",
+                   "kv_cache_quantization_paged_amd/csrc/kvfp4_internal.h")
+TRAFFIC_SUMMARY = "profiles/kv_dequantize_paged_decode_counters.md"
+
+
+def dequant_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DEQUANT_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the decode dequant from the committed
+    rocprofv3 counter summary, or None when the kernel's sources have
+    changed since those counters were taken."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if "=" in line and line.strip().startswith(("traffic_bytes_per_launch", "source_sha256")):
+            k, v = line.strip().strip("`").split("=", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != dequant_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def replicas_for(read_bytes: int) -> int:
+    """Replicas whose inputs together exceed ~2.5x the 256 MB Infinity Cache,
+    so every launch reads its inputs from HBM, as a serving step does (a
+    layer's cache is read again only after every other layer has run)."""
+    return max(2, -(-640_000_000 // max(1, read_bytes)))
 
 
 def rates(nbytes, r):
@@ -370,6 +413,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--leg-iters", type=int, default=50)
+    ap.add_argument("--legs", default="prefill,materialize,four_over_six,copy",
+                    help="comma list of legs to run after the headline step (empty: none)")
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=16)
@@ -381,12 +426,13 @@ def main():
 
     import torch
     env = Env()
-    log("bench: building the decode workload (2 replicas)")
-    reps = [Decode(env), Decode(env)]
+    n_rep = replicas_for(144_000_000)
+    log(f"bench: building the decode workload ({n_rep} replicas)")
+    reps = [Decode(env) for _ in range(n_rep)]
     torch.cuda.synchronize()
 
     def step(i):
-        r = reps[i % 2]
+        r = reps[i % n_rep]
         r.append()
         r.dequant()
 
@@ -398,7 +444,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        r = reps[i % 2]
+        r = reps[i % n_rep]
         r.append()
         evs[i][0].record()
         r.dequant()
@@ -420,14 +466,20 @@ def main():
                                "GBps": achieved, "frac": achieved / PEAK_GBS}}
     del reps
     torch.cuda.empty_cache()
-    if not args.no_legs:
-        log("bench: legs")
+    chosen = set() if args.no_legs else {x for x in args.legs.split(",") if x}
+    if chosen:
+        log(f"bench: legs {sorted(chosen)}")
+    if "prefill" in chosen:
         legs["prefill_dequantize"] = leg_prefill_dequant(env, args.leg_iters, 5)
         torch.cuda.empty_cache()
+    if "materialize" in chosen:
         legs["materialize_fp8"] = leg_materialize(env, args.leg_iters, 5)
         torch.cuda.empty_cache()
+    if "four_over_six" in chosen:
         legs["four_over_six_quantize"] = leg_four_over_six(env, args.leg_iters, 5)
         torch.cuda.empty_cache()
+    if "copy" in chosen:
+        # also the known-size copy that calibrates the byte counters
         legs["copy_context"] = leg_copy(env, 1 << 29, args.leg_iters, 5)
 
     cpu = None
@@ -445,7 +497,7 @@ def main():
                    "batch": 64, "page_size": 16, "num_kv_heads": 8, "head_dim": 128, "layout": "NHD",
                    "step_bytes": step_bytes, "peak_GBps": PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBS, "traffic": None,
+                     "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(),
                      "kernel": "kv_dequantize_paged (dequant_kernel<NHD, bf16, int32 table>)"},
         "cpu_baseline": cpu,
         "legs": legs,

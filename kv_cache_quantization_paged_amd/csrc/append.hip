@@ -135,7 +135,8 @@ __device__ __forceinline__ void quantize_one(const AppendArgs &a, const ScaleTab
         }
     }
     const int64_t row = hnd ? ((int64_t)h * a.ps + slot) : ((int64_t)slot * a.H + h);
-    *(uint2 *)(a.data[kv] + page * a.stride[kv] + row * (a.D >> 1) + c * 8) = codes;
+    const u32x2 cv = {codes.x, codes.y};
+    __builtin_nontemporal_store(cv, (u32x2 *)(a.data[kv] + page * a.stride[kv] + row * (a.D >> 1) + c * 8));
     a.sf[kv][page * a.sf_stride[kv] + row * nb + c] = (uint8_t)s;
 }
 
@@ -245,7 +246,12 @@ hipError_t launch_quantize_append(const kvfp4_paged_cache_t &c, const void *key,
     const int bpr = a.H * (a.D >> 4);
     const int64_t rows_per_wg = bpr <= kThreads ? kThreads / bpr : 1;
     const int64_t wgs = (nnz + rows_per_wg - 1) / rows_per_wg;
-    const int grid = (int)(wgs < kPersistentWorkgroups ? wgs : kPersistentWorkgroups);
+    // The standard recipe is memory-bound: one workgroup per group of rows
+    // balances best. The 4over6 recipes are VALU-bound: a persistent grid
+    // builds the LDS tables once per workgroup and overlaps a row's loads
+    // with the previous row's arithmetic.
+    const int64_t cap = recipe == nullptr ? ((int64_t)1 << 24) : kPersistentWorkgroups;
+    const int grid = (int)(wgs < cap ? wgs : cap);
     const bool hnd = c.layout == KVFP4_HND;
     const int rk = recipe == nullptr ? 0 : (recipe->err_mode == KVFP4_ERR_MSE ? 1 : 2);
     return in_bf16 ? launch1<true>(rk, hnd, a, grid, st) : launch1<false>(rk, hnd, a, grid, st);

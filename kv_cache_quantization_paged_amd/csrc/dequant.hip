@@ -27,7 +27,7 @@ namespace kvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 8;            // chunks in flight per lane
+constexpr int kBatch = 16;           // chunks in flight per lane and tensor
 constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid size in work-items stays below 2^32)
 
 struct DequantArgs {
@@ -47,13 +47,13 @@ struct DequantArgs {
 
 // 4 code bytes (8 values) -> 4 packed 16-bit pairs
 template <bool BF16>
-__device__ __forceinline__ uint4 decode_chunk(uint32_t codes, float dec)
+__device__ __forceinline__ u32x4 decode_chunk(uint32_t codes, float dec)
 {
     const f32x2 v0 = fp4x2_to_f32x2<0>(codes);
     const f32x2 v1 = fp4x2_to_f32x2<1>(codes);
     const f32x2 v2 = fp4x2_to_f32x2<2>(codes);
     const f32x2 v3 = fp4x2_to_f32x2<3>(codes);
-    uint4 r;
+    u32x4 r;
     if (BF16) {
         r.x = pack_bf16x2(dec * v0.x, dec * v0.y);
         r.y = pack_bf16x2(dec * v1.x, dec * v1.y);
@@ -74,63 +74,94 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a)
     const int cpr = a.D >> 3;                  // chunks per (token, head) row
     const int nb = a.D >> 4;
     const int tid = threadIdx.x;
-    // mixed-radix position of chunk (tid + 256 k): row advances by r_step (+1
-    // on a carry from cc), and the row's (t, h) follow
+    // mixed-radix position of chunk (tid + 256 k): the row advances by r_step
+    // (+1 on a carry from cc), and the row's (t, h) follow
     const int r_step = kThreads / cpr, c_step = kThreads - r_step * cpr;
     const int rt_step = r_step / a.H, rh_step = r_step - rt_step * a.H;
     const float g[2] = {*a.scale[0], *a.scale[1]};
+    // HND offset steps for kThreads chunks: base step, extra on a chunk-column
+    // carry (next head row of the same token), extra on a head wrap (head 0 of
+    // the next token)
+    const int hb = a.ps * (a.D >> 1), hbs = a.ps * nb;
+    const int k0_c = (rh_step * a.ps + rt_step) * (a.D >> 1) + c_step * 4;
+    const int kc_c = hb - cpr * 4;
+    const int kw_c = -(a.H * a.ps - 1) * (a.D >> 1);
+    const int k0_s = (rh_step * a.ps + rt_step) * nb + c_step / 2;
+    const int kc_s = hbs - nb;
+    const int kw_s = -(a.H * a.ps - 1) * nb;
+    const uint32_t page_bytes = (uint32_t)(a.ps * a.H * (a.D >> 1));
+    const uint32_t page_sf_bytes = (uint32_t)(a.ps * a.H * nb);
 
     // one pair per workgroup (the loop only repeats for tables of more than
     // kMaxGrid pairs)
     for (int pair = blockIdx.x; pair < a.num_pairs; pair += gridDim.x) {
         const int b = pair / a.pages_per_req;
         const int j = pair - b * a.pages_per_req;
-        const int len = min(a.seq_lens[b], a.T);
+        const int len = uniform(min(a.seq_lens[b], a.T));
         const int t_first = j * a.ps;
         if (t_first >= len)
             continue;
         const int n_tok = min(a.ps, len - t_first);
-        const int64_t page = BT64 ? ((const int64_t *)a.block_tables)[b * a.bt_row_stride + j]
-                                  : (int64_t)((const int32_t *)a.block_tables)[b * a.bt_row_stride + j];
+        const int64_t page = uniform64(BT64 ? ((const int64_t *)a.block_tables)[b * a.bt_row_stride + j]
+                                            : (int64_t)((const int32_t *)a.block_tables)[b * a.bt_row_stride + j]);
         const int n_chunks = n_tok * a.H * cpr;
         const int64_t out_off = ((int64_t)b * a.T + t_first) * a.H * a.D;
+        // chunks past the page's valid tokens read zeros or in-page bytes and
+        // their stores fall outside the outputs' ranges: no per-chunk branch
+        const rsrc_t src[2] = {make_rsrc(a.data[0] + page * a.stride[0], page_bytes),
+                               make_rsrc(a.data[1] + page * a.stride[1], page_bytes)};
+        const rsrc_t sfs[2] = {make_rsrc(a.sf[0] + page * a.sf_stride[0], page_sf_bytes),
+                               make_rsrc(a.sf[1] + page * a.sf_stride[1], page_sf_bytes)};
+        const rsrc_t dst[2] = {make_rsrc(a.out[0] + out_off, (uint32_t)n_chunks * 16u),
+                               make_rsrc(a.out[1] + out_off, (uint32_t)n_chunks * 16u)};
+        // byte offsets of this lane's chunk in a code / scale page (K and V
+        // pages share the geometry). NHD pages hold rows in output order, so
+        // chunk ci sits at 4 ci / ci / 2. HND rows are (h, t): the offsets
+        // follow the chunk's (h, cc) counters by additions only.
+        const int row0 = tid / cpr;
+        int cc = tid - row0 * cpr, h = row0 - (row0 / a.H) * a.H;
+        const int t0 = row0 / a.H;
+        uint32_t off_c = (uint32_t)((h * a.ps + t0) * (a.D >> 1) + cc * 4);
+        uint32_t off_s = (uint32_t)((h * a.ps + t0) * nb + (cc >> 1));
+        for (int base = 0; base < n_chunks; base += kBatch * kThreads) {
+            // every load of the round is issued before its first store: a wait
+            // for a load also waits for all earlier stores
+            uint32_t code[2][kBatch], sbyte[2][kBatch];
 #pragma unroll
-        for (int kv = 0; kv < 2; ++kv) {
-            const uint8_t *src = a.data[kv] + page * a.stride[kv];
-            const uint8_t *sfs = a.sf[kv] + page * a.sf_stride[kv];
-            uint4 *dst = (uint4 *)(a.out[kv] + out_off);
-            const float gk = g[kv];
-            int row = tid / cpr, cc = tid - (tid / cpr) * cpr;
-            int t = row / a.H, h = row - (row / a.H) * a.H;
-            for (int base = 0; base < n_chunks; base += kBatch * kThreads) {
-                uint32_t code[kBatch], sbyte[kBatch];
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int ci = base + u * kThreads + tid;
-                    if (ci < n_chunks) {
-                        const int in_row = HND ? (h * a.ps + t) : row;
-                        code[u] = *(const uint32_t *)(src + (int64_t)in_row * (a.D >> 1) + cc * 4);
-                        sbyte[u] = sfs[(int64_t)in_row * nb + (cc >> 1)];
-                    }
-                    // advance (row, cc, t, h) by kThreads chunks
+            for (int u = 0; u < kBatch; ++u) {
+                uint32_t oc, os;
+                if (!HND) {
+                    const uint32_t ci = (uint32_t)(base + u * kThreads + tid);
+                    oc = ci * 4u;
+                    os = ci >> 1;
+                } else {
+                    oc = off_c;
+                    os = off_s;
+                    // advance (h, cc) by kThreads chunks; cc keeps its parity
+                    // (cpr and c_step are even), so the scale offset moves by
+                    // exactly half the chunk-column step
                     cc += c_step;
-                    int carry = cc >= cpr;
+                    const int carry = cc >= cpr;
                     cc -= carry ? cpr : 0;
-                    row += r_step + carry;
                     h += rh_step + carry;
-                    t += rt_step;
-                    if (h >= a.H) {
-                        h -= a.H;
-                        t += 1;
-                    }
+                    const int wrap = h >= a.H;
+                    h -= wrap ? a.H : 0;
+                    off_c += (uint32_t)(k0_c + (carry ? kc_c : 0) + (wrap ? kw_c : 0));
+                    off_s += (uint32_t)(k0_s + (carry ? kc_s : 0) + (wrap ? kw_s : 0));
                 }
 #pragma unroll
+                for (int kv = 0; kv < 2; ++kv) {
+                    code[kv][u] = buf_load_u32(src[kv], oc);
+                    sbyte[kv][u] = buf_load_u8(sfs[kv], os);
+                }
+            }
+#pragma unroll
+            for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
                 for (int u = 0; u < kBatch; ++u) {
-                    const int ci = base + u * kThreads + tid;
-                    if (ci < n_chunks) {
-                        const float dec = e4m3_byte_to_f32(sbyte[u]) * gk;
-                        dst[ci] = decode_chunk<BF16>(code[u], dec);
-                    }
+                    const uint32_t ci = (uint32_t)(base + u * kThreads + tid);
+                    const float dec = e4m3_byte_to_f32(sbyte[kv][u]) * g[kv];
+                    buf_store_u32x4_nt(decode_chunk<BF16>(code[kv][u], dec), dst[kv], ci * 16u);
                 }
             }
         }

@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a)
                 const uint32_t smask = (sb & 0x80u) ? 0x80808080u : 0u;
                 const uint2 lo = convert8(codes.x, l, smask);
                 const uint2 hi = convert8(codes.y, l, smask);
-                o[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
+                __builtin_nontemporal_store(v, (u32x4 *)&o[q]);   // the FP8 copy is read by a later kernel only
                 c += c_step;
                 int carry = c >= nb;
                 c -= carry ? nb : 0;

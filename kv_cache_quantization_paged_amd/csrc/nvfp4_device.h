@@ -115,6 +115,73 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_hw(float x)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xFFu;
 }
 
+// ------------------------------------------------------ buffer access ----
+// Raw buffer loads/stores: a wave-uniform base in scalar registers plus a
+// 32-bit per-lane byte offset (no 64-bit address arithmetic per lane). An
+// access whose offset lies at or beyond `bytes` reads zero and a store there
+// is dropped by the hardware range check; the kernels only rely on that for
+// whole 4- or 16-byte accesses at aligned offsets, never for partial ones.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufferFlags = 0x00020000;   // gfx9 raw-buffer dword 3 (32-bit data format)
+
+// `base` and `bytes` must be the same in every lane of the wavefront; they are
+// moved to scalar registers here so that no per-lane descriptor is ever built
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    void *p = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
+// a value known to be equal in every lane of the wavefront, in a scalar register
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t buf_load_u8(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_u32(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load_u32x2(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x4 buf_load_u32x4(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u8(uint32_t v, rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u32x2(u32x2 v, rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u32x4(u32x4 v, rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+// non-temporal ("nt") store: for outputs no later kernel in the same pass
+// reads back, so they stream to HBM instead of sitting dirty in the caches
+// (and being written back inside whatever runs next)
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ void buf_store_u32x4_nt(u32x4 v, rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNonTemporal);
+}
+
 // ------------------------------------------------------- 16-bit floats ----
 // RNE fp32 -> bf16 / fp16 bit patterns, two at a time (gfx950 converts with
 // round-to-nearest-even; fp16 keeps subnormals).
