@@ -97,7 +97,7 @@ def make_cache(rng: np.random.Generator, num_pages: int, page_size: int, num_hea
 
     def alloc(n):
         if fill == "random":
-            return rng.integers(0, 256, size=n, dtype=np.uint8)
+            return np.frombuffer(bytearray(rng.bytes(n)), dtype=np.uint8)
         return np.zeros(n, np.uint8)
 
     def view(base, off, stride, nb):
@@ -151,8 +151,16 @@ def rows_for_positions(starts: np.ndarray, ends: np.ndarray):
 # ---------------------------------------------------------------------------
 # value distributions
 # ---------------------------------------------------------------------------
+def _bulk_normal(rng, shape) -> np.ndarray:
+    """Standard normal fp32 draws in bulk: torch's (multithreaded) CPU
+    generator, seeded by the next draw of ``rng``."""
+    import torch
+    g = torch.Generator().manual_seed(int(rng.integers(0, 2**62)))
+    return torch.randn(tuple(shape), generator=g, dtype=torch.float32).numpy()
+
+
 def normal_rows(rng, shape) -> np.ndarray:
-    return rng.standard_normal(size=shape, dtype=np.float32)
+    return _bulk_normal(rng, shape)
 
 
 def head_scales(rng, H: int, lo=0.1, hi=10.0) -> np.ndarray:
@@ -162,14 +170,34 @@ def head_scales(rng, H: int, lo=0.1, hi=10.0) -> np.ndarray:
 
 def head_scaled_normal(rng, nnz: int, a: np.ndarray, D: int) -> np.ndarray:
     """N(0,1) rows [nnz, H, D] times the per-head scales ``a``."""
-    return rng.standard_normal(size=(nnz, len(a), D), dtype=np.float32) * a[None, :, None]
+    return _bulk_normal(rng, (nnz, len(a), D)) * a[None, :, None]
 
 
-def student_t_with_outliers(rng, shape, nu=3.0, frac=0.001, factor=20.0) -> np.ndarray:
-    x = rng.standard_t(nu, size=shape).astype(np.float32)
+def sample_without_replacement(rng, n: int, k: int) -> np.ndarray:
+    """k distinct indices in [0, n), uniformly (draw with replacement, keep
+    the first occurrence of each value in draw order, top up until k)."""
+    out = np.empty(0, np.int64)
+    while out.size < k:
+        draw = rng.integers(0, n, size=int((k - out.size) * 1.05) + 16)
+        cat = np.concatenate([out, draw])
+        _, first = np.unique(cat, return_index=True)
+        out = cat[np.sort(first)]
+    return out[:k]
+
+
+def student_t_with_outliers(rng, shape, nu=3, frac=0.001, factor=20.0) -> np.ndarray:
+    """Student-t with ``nu`` (integer) degrees of freedom, z / sqrt(chi2/nu)
+    with chi2 a sum of nu squared normals; then exactly round(frac * n)
+    entries, chosen without replacement, multiplied by ``factor``."""
+    z = _bulk_normal(rng, shape)
+    chi2 = np.zeros(shape, np.float32)
+    for _ in range(int(nu)):
+        w = _bulk_normal(rng, shape)
+        chi2 += w * w
+    x = (z / np.sqrt(chi2 / np.float32(nu))).astype(np.float32)
     n = x.size
     k = int(round(frac * n))
-    idx = rng.choice(n, size=k, replace=False)
+    idx = sample_without_replacement(rng, n, k)
     flat = x.reshape(-1)
     flat[idx] *= np.float32(factor)
     return x
@@ -371,7 +399,7 @@ def materialize_fp8(seed: int = 1004, B: int = 32, lo: int = 128, hi: int = 3276
     lens, P, maxp, bt, indptr = materialize_tables(rng, B, lo, hi, ps, shared, compact)
     cache = make_cache(rng, P, ps, H, D, HND, data_pad=data_pad, fill="zero")
     for a in (cache.k_data, cache.v_data):
-        a[...] = rng.integers(0, 256, size=a.shape, dtype=np.uint8)
+        a[...] = np.frombuffer(rng.bytes(a.size), dtype=np.uint8).reshape(a.shape)
     for a in (cache.k_sf, cache.v_sf):
         a[...] = scale_bytes(rng, a.shape)
     return Materialize(cache, bt, shared, lens.astype(np.int32), indptr, int(indptr[-1]), maxp,
