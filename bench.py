@@ -308,6 +308,45 @@ def leg_four_over_six(env, iters, warmup):
     return res
 
 
+def page_order_replica(env, order, seed):
+    """64 full 4096-token requests in decode geometry (page_size 16, 8 heads,
+    head_dim 128, NHD, bf16 out); `order` "random" shuffles the 16,384 pages
+    over the requests, "sequential" gives request b pages 256 b .. 256 b + 255."""
+    torch, K = env.torch, env.K
+    B, T, ps, H, D = 64, 4096, 16, 8, 128
+    P = B * T // ps
+    cache, keep = env.cache(P, ps, H, D, K.KVFP4_NHD, seed)
+    if order == "random":
+        bt = torch.randperm(P, generator=env.gen(seed + 1), device=env.dev).to(torch.int32).view(B, T // ps)
+    else:
+        bt = torch.arange(P, dtype=torch.int32, device=env.dev).view(B, T // ps)
+    sl = env.i32(np.full(B, T))
+    ok = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=env.dev)
+    ov = torch.empty_like(ok)
+    g = torch.ones(1, dtype=torch.float32, device=env.dev)
+    nbytes = dequant_bytes(np.full(B, T), ps, H, D, 4)
+    return (lambda: K.kv_dequantize_paged(cache, bt, sl, g, g, ok, ov)), nbytes, (cache, keep, bt, sl, ok, ov, g)
+
+
+def leg_page_order(env, iters, warmup):
+    """Context, not a workload of the method: the same dequant over the same
+    bytes, with the physical pages in request order or shuffled. The gap is
+    what scattered page placement costs at the DRAM level."""
+    torch = env.torch
+    res = {"workload": "64 x 4096 tokens, page_size 16, 8 heads, head_dim 128, NHD, bf16 out; 16,384 pages in "
+                       "request order vs shuffled"}
+    for order in ("sequential", "random"):
+        fns, keep = [], []
+        for i in range(2):
+            fn, nbytes, k = page_order_replica(env, order, 2000 + i)
+            fns.append(fn)
+            keep.append(k)
+        res[order] = dict(kernel="kv_dequantize_paged", bytes=nbytes, **rates(nbytes, env.steady(fns, iters, warmup)))
+        del fns, keep
+        torch.cuda.empty_cache()
+    return res
+
+
 def leg_copy(env, nbytes, iters, warmup):
     torch = env.torch
     pairs = []
@@ -353,6 +392,30 @@ def recorded_traffic():
         return None
 
 
+def graph_latency(env, fns, per_graph, replays):
+    """Mean time per call of fns[i % len(fns)] captured `per_graph` times
+    into one HIP graph and replayed `replays` times (ms)."""
+    torch = env.torch
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fns[i % len(fns)]()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * per_graph)
+    del g
+    return ms
+
+
 def replicas_for(read_bytes: int) -> int:
     """Replicas whose inputs together exceed ~2.5x the 256 MB Infinity Cache,
     so every launch reads its inputs from HBM, as a serving step does (a
@@ -369,41 +432,49 @@ def rates(nbytes, r):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode step
 # ---------------------------------------------------------------------------
-def cpu_baseline(sample_requests: int, ps=16, H=8, D=128, pool=20000, seed=1002):
+def cpu_baseline(min_seconds: float, ps=16, H=8, D=128, pool=20000, seed=1002):
+    """The oracle on the host cores: the whole decode step (quantize-append of
+    the 64 new tokens, then dequantize of the full 124,503-token context),
+    repeated until at least `min_seconds` have passed (3 times at least);
+    the median step time gives the rate. The history is quantized first, by
+    the oracle, outside the timing."""
     import oracle
     import workloads as W
     rng = np.random.default_rng(seed)
     old, new_len, indices, indptr, last, bt = W.decode_append_tables(rng, 64, 4096, pool, ps)
     a_k, a_v = W.head_scales(rng, H), W.head_scales(rng, H)
-    R = sample_requests
+    B = len(old)
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     cache = W.make_cache(rng, pool, ps, H, D, W.NHD, fill="zero")
-    hist = int(old[:R].sum())
+    hist = int(old.sum())
     hk = W.f32_to_bits(W.head_scaled_normal(rng, hist, a_k, D), True)
     hv = W.f32_to_bits(W.head_scaled_normal(rng, hist, a_v, D), True)
-    nk = W.f32_to_bits(W.head_scaled_normal(rng, R, a_k, D), True)
-    nv = W.f32_to_bits(W.head_scaled_normal(rng, R, a_v, D), True)
+    nk = W.f32_to_bits(W.head_scaled_normal(rng, B, a_k, D), True)
+    nv = W.f32_to_bits(W.head_scaled_normal(rng, B, a_v, D), True)
     gk = oracle.global_scale(np.concatenate([hk.ravel(), nk.ravel()]), True)
     gv = oracle.global_scale(np.concatenate([hv.ravel(), nv.ravel()]), True)
-    hb, hp = W.rows_for_positions(np.zeros(R, np.int64), old[:R])
-    # only the first R requests: truncate the CSR table to them
-    ind_r, ptr_r, last_r = indices[:indptr[R]], indptr[:R + 1], last[:R]
-    oracle.quantize_append(cache, hk, hv, True, hb, hp, ind_r, ptr_r, last_r, gk, gv, threads=threads)
-    T = int(new_len[:R].max())
-    ok = np.zeros((R, T, H, D), np.uint16)
+    hb, hp = W.rows_for_positions(np.zeros(B, np.int64), old)
+    oracle.quantize_append(cache, hk, hv, True, hb, hp, indices, indptr, last, gk, gv, threads=threads)
+    del hk, hv
+    T = int(new_len.max())
+    ok = np.zeros((B, T, H, D), np.uint16)
     ov = np.zeros_like(ok)
-    t0 = time.perf_counter()
-    oracle.quantize_append(cache, nk, nv, True, np.arange(R, dtype=np.int32), old[:R].astype(np.int32),
-                           ind_r, ptr_r, last_r, gk, gv, threads=threads)
-    oracle.dequantize_paged(cache, np.ascontiguousarray(bt[:R]), new_len[:R].astype(np.int32), gk, gv, ok, ov, True,
-                            threads=threads)
-    dt = time.perf_counter() - t0
-    nbytes = append_bytes(R, H, D) + dequant_bytes(new_len[:R], ps, H, D, 4)
+    bi, pos = np.arange(B, dtype=np.int32), old.astype(np.int32)
+    lens = new_len.astype(np.int32)
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - t_all < min_seconds:
+        t0 = time.perf_counter()
+        oracle.quantize_append(cache, nk, nv, True, bi, pos, indices, indptr, last, gk, gv, threads=threads)
+        oracle.dequantize_paged(cache, bt, lens, gk, gv, ok, ov, True, threads=threads)
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
+    nbytes = append_bytes(B, H, D) + dequant_bytes(new_len, ps, H, D, 4)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": dt,
-            "sample": f"decode step restricted to the first {R} of 64 requests ({int(new_len[:R].sum())} context "
-                      f"tokens of 124,503): oracle quantize-append of their new tokens + dequantize of their "
-                      f"full context, {threads} threads"}
+            "seconds_per_step": dt, "steps": len(times),
+            "sample": f"the whole decode step (quantize-append of 64 new tokens + dequantize of the full "
+                      f"{int(new_len.sum())}-token context), {len(times)} repetitions in "
+                      f"{time.perf_counter() - t_all:.1f} s, median step time, {threads} threads"}
 
 
 # ---------------------------------------------------------------------------
@@ -413,11 +484,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--leg-iters", type=int, default=50)
-    ap.add_argument("--legs", default="prefill,materialize,four_over_six,copy",
+    ap.add_argument("--legs", default="prefill,materialize,four_over_six,page_order,copy",
                     help="comma list of legs to run after the headline step (empty: none)")
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time spent timing the oracle (whole decode steps)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged NVFP4 path needs no collectives and this build has no "
@@ -458,9 +530,12 @@ def main():
     value = step_bytes / (ms_step * 1e6)
     achieved = reps[0].dequant_bytes / (deq_avg * 1e6)
 
-    # append latency of the decode step, back to back
-    app_ms = env.steady([r.append for r in reps], 50, 5)[0]
-    legs = {"decode_append_us": app_ms * 1e3,
+    # append latency of the decode step: eager launches are bound by the
+    # host-side launch path at this size, so the kernel time comes from
+    # replays of a HIP graph holding 20 back-to-back appends
+    app_eager_ms = env.steady([r.append for r in reps], 50, 5)[0]
+    app_ms = graph_latency(env, [r.append for r in reps], 20, 10)
+    legs = {"decode_append_us": app_ms * 1e3, "decode_append_us_eager": app_eager_ms * 1e3,
             "decode_dequant": {"kernel": "kv_dequantize_paged", "bytes": reps[0].dequant_bytes,
                                "us_avg": deq_avg * 1e3, "us_median": statistics.median(deq_ms) * 1e3,
                                "GBps": achieved, "frac": achieved / PEAK_GBS}}
@@ -478,6 +553,8 @@ def main():
     if "four_over_six" in chosen:
         legs["four_over_six_quantize"] = leg_four_over_six(env, args.leg_iters, 5)
         torch.cuda.empty_cache()
+    if "page_order" in chosen:
+        legs["page_order_context"] = leg_page_order(env, args.leg_iters, 5)
     if "copy" in chosen:
         # also the known-size copy that calibrates the byte counters
         legs["copy_context"] = leg_copy(env, 1 << 29, args.leg_iters, 5)
@@ -485,7 +562,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
-        cpu = cpu_baseline(args.cpu_sample_requests)
+        cpu = cpu_baseline(args.cpu_seconds)
 
     out = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

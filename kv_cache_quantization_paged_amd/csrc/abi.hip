@@ -153,7 +153,8 @@ kvfp4_status_t kv_materialize_fp8(const kvfp4_paged_cache_t *cache, int32_t v_sf
     }
     return from_hip(launch_materialize_fp8(*cache, v_sf_interleaved != 0, block_tables, uses_shared_paged_kv_idx != 0,
                                            bt_row_stride, bt_kv_stride, seq_lens, kv_page_indptr, batch_size,
-                                           out_fp8, fp8_block_tables, max_pages_per_seq, (hipStream_t)stream));
+                                           out_fp8, num_out_pages, fp8_block_tables, max_pages_per_seq,
+                                           (hipStream_t)stream));
 }
 
 kvfp4_status_t kv_global_scale(const void *x, int32_t dtype, int64_t n, float e4m3_max, float *g_out, void *stream)

@@ -1,19 +1,22 @@
 // dequant.hip - paged NVFP4 gather-dequantize for gfx950
 // (FlashInfer page flashinfer.quantization.nvfp4_kv_dequantize_paged).
 //
-// Work item: one logical page j of one request b, K and V together (one
-// block-table lookup for both). The page's output rows out[b, j*ps + t, h, :]
-// (t < tokens of the page, every head) are one contiguous run of n_tok*H*D
-// 16-bit values, so lane l of a wavefront always stores the 16 bytes right
-// after lane l-1: each store instruction writes 1 KiB of contiguous HBM
-// whatever the cache layout. A lane owns 8 consecutive outputs per chunk:
-// 4 code bytes and its block's scale byte in, 16 bytes out. NHD vs HND only
-// changes where a chunk's code bytes are read. The grid has one workgroup per
-// (request, page) pair of the B * ceil(T/ps) table; workgroups past a
-// request's length exit at once. Active pages are scattered through that
-// table when lengths differ, and a persistent loop over it leaves some
-// workgroups with several times the work of others; one workgroup per pair
-// lets the dispatcher keep every CU busy.
+// Work item: up to kUnit chunks (kBatch per lane) of one logical page j of
+// one request b, K and V together (one block-table lookup for both). The
+// page's output rows out[b, j*ps + t, h, :] (t < tokens of the page, every
+// head) are one contiguous run of n_tok*H*D 16-bit values, so lane l of a
+// wavefront always stores the 16 bytes right after lane l-1: each store
+// instruction writes 1 KiB of contiguous HBM whatever the cache layout. A
+// lane owns 8 consecutive outputs per chunk: 4 code bytes and its block's
+// scale byte in, 16 bytes out. NHD vs HND only changes where a chunk's code
+// bytes are read. The grid has one workgroup per (request, page, part) of the
+// B * ceil(T/ps) table, so large pages still spread over many workgroups;
+// workgroups past a request's length exit at once. Active pages are scattered
+// through that table when lengths differ, and a persistent loop over it
+// leaves some workgroups with several times the work of others; one
+// workgroup per item lets the dispatcher keep every CU busy. The lengths, the
+// table and the global scales are read-only for the whole launch: as
+// __restrict__ kernel parameters their wave-uniform reads are scalar loads.
 //
 // value = RNE16(fp32(fp32(E4M3(s) * g) * e2m1(c))): the scale and the codes
 // are decoded by gfx950's conversion instructions (exact: E4M3 -> fp32, and
@@ -27,7 +30,8 @@ namespace kvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 16;           // chunks in flight per lane and tensor
+constexpr int kBatch = 8;            // chunks in flight per lane and tensor
+constexpr int kUnit = kBatch * kThreads;   // chunks per work item
 constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid size in work-items stays below 2^32)
 
 struct DequantArgs {
@@ -35,14 +39,12 @@ struct DequantArgs {
     const uint8_t *sf[2];
     int64_t stride[2];
     int64_t sf_stride[2];
-    const void *block_tables;
     int64_t bt_row_stride;
-    const int32_t *seq_lens;
-    const float *scale[2];
     uint16_t *out[2];
     int32_t ps, H, D, T;
     int32_t pages_per_req;   // ceil(T / ps)
-    int32_t num_pairs;       // B * pages_per_req
+    int32_t parts;           // work items per page: ceil(ps * H * D / 8 / kUnit)
+    int32_t num_items;       // B * pages_per_req * parts
 };
 
 // 4 code bytes (8 values) -> 4 packed 16-bit pairs
@@ -69,16 +71,19 @@ __device__ __forceinline__ u32x4 decode_chunk(uint32_t codes, float dec)
 }
 
 template <bool HND, bool BF16, bool BT64>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a)
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const void *__restrict__ block_tables,
+                                                           const int32_t *__restrict__ seq_lens,
+                                                           const float *__restrict__ k_scale,
+                                                           const float *__restrict__ v_scale)
 {
     const int cpr = a.D >> 3;                  // chunks per (token, head) row
     const int nb = a.D >> 4;
     const int tid = threadIdx.x;
-    // mixed-radix position of chunk (tid + 256 k): the row advances by r_step
+    // mixed-radix position of chunk (c + 256 k): the row advances by r_step
     // (+1 on a carry from cc), and the row's (t, h) follow
     const int r_step = kThreads / cpr, c_step = kThreads - r_step * cpr;
     const int rt_step = r_step / a.H, rh_step = r_step - rt_step * a.H;
-    const float g[2] = {*a.scale[0], *a.scale[1]};
+    const float g[2] = {*k_scale, *v_scale};
     // HND offset steps for kThreads chunks: base step, extra on a chunk-column
     // carry (next head row of the same token), extra on a head wrap (head 0 of
     // the next token)
@@ -92,19 +97,23 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a)
     const uint32_t page_bytes = (uint32_t)(a.ps * a.H * (a.D >> 1));
     const uint32_t page_sf_bytes = (uint32_t)(a.ps * a.H * nb);
 
-    // one pair per workgroup (the loop only repeats for tables of more than
-    // kMaxGrid pairs)
-    for (int pair = blockIdx.x; pair < a.num_pairs; pair += gridDim.x) {
+    // one item per workgroup (the loop only repeats for more than kMaxGrid)
+    for (int item = blockIdx.x; item < a.num_items; item += gridDim.x) {
+        const int pair = item / a.parts;
+        const int part = item - pair * a.parts;
         const int b = pair / a.pages_per_req;
         const int j = pair - b * a.pages_per_req;
-        const int len = uniform(min(a.seq_lens[b], a.T));
+        const int len = min(seq_lens[b], a.T);
         const int t_first = j * a.ps;
         if (t_first >= len)
             continue;
         const int n_tok = min(a.ps, len - t_first);
-        const int64_t page = uniform64(BT64 ? ((const int64_t *)a.block_tables)[b * a.bt_row_stride + j]
-                                            : (int64_t)((const int32_t *)a.block_tables)[b * a.bt_row_stride + j]);
         const int n_chunks = n_tok * a.H * cpr;
+        const int first = part * kUnit;
+        if (first >= n_chunks)
+            continue;
+        const int64_t page = BT64 ? ((const int64_t *)block_tables)[b * a.bt_row_stride + j]
+                                  : (int64_t)((const int32_t *)block_tables)[b * a.bt_row_stride + j];
         const int64_t out_off = ((int64_t)b * a.T + t_first) * a.H * a.D;
         // chunks past the page's valid tokens read zeros or in-page bytes and
         // their stores fall outside the outputs' ranges: no per-chunk branch
@@ -118,63 +127,70 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a)
         // pages share the geometry). NHD pages hold rows in output order, so
         // chunk ci sits at 4 ci / ci / 2. HND rows are (h, t): the offsets
         // follow the chunk's (h, cc) counters by additions only.
-        const int row0 = tid / cpr;
-        int cc = tid - row0 * cpr, h = row0 - (row0 / a.H) * a.H;
+        const int ci0 = first + tid;
+        const int row0 = ci0 / cpr;
+        int cc = ci0 - row0 * cpr, h = row0 - (row0 / a.H) * a.H;
         const int t0 = row0 / a.H;
         uint32_t off_c = (uint32_t)((h * a.ps + t0) * (a.D >> 1) + cc * 4);
         uint32_t off_s = (uint32_t)((h * a.ps + t0) * nb + (cc >> 1));
-        for (int base = 0; base < n_chunks; base += kBatch * kThreads) {
-            // every load of the round is issued before its first store: a wait
-            // for a load also waits for all earlier stores
-            uint32_t code[2][kBatch], sbyte[2][kBatch];
+        // every load of the item is issued before its first store: a wait
+        // for a load also waits for all earlier stores
+        uint32_t code[2][kBatch], sbyte[2][kBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                uint32_t oc, os;
-                if (!HND) {
-                    const uint32_t ci = (uint32_t)(base + u * kThreads + tid);
-                    oc = ci * 4u;
-                    os = ci >> 1;
-                } else {
-                    oc = off_c;
-                    os = off_s;
-                    // advance (h, cc) by kThreads chunks; cc keeps its parity
-                    // (cpr and c_step are even), so the scale offset moves by
-                    // exactly half the chunk-column step
-                    cc += c_step;
-                    const int carry = cc >= cpr;
-                    cc -= carry ? cpr : 0;
-                    h += rh_step + carry;
-                    const int wrap = h >= a.H;
-                    h -= wrap ? a.H : 0;
-                    off_c += (uint32_t)(k0_c + (carry ? kc_c : 0) + (wrap ? kw_c : 0));
-                    off_s += (uint32_t)(k0_s + (carry ? kc_s : 0) + (wrap ? kw_s : 0));
-                }
-#pragma unroll
-                for (int kv = 0; kv < 2; ++kv) {
-                    code[kv][u] = buf_load_u32(src[kv], oc);
-                    sbyte[kv][u] = buf_load_u8(sfs[kv], os);
-                }
+        for (int u = 0; u < kBatch; ++u) {
+            uint32_t oc, os;
+            if (!HND) {
+                const uint32_t ci = (uint32_t)(ci0 + u * kThreads);
+                oc = ci * 4u;
+                os = ci >> 1;
+            } else {
+                oc = off_c;
+                os = off_s;
+                // advance (h, cc) by kThreads chunks; cc keeps its parity
+                // (cpr and c_step are even), so the scale offset moves by
+                // exactly half the chunk-column step
+                cc += c_step;
+                const int carry = cc >= cpr;
+                cc -= carry ? cpr : 0;
+                h += rh_step + carry;
+                const int wrap = h >= a.H;
+                h -= wrap ? a.H : 0;
+                off_c += (uint32_t)(k0_c + (carry ? kc_c : 0) + (wrap ? kw_c : 0));
+                off_s += (uint32_t)(k0_s + (carry ? kc_s : 0) + (wrap ? kw_s : 0));
             }
 #pragma unroll
             for (int kv = 0; kv < 2; ++kv) {
+                code[kv][u] = buf_load_u32(src[kv], oc);
+                sbyte[kv][u] = buf_load_u8(sfs[kv], os);
+            }
+        }
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const uint32_t ci = (uint32_t)(base + u * kThreads + tid);
-                    const float dec = e4m3_byte_to_f32(sbyte[kv][u]) * g[kv];
-                    buf_store_u32x4_nt(decode_chunk<BF16>(code[kv][u], dec), dst[kv], ci * 16u);
-                }
+        for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const uint32_t ci = (uint32_t)(ci0 + u * kThreads);
+                const float dec = e4m3_byte_to_f32(sbyte[kv][u]) * g[kv];
+                buf_store_u32x4_nt(decode_chunk<BF16>(code[kv][u], dec), dst[kv], ci * 16u);
             }
         }
     }
 }
 
+struct DequantPtrs {
+    const void *block_tables;
+    const int32_t *seq_lens;
+    const float *k_scale, *v_scale;
+};
+
 template <bool HND, bool BF16>
-hipError_t launch3(bool bt64, const DequantArgs &a, int grid, hipStream_t st)
+hipError_t launch3(bool bt64, const DequantArgs &a, const DequantPtrs &p, int grid, hipStream_t st)
 {
     if (bt64)
-        hipLaunchKernelGGL((dequant_kernel<HND, BF16, true>), dim3(grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((dequant_kernel<HND, BF16, true>), dim3(grid), dim3(kThreads), 0, st, a, p.block_tables,
+                           p.seq_lens, p.k_scale, p.v_scale);
     else
-        hipLaunchKernelGGL((dequant_kernel<HND, BF16, false>), dim3(grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((dequant_kernel<HND, BF16, false>), dim3(grid), dim3(kThreads), 0, st, a, p.block_tables,
+                           p.seq_lens, p.k_scale, p.v_scale);
     return hipGetLastError();
 }
 
@@ -194,11 +210,7 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
     a.stride[1] = c.v_page_stride;
     a.sf_stride[0] = c.k_sf_page_stride;
     a.sf_stride[1] = c.v_sf_page_stride;
-    a.block_tables = block_tables;
     a.bt_row_stride = bt_row_stride;
-    a.seq_lens = seq_lens;
-    a.scale[0] = k_scale;
-    a.scale[1] = v_scale;
     a.out[0] = (uint16_t *)out_k;
     a.out[1] = (uint16_t *)out_v;
     a.ps = c.page_size;
@@ -206,17 +218,20 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
     a.D = c.head_dim;
     a.T = max_seq_len;
     a.pages_per_req = (max_seq_len + c.page_size - 1) / c.page_size;
-    const int64_t pairs = (int64_t)batch * a.pages_per_req;
-    if (pairs == 0)
+    const int64_t page_chunks = (int64_t)c.page_size * c.num_kv_heads * (c.head_dim / 8);
+    a.parts = (int32_t)((page_chunks + kUnit - 1) / kUnit);
+    const int64_t items = (int64_t)batch * a.pages_per_req * a.parts;
+    if (items == 0)
         return hipSuccess;
-    if (pairs > INT32_MAX)
+    if (items > INT32_MAX)
         return hipErrorInvalidValue;
-    a.num_pairs = (int32_t)pairs;
-    const int grid = (int)(pairs < kMaxGrid ? pairs : kMaxGrid);
+    a.num_items = (int32_t)items;
+    const DequantPtrs p = {block_tables, seq_lens, k_scale, v_scale};
+    const int grid = (int)(items < kMaxGrid ? items : kMaxGrid);
     const bool hnd = c.layout == KVFP4_HND;
     if (hnd)
-        return out_bf16 ? launch3<true, true>(bt64, a, grid, st) : launch3<true, false>(bt64, a, grid, st);
-    return out_bf16 ? launch3<false, true>(bt64, a, grid, st) : launch3<false, false>(bt64, a, grid, st);
+        return out_bf16 ? launch3<true, true>(bt64, a, p, grid, st) : launch3<true, false>(bt64, a, p, grid, st);
+    return out_bf16 ? launch3<false, true>(bt64, a, p, grid, st) : launch3<false, false>(bt64, a, p, grid, st);
 }
 
 }  // namespace kvfp4

@@ -26,7 +26,8 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
 hipError_t launch_materialize_fp8(const kvfp4_paged_cache_t &c, bool v_interleaved, const int32_t *bt,
                                   bool shared, int64_t bt_row_stride, int64_t bt_kv_stride,
                                   const int32_t *seq_lens, const int32_t *indptr, int32_t batch,
-                                  void *out, int32_t *table, int32_t maxp, hipStream_t st);
+                                  void *out, int64_t num_out_pages, int32_t *table, int32_t maxp,
+                                  hipStream_t st);
 
 hipError_t launch_global_scale(const void *x, bool bf16, int64_t n, float e4m3_max, float *g_out,
                                hipStream_t st);

@@ -173,13 +173,15 @@ __device__ __forceinline__ void buf_store_u32x4(u32x4 v, rsrc_t r, uint32_t off)
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
-// non-temporal ("nt") store: for outputs no later kernel in the same pass
-// reads back, so they stream to HBM instead of sitting dirty in the caches
-// (and being written back inside whatever runs next)
-constexpr int kNonTemporal = 2;
+// streaming store for outputs no later kernel in the same pass reads back:
+// non-temporal (nt) with system scope (sc1), so the lines go on to HBM instead
+// of sitting dirty in the caches (and being written back inside whatever runs
+// next). Measured 1-2% faster than nt alone on the dequant and materialize
+// streams.
+constexpr int kStreamStore = 2 | 16;     // cache-policy bits: nt | sc1
 __device__ __forceinline__ void buf_store_u32x4_nt(u32x4 v, rsrc_t r, uint32_t off)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStreamStore);
 }
 
 // ------------------------------------------------------- 16-bit floats ----
