@@ -100,6 +100,13 @@ def _load():
     lib.orc_materialize_fp8.restype = C.c_int
     lib.orc_materialize_fp8.argtypes = [C.POINTER(_Cache), C.c_int, P, C.c_int, i64, i64, i32, P, P,
                                         i32, P, i64, P, i32, C.c_int]
+    lib.orc_quantize_contiguous.restype = C.c_int
+    lib.orc_quantize_contiguous.argtypes = [P, C.c_int, i64, i64, f32, C.POINTER(_Recipe), P, P, C.c_int]
+    lib.orc_dequantize_contiguous.restype = C.c_int
+    lib.orc_dequantize_contiguous.argtypes = [P, P, i64, i64, f32, P, C.c_int, C.c_int]
+    lib.orc_quantize_paged_cache.restype = C.c_int
+    lib.orc_quantize_paged_cache.argtypes = [C.POINTER(_Cache), P, P, C.c_int, f32, f32, C.POINTER(_Recipe),
+                                             C.c_int, C.c_int]
     _lib = lib
     return lib
 
@@ -269,3 +276,52 @@ def materialize_fp8(cache, block_tables, seq_lens, kv_page_indptr, out, fp8_bloc
                                      _ptr(fp8_block_tables), fp8_block_tables.shape[1], int(threads))
     if rc != 0:
         raise ValueError(f"oracle materialize_fp8 rejected its arguments ({rc})")
+
+
+def quantize_contiguous(x_bits, in_is_bf16, g, recipe: Recipe = STANDARD, threads: int = 1):
+    """[KV] R10: uint16 bit patterns [..., cols] (cols % 16 == 0) -> (codes
+    uint8 [..., cols/2], scales uint8 [..., cols/16])."""
+    x = _need(np.asarray(x_bits), np.uint16, "x")
+    cols = x.shape[-1] if x.ndim else 0
+    rows = x.size // cols if cols else 0
+    codes = np.zeros(x.shape[:-1] + (cols // 2,), np.uint8)
+    scales = np.zeros(x.shape[:-1] + (cols // 16,), np.uint8)
+    rc = _load().orc_quantize_contiguous(_ptr(x), int(bool(in_is_bf16)), rows, cols, float(g),
+                                         C.byref(recipe._c()), _ptr(codes), _ptr(scales), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle quantize_contiguous rejected its arguments ({rc})")
+    return codes, scales
+
+
+def dequantize_contiguous(codes, scales, g, out_is_bf16, threads: int = 1):
+    """[KV] R10: codes [..., cols/2], scales [..., cols/16] -> uint16 [..., cols]."""
+    cd = _need(np.asarray(codes), np.uint8, "codes")
+    sc = _need(np.asarray(scales), np.uint8, "scales")
+    cols = cd.shape[-1] * 2
+    if sc.shape[:-1] != cd.shape[:-1] or sc.shape[-1] * 16 != cols:
+        raise ValueError("codes / scales shapes disagree")
+    rows = cd.size * 2 // cols if cols else 0
+    out = np.zeros(cd.shape[:-1] + (cols,), np.uint16)
+    rc = _load().orc_dequantize_contiguous(_ptr(cd), _ptr(sc), rows, cols, float(g), _ptr(out),
+                                           int(bool(out_is_bf16)), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle dequantize_contiguous rejected its arguments ({rc})")
+    return out
+
+
+def quantize_paged_cache(cache, k_in_bits, v_in_bits, in_is_bf16, k_scale, v_scale,
+                         recipe: Recipe = STANDARD, v_sf_interleaved: bool = True, threads: int = 1):
+    """[KV] R11 in place on ``cache``: pools [num_pages, ps, H, D] (NHD) or
+    [num_pages, H, ps, D] (HND) as uint16 bit patterns."""
+    cs = _cache_struct(cache.k_data, cache.v_data, cache.k_sf, cache.v_sf, cache.page_size,
+                       cache.num_heads, cache.head_dim, cache.layout)
+    k = _need(np.asarray(k_in_bits), np.uint16, "k_in")
+    v = _need(np.asarray(v_in_bits), np.uint16, "v_in")
+    n = cs.num_pages * cache.page_size * cache.num_heads * cache.head_dim
+    if k.size != n or v.size != n:
+        raise ValueError("pools must hold num_pages pages of the cache's geometry")
+    rc = _load().orc_quantize_paged_cache(C.byref(cs), _ptr(k), _ptr(v), int(bool(in_is_bf16)), float(k_scale),
+                                          float(v_scale), C.byref(recipe._c()), int(bool(v_sf_interleaved)),
+                                          int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle quantize_paged_cache rejected its arguments ({rc})")

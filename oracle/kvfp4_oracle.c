@@ -53,6 +53,17 @@
  *   R9  V block scales for materialize, when interleaved: inside a
  *       (page, head) tile, the scale of token t, block column c sits at byte
  *       ((t / 4) * (D / 16) + c) * 4 + t % 4.
+ *   R10 contiguous codec [KV]: the linear-layout quantize / dequantize of
+ *       the "FP4 KV Cache Quantization" section take the same global decode
+ *       scale g and the same block arithmetic (R1-R7) as the paged calls;
+ *       blocks of 16 run along the last dimension, scales are linear.
+ *   R11 whole-pool quantizer [KV] (nvfp4_quantize_paged_kv_cache, "for the
+ *       trtllm-gen MHA kernel"): quantizes every slot of every page with
+ *       R1-R5, K scales linear, V scales in the R9 interleave, which is the
+ *       layout [MF] says this function produces.
+ *
+ * [KV] flashinfer.quantization module page, "FP4 KV Cache Quantization"
+ *      (nvfp4_kv_quantize, nvfp4_kv_dequantize, nvfp4_quantize_paged_kv_cache).
  */
 #include "kvfp4_oracle.h"
 
@@ -701,5 +712,153 @@ int orc_materialize_fp8(const orc_cache_t *cache, int v_sf_interleaved,
                                   bt_kv_stride, seq_lens, kv_page_indptr, out, fp8_block_tables,
                                   max_pages_per_seq};
     parallel_for(batch_size, threads, materialize_requests, &ctx);
+    return 0;
+}
+
+/* ======================================================================== */
+/* contiguous codec [KV], R10                                                */
+/* ======================================================================== */
+struct contig_q_ctx {
+    const uint16_t *x;
+    int bf16;
+    int64_t cols;
+    float g;
+    const orc_recipe_t *recipe;
+    uint8_t *codes, *scales;
+};
+
+static void quantize_rows(void *vctx, int64_t lo, int64_t hi)
+{
+    const struct contig_q_ctx *a = (const struct contig_q_ctx *)vctx;
+    const int64_t nb = a->cols / 16;
+    for (int64_t r = lo; r < hi; r++)
+        for (int64_t blk = 0; blk < nb; blk++) {
+            float x[16];
+            uint8_t codes[16], s;
+            for (int i = 0; i < 16; i++)
+                x[i] = (float)orc_half_value(a->x[r * a->cols + blk * 16 + i], a->bf16);
+            quantize_block_unchecked(x, a->g, a->recipe, codes, &s, NULL, NULL, NULL);
+            a->scales[r * nb + blk] = s;
+            for (int j = 0; j < 8; j++)
+                a->codes[r * (a->cols / 2) + blk * 8 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        }
+}
+
+int orc_quantize_contiguous(const uint16_t *x, int in_is_bf16, int64_t rows, int64_t cols, float g,
+                            const orc_recipe_t *recipe, uint8_t *codes, uint8_t *scales, int threads)
+{
+    if (!recipe_ok(recipe) || rows < 0 || cols < 0 || cols % 16 != 0)
+        return -1;
+    if (rows == 0 || cols == 0)
+        return 0;
+    if (!x || !codes || !scales)
+        return -1;
+    if (!(g > 0.0f) || !isfinite(g))
+        return -2;
+    for (int64_t i = 0; i < rows * cols; i++)
+        if (!isfinite(orc_half_value(x[i], in_is_bf16)))
+            return -3;
+    struct contig_q_ctx ctx = {x, in_is_bf16, cols, g, recipe, codes, scales};
+    parallel_for(rows, threads, quantize_rows, &ctx);
+    return 0;
+}
+
+struct contig_dq_ctx {
+    const uint8_t *codes, *scales;
+    int64_t cols;
+    float g;
+    uint16_t *out;
+    int bf16;
+};
+
+static void dequantize_rows(void *vctx, int64_t lo, int64_t hi)
+{
+    const struct contig_dq_ctx *a = (const struct contig_dq_ctx *)vctx;
+    for (int64_t r = lo; r < hi; r++)
+        for (int64_t e = 0; e < a->cols; e++) {
+            uint8_t byte = a->codes[r * (a->cols / 2) + e / 2];
+            int code = (e & 1) ? (byte >> 4) : (byte & 15);
+            float dec = (float)orc_e4m3_value(a->scales[r * (a->cols / 16) + e / 16]) * a->g;   /* R7 */
+            a->out[r * a->cols + e] = orc_round_half(dec * (float)orc_e2m1_value(code), a->bf16);
+        }
+}
+
+int orc_dequantize_contiguous(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                              float g, uint16_t *out, int out_is_bf16, int threads)
+{
+    if (rows < 0 || cols < 0 || cols % 16 != 0)
+        return -1;
+    if (rows == 0 || cols == 0)
+        return 0;
+    if (!codes || !scales || !out)
+        return -1;
+    if (!isfinite(g))
+        return -2;
+    struct contig_dq_ctx ctx = {codes, scales, cols, g, out, out_is_bf16};
+    parallel_for(rows, threads, dequantize_rows, &ctx);
+    return 0;
+}
+
+/* ======================================================================== */
+/* whole-pool quantizer [KV], R11                                            */
+/* ======================================================================== */
+struct pool_ctx {
+    const orc_cache_t *c;
+    const uint16_t *k_in, *v_in;
+    int bf16;
+    float ks, vs;
+    const orc_recipe_t *recipe;
+    int v_interleaved;
+};
+
+static void quantize_pages(void *vctx, int64_t lo, int64_t hi)
+{
+    const struct pool_ctx *a = (const struct pool_ctx *)vctx;
+    const orc_cache_t *c = a->c;
+    const int64_t H = c->num_heads, D = c->head_dim, ps = c->page_size, nb = D / 16;
+    for (int64_t page = lo; page < hi; page++)
+        for (int kv = 0; kv < 2; kv++) {
+            const uint16_t *src = (kv ? a->v_in : a->k_in) + page * ps * H * D;
+            float g = kv ? a->vs : a->ks;
+            uint8_t *data = (kv ? c->v_data : c->k_data) + page * (kv ? c->v_page_stride : c->k_page_stride);
+            uint8_t *sf = (kv ? c->v_sf : c->k_sf) + page * (kv ? c->v_sf_page_stride : c->k_sf_page_stride);
+            for (int64_t t = 0; t < ps; t++)
+                for (int64_t h = 0; h < H; h++) {
+                    int64_t row = page_row(c, t, h);       /* the input page has the same row order */
+                    for (int64_t blk = 0; blk < nb; blk++) {
+                        float x[16];
+                        uint8_t codes[16], s;
+                        for (int i = 0; i < 16; i++)
+                            x[i] = (float)orc_half_value(src[row * D + blk * 16 + i], a->bf16);
+                        quantize_block_unchecked(x, g, a->recipe, codes, &s, NULL, NULL, NULL);
+                        for (int j = 0; j < 8; j++)
+                            data[row * (D / 2) + blk * 8 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+                        int64_t sidx;
+                        if (kv == 1 && a->v_interleaved)         /* R9 / R11 */
+                            sidx = h * ps * nb + ((t / 4) * nb + blk) * 4 + t % 4;
+                        else
+                            sidx = row * nb + blk;
+                        sf[sidx] = s;
+                    }
+                }
+        }
+}
+
+int orc_quantize_paged_cache(const orc_cache_t *cache, const uint16_t *k_in, const uint16_t *v_in,
+                             int in_is_bf16, float k_scale, float v_scale, const orc_recipe_t *recipe,
+                             int v_sf_interleaved, int threads)
+{
+    if (!cache_ok(cache) || !recipe_ok(recipe) || !k_in || !v_in)
+        return -1;
+    if (v_sf_interleaved && (cache->layout != 1 || cache->page_size % 4 != 0))
+        return -1;
+    if (!(k_scale > 0.0f) || !isfinite(k_scale) || !(v_scale > 0.0f) || !isfinite(v_scale))
+        return -2;
+    const int64_t n = (int64_t)cache->num_pages * cache->page_size * cache->num_heads * cache->head_dim;
+    for (int64_t i = 0; i < n; i++)
+        if (!isfinite(orc_half_value(k_in[i], in_is_bf16)) || !isfinite(orc_half_value(v_in[i], in_is_bf16)))
+            return -3;
+    struct pool_ctx ctx = {cache, k_in, v_in, in_is_bf16, k_scale, v_scale, recipe, v_sf_interleaved};
+    parallel_for(cache->num_pages, threads, quantize_pages, &ctx);
     return 0;
 }

@@ -85,6 +85,25 @@ int orc_materialize_fp8(const orc_cache_t *cache, int v_sf_interleaved,
                         uint8_t *out, int64_t num_out_pages,
                         int32_t *fp8_block_tables, int32_t max_pages_per_seq, int threads);
 
+/* ---- contiguous codec with linear block scales ------------------------- */
+/* x is [rows, cols] row-major fp16/bf16 with cols % 16 == 0; blocks of 16
+ * run along each row. codes [rows, cols/2] (low nibble = even element),
+ * scales [rows, cols/16]; g is the global decode scale. */
+int orc_quantize_contiguous(const uint16_t *x, int in_is_bf16, int64_t rows, int64_t cols, float g,
+                            const orc_recipe_t *recipe, uint8_t *codes, uint8_t *scales, int threads);
+int orc_dequantize_contiguous(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                              float g, uint16_t *out, int out_is_bf16, int threads);
+
+/* ---- whole-pool quantizer ---------------------------------------------- */
+/* k_in / v_in are contiguous fp16/bf16 pools of cache->num_pages pages, each
+ * page [ps, H, D] (NHD) or [H, ps, D] (HND) as cache->layout; every slot of
+ * every page is quantized into the cache (same layout, the cache's page
+ * strides). V scales are written 4-token interleaved when v_sf_interleaved
+ * (HND and page_size % 4 == 0 only), K scales always linear. */
+int orc_quantize_paged_cache(const orc_cache_t *cache, const uint16_t *k_in, const uint16_t *v_in,
+                             int in_is_bf16, float k_scale, float v_scale, const orc_recipe_t *recipe,
+                             int v_sf_interleaved, int threads);
+
 #ifdef __cplusplus
 }
 #endif
