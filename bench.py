@@ -308,6 +308,67 @@ def leg_four_over_six(env, iters, warmup):
     return res
 
 
+def codec_bytes(n_elems):
+    """16-bit values one way, packed codes and scales the other, plus g"""
+    return 2 * n_elems + n_elems // 2 + n_elems // 16 + 4
+
+
+def leg_contiguous(env, iters, warmup):
+    """kv_quantize / kv_dequantize of the 4over6 workload's K tensor seen as
+    a contiguous [65536, 1024] bf16 matrix (Student-t(3), 0.1% outliers)."""
+    torch, K = env.torch, env.K
+    rows, cols = 65536, 8 * 128
+    reps = []
+    for i in range(replicas_for(rows * cols * 2)):
+        g = env.gen(3000 + i)
+        x = student_t3(env, (rows, cols), g).to(torch.bfloat16)
+        gs = torch.empty(1, dtype=torch.float32, device=env.dev)
+        K.kv_global_scale(x, 256.0, gs)
+        d = torch.empty((rows, cols // 2), dtype=torch.uint8, device=env.dev)
+        sc = torch.empty((rows, cols // 16), dtype=torch.uint8, device=env.dev)
+        y = torch.empty_like(x)
+        reps.append((x, gs, d, sc, y))
+    nb = codec_bytes(rows * cols)
+    res = {"workload": "contiguous [65536, 1024] bf16, Student-t(3) with 0.1% entries x20, global scale for "
+                       "e4m3_max 256"}
+    for name, rec in (("quantize_standard", None), ("quantize_mse", K.Recipe(256.0, K.KVFP4_ERR_MSE)),
+                      ("quantize_mae", K.Recipe(256.0, K.KVFP4_ERR_MAE))):
+        fns = [(lambda r=r, rec=rec: K.kv_quantize(r[0], r[1], r[2], r[3], rec)) for r in reps]
+        res[name] = dict(kernel="kv_quantize", bytes=nb, **rates(nb, env.steady(fns, iters, warmup)))
+    fns = [(lambda r=r: K.kv_dequantize(r[2], r[3], r[1], r[4])) for r in reps]
+    res["dequantize"] = dict(kernel="kv_dequantize", bytes=nb, **rates(nb, env.steady(fns, iters, warmup)))
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
+def leg_pool_quantize(env, iters, warmup):
+    """kv_quantize_paged_cache of a bf16 N(0,1) pool in the materialize
+    workload's geometry (12,070 HND pages of 16 tokens, 8 heads, head_dim
+    128), V scales 4-token interleaved, standard recipe."""
+    torch, K = env.torch, env.K
+    P, ps, H, D = 12070, 16, 8, 128
+    reps = []
+    for i in range(replicas_for(2 * P * ps * H * D * 2)):
+        g = env.gen(4000 + i)
+        k = torch.randn((P, H, ps, D), generator=g, device=env.dev).to(torch.bfloat16)
+        v = torch.randn((P, H, ps, D), generator=g, device=env.dev).to(torch.bfloat16)
+        gk = torch.empty(1, dtype=torch.float32, device=env.dev)
+        gv = torch.empty(1, dtype=torch.float32, device=env.dev)
+        K.kv_global_scale(k, 448.0, gk)
+        K.kv_global_scale(v, 448.0, gv)
+        cache, keep = env.cache(P, ps, H, D, K.KVFP4_HND, 4100 + i)
+        reps.append((k, v, gk, gv, cache, keep))
+    nb = 2 * codec_bytes(P * ps * H * D)
+    fns = [(lambda r=r: K.kv_quantize_paged_cache(r[4], r[0], r[1], r[2], r[3], None, True)) for r in reps]
+    res = dict(kernel="kv_quantize_paged_cache", bytes=nb, **rates(nb, env.steady(fns, iters, warmup)))
+    res["workload"] = ("whole-pool quantize: 12,070 HND pages x (16 tokens, 8 heads, head_dim 128), bf16 N(0,1) "
+                       "K and V, standard recipe, V scales 4-token interleaved")
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
 def page_order_replica(env, order, seed):
     """64 full 4096-token requests in decode geometry (page_size 16, 8 heads,
     head_dim 128, NHD, bf16 out); `order` "random" shuffles the 16,384 pages
@@ -484,7 +545,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--leg-iters", type=int, default=50)
-    ap.add_argument("--legs", default="prefill,materialize,four_over_six,page_order,copy",
+    ap.add_argument("--legs", default="prefill,materialize,four_over_six,contiguous,pool_quantize,page_order,copy",
                     help="comma list of legs to run after the headline step (empty: none)")
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -552,6 +613,11 @@ def main():
         torch.cuda.empty_cache()
     if "four_over_six" in chosen:
         legs["four_over_six_quantize"] = leg_four_over_six(env, args.leg_iters, 5)
+        torch.cuda.empty_cache()
+    if "contiguous" in chosen:
+        legs["contiguous_codec"] = leg_contiguous(env, args.leg_iters, 5)
+    if "pool_quantize" in chosen:
+        legs["pool_quantize"] = leg_pool_quantize(env, args.leg_iters, 5)
         torch.cuda.empty_cache()
     if "page_order" in chosen:
         legs["page_order_context"] = leg_page_order(env, args.leg_iters, 5)

@@ -1,12 +1,16 @@
 /*
  * kvfp4.h - C ABI of the paged NVFP4 KV-cache library for AMD MI355X (gfx950).
  *
- * Four calls, all asynchronous on a caller-given HIP stream:
+ * Calls, all asynchronous on a caller-given HIP stream:
  *   kv_quantize_append   fp16/bf16 K/V rows -> packed E2M1 + E4M3 block scales
  *                        in paged NHD/HND caches addressed by a CSR page table
  *   kv_dequantize_paged  paged NVFP4 -> contiguous [B, T, H, D] fp16/bf16
  *   kv_materialize_fp8   active pages -> float8_e4m3fn page copy + block table
  *   kv_global_scale      per-tensor global decode scale amax / (6 * e4m3_max)
+ *   kv_quantize          contiguous fp16/bf16 -> NVFP4 with linear scales
+ *   kv_dequantize        contiguous NVFP4 with linear scales -> fp16/bf16
+ *   kv_quantize_paged_cache  a whole 16-bit page pool -> NVFP4 cache, V
+ *                        scales optionally 4-token interleaved
  *
  * Sources (FlashInfer 0.7.4 documentation): the API pages
  * flashinfer.page.nvfp4_quantize_append_paged_kv_cache,
@@ -195,6 +199,53 @@ kvfp4_status_t kv_materialize_fp8(const kvfp4_paged_cache_t *cache, int32_t v_sf
  */
 kvfp4_status_t kv_global_scale(const void *x, int32_t dtype, int64_t n, float e4m3_max,
                                float *g_out, void *stream);
+
+/*
+ * kv_quantize - nvfp4_kv_quantize(input, global_scale) (module page, "FP4 KV
+ * Cache Quantization": the NVFP4 KV-cache format with the linear block-scale
+ * layout). input is [rows, cols] row-major fp16/bf16 (in_dtype), cols a
+ * multiple of 16; blocks of 16 run along each row. fp4_data receives
+ * [rows, cols/2] packed codes (even element in the low nibble), block_scales
+ * [rows, cols/16] E4M3 bytes. global_scale points to one device fp32, the
+ * global decode scale g (as make_nvfp4_global_scale returns it). The block
+ * arithmetic is the append's: amax / (6 g) clamped at 448, or at the recipe's
+ * e4m3_max with the two-candidate 4over6 search (recipe non-NULL). input and
+ * fp4_data must be 16-byte aligned; rows * cols / 16 < 2^31. rows == 0 is a
+ * no-op. Rejects err_use_fast_math like kv_quantize_append.
+ */
+kvfp4_status_t kv_quantize(const void *input, int32_t in_dtype, int64_t rows, int64_t cols,
+                           const float *global_scale, const kvfp4_recipe_t *recipe,
+                           void *fp4_data, void *block_scales, void *stream);
+
+/*
+ * kv_dequantize - nvfp4_kv_dequantize(fp4_data, block_scales, ...) (module
+ * page, "FP4 KV Cache Quantization"): the inverse layout of kv_quantize.
+ * out[r, e] = RNE_{f16|bf16}(fp32(fp32(E4M3(s) * g) * e2m1(c))), the paged
+ * dequant's arithmetic. fp4_data [rows, cols/2], block_scales [rows, cols/16],
+ * output [rows, cols] of out_dtype; global_scale points to one device fp32.
+ * fp4_data and output must be 16-byte aligned, cols a multiple of 16.
+ */
+kvfp4_status_t kv_dequantize(const void *fp4_data, const void *block_scales, int64_t rows, int64_t cols,
+                             const float *global_scale, void *output, int32_t out_dtype, void *stream);
+
+/*
+ * kv_quantize_paged_cache - nvfp4_quantize_paged_kv_cache(k_cache, v_cache)
+ * (module page, "FP4 KV Cache Quantization"; the materialize page names it as
+ * the producer of 4-token-interleaved V scales): quantizes every slot of every
+ * page of two 16-bit page pools into `cache`. k_in / v_in are contiguous
+ * [cache->num_pages, page_size, H, D] (NHD) or [num_pages, H, page_size, D]
+ * (HND) fp16/bf16 pools in the cache's layout; page p of the pool lands in
+ * page p of the cache (page strides as in the descriptor; padding bytes are
+ * not written). k_scale / v_scale point to one device fp32 each (global
+ * decode scales, e.g. from kv_global_scale). K scales are written linear; V
+ * scales 4-token interleaved when v_sf_interleaved != 0 (HND and
+ * page_size % 4 == 0 required), linear otherwise. recipe as for append.
+ * k_in, v_in must be 16-byte aligned; num_pages * page_size * H * D / 16 <
+ * 2^31.
+ */
+kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const void *k_in, const void *v_in,
+                                       int32_t in_dtype, const float *k_scale, const float *v_scale,
+                                       const kvfp4_recipe_t *recipe, int32_t v_sf_interleaved, void *stream);
 
 /* Static description of a status code. */
 const char *kvfp4_status_string(kvfp4_status_t status);

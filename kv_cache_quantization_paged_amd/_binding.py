@@ -23,7 +23,7 @@ KVFP4_I32, KVFP4_I64 = 0, 1
 KVFP4_ERR_MSE, KVFP4_ERR_MAE = 0, 1
 
 EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
-            "kvfp4_status_string")
+            "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kvfp4_status_string")
 
 
 class PagedCacheDesc(C.Structure):
@@ -73,6 +73,13 @@ def load_library():
                                        P, i64, P, i32, P]
     lib.kv_global_scale.restype = i32
     lib.kv_global_scale.argtypes = [P, i32, i64, f32, P, P]
+    lib.kv_quantize.restype = i32
+    lib.kv_quantize.argtypes = [P, i32, i64, i64, P, C.POINTER(RecipeDesc), P, P, P]
+    lib.kv_dequantize.restype = i32
+    lib.kv_dequantize.argtypes = [P, P, i64, i64, P, P, i32, P]
+    lib.kv_quantize_paged_cache.restype = i32
+    lib.kv_quantize_paged_cache.argtypes = [C.POINTER(PagedCacheDesc), P, P, i32, P, P, C.POINTER(RecipeDesc),
+                                            i32, P]
     lib.kvfp4_status_string.restype = C.c_char_p
     lib.kvfp4_status_string.argtypes = [i32]
     _lib = lib
@@ -260,3 +267,68 @@ def kv_global_scale(x, e4m3_max: float, g_out, stream=None):
     st = lib.kv_global_scale(_ptr(x), _half_enum(x.dtype), x.numel(), float(e4m3_max), _ptr(g_out),
                              _stream(stream))
     _check(st, "kv_global_scale")
+
+
+def _need_scale(t, name):
+    if t.dtype != torch.float32 or not t.is_cuda or t.numel() < 1:
+        raise TypeError(f"{name} must be a float32 CUDA tensor")
+
+
+def kv_quantize(x, global_scale, fp4_data, block_scales, recipe: Recipe | None = None, stream=None):
+    """x [..., cols] fp16/bf16 -> fp4_data uint8 [..., cols/2], block_scales
+    uint8 [..., cols/16] (all contiguous CUDA tensors)."""
+    lib = load_library()
+    _need_scale(global_scale, "global_scale")
+    if not (x.is_cuda and x.is_contiguous() and fp4_data.is_contiguous() and block_scales.is_contiguous()):
+        raise ValueError("x, fp4_data and block_scales must be contiguous CUDA tensors")
+    if x.dim() < 1:
+        raise ValueError("x needs a last dimension")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    if fp4_data.dtype != torch.uint8 or block_scales.dtype != torch.uint8:
+        raise TypeError("fp4_data and block_scales are uint8")
+    if fp4_data.numel() != rows * (cols // 2) or block_scales.numel() != rows * (cols // 16):
+        raise ValueError("fp4_data must hold [..., cols/2] and block_scales [..., cols/16] bytes")
+    rd = recipe.desc() if recipe is not None else None
+    st = lib.kv_quantize(_ptr(x), _half_enum(x.dtype), rows, cols, _ptr(global_scale),
+                         C.byref(rd) if rd is not None else None, _ptr(fp4_data), _ptr(block_scales),
+                         _stream(stream))
+    _check(st, "kv_quantize")
+
+
+def kv_dequantize(fp4_data, block_scales, global_scale, output, stream=None):
+    """fp4_data uint8 [..., cols/2], block_scales uint8 [..., cols/16] ->
+    output fp16/bf16 [..., cols]."""
+    lib = load_library()
+    _need_scale(global_scale, "global_scale")
+    if not (output.is_cuda and output.is_contiguous() and fp4_data.is_contiguous() and block_scales.is_contiguous()):
+        raise ValueError("fp4_data, block_scales and output must be contiguous CUDA tensors")
+    cols = output.shape[-1]
+    rows = output.numel() // cols if cols else 0
+    if fp4_data.dtype != torch.uint8 or block_scales.dtype != torch.uint8:
+        raise TypeError("fp4_data and block_scales are uint8")
+    if fp4_data.numel() != rows * (cols // 2) or block_scales.numel() != rows * (cols // 16):
+        raise ValueError("fp4_data must hold [..., cols/2] and block_scales [..., cols/16] bytes")
+    st = lib.kv_dequantize(_ptr(fp4_data), _ptr(block_scales), rows, cols, _ptr(global_scale), _ptr(output),
+                           _half_enum(output.dtype), _stream(stream))
+    _check(st, "kv_dequantize")
+
+
+def kv_quantize_paged_cache(cache: PagedCache, k_in, v_in, k_scale, v_scale, recipe: Recipe | None = None,
+                            v_sf_interleaved: bool = True, stream=None):
+    """Quantize whole 16-bit page pools (contiguous, the cache's layout and
+    page count) into ``cache``."""
+    lib = load_library()
+    _need_scale(k_scale, "k_scale")
+    _need_scale(v_scale, "v_scale")
+    n = cache.num_pages * cache.page_size * cache.num_kv_heads * cache.head_dim
+    for t, name in ((k_in, "k_in"), (v_in, "v_in")):
+        if not (t.is_cuda and t.is_contiguous()) or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous CUDA pool of num_pages pages of the cache's geometry")
+    if k_in.dtype != v_in.dtype:
+        raise ValueError("k_in and v_in must have the same dtype")
+    rd = recipe.desc() if recipe is not None else None
+    st = lib.kv_quantize_paged_cache(C.byref(cache.desc), _ptr(k_in), _ptr(v_in), _half_enum(k_in.dtype),
+                                     _ptr(k_scale), _ptr(v_scale), C.byref(rd) if rd is not None else None,
+                                     int(bool(v_sf_interleaved)), _stream(stream))
+    _check(st, "kv_quantize_paged_cache")

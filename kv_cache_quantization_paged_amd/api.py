@@ -7,6 +7,8 @@
   flashinfer.quantization module page)
 * ``NVFP44Over6Config``, ``make_nvfp4_global_scale``, ``nvfp4_e4m3_max``
   (module page, "NVFP4 4over6 Recipes")
+* ``nvfp4_kv_quantize``, ``nvfp4_kv_dequantize``,
+  ``nvfp4_quantize_paged_kv_cache`` (module page, "FP4 KV Cache Quantization")
 
 Caches are given as on the pages: a (K, V) tuple of uint8 tensors or one
 stacked 5-D tensor with K/V on dimension 1, in "NHD" or "HND" layout. This
@@ -168,3 +170,60 @@ class NVFP4KVMaterializer:
         B.kv_materialize_fp8(cache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
                              self.shared, self.v_sf_interleaved)
         return out, fp8_block_tables
+
+
+# ---------------------------------------------------------------------------
+# contiguous codec and whole-pool quantizer ("FP4 KV Cache Quantization")
+# ---------------------------------------------------------------------------
+def nvfp4_kv_quantize(input: torch.Tensor, global_scale: torch.Tensor,
+                      nvfp4_4over6: Optional[NVFP44Over6Config] = None):
+    """NVFP4 with the linear block-scale layout: returns (fp4_data uint8
+    [..., D/2], block_scales uint8 [..., D/16]). ``global_scale`` is the
+    1-element float32 decode scale (``make_nvfp4_global_scale`` with the same
+    recipe)."""
+    x = input.contiguous()
+    D = x.shape[-1]
+    data = torch.empty(x.shape[:-1] + (D // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (D // 16,), dtype=torch.uint8, device=x.device)
+    recipe = nvfp4_4over6._recipe() if nvfp4_4over6 is not None else None
+    B.kv_quantize(x, global_scale, data, scales, recipe)
+    return data, scales
+
+
+def nvfp4_kv_dequantize(fp4_data: torch.Tensor, block_scales: torch.Tensor, global_scale: torch.Tensor,
+                        output_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """Inverse of ``nvfp4_kv_quantize``: [..., D] in ``output_dtype``."""
+    if out is None:
+        out = torch.empty(fp4_data.shape[:-1] + (2 * fp4_data.shape[-1],), dtype=output_dtype,
+                          device=fp4_data.device)
+    B.kv_dequantize(fp4_data.contiguous(), block_scales.contiguous(), global_scale, out)
+    return out
+
+
+def nvfp4_quantize_paged_kv_cache(k_cache: torch.Tensor, v_cache: torch.Tensor, kv_layout: str = "HND",
+                                  k_global_scale: Optional[torch.Tensor] = None,
+                                  v_global_scale: Optional[torch.Tensor] = None,
+                                  v_sf_interleaved: bool = True,
+                                  nvfp4_4over6: Optional[NVFP44Over6Config] = None):
+    """Quantize 16-bit page pools [num_pages, H, ps, D] (HND) or
+    [num_pages, ps, H, D] (NHD) to NVFP4. Returns (k_data, v_data, k_sf,
+    v_sf, k_global_scale, v_global_scale); V scales are 4-token interleaved
+    (the layout the FP8 materializer reads) unless ``v_sf_interleaved`` is
+    False. Missing global scales are built from the pools with the recipe."""
+    layout = _layout(kv_layout)
+    k, v = k_cache.contiguous(), v_cache.contiguous()
+    if k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("k_cache and v_cache must be matching 4-D page pools")
+    if k_global_scale is None:
+        k_global_scale = make_nvfp4_global_scale(k, nvfp4_4over6_config=nvfp4_4over6)
+    if v_global_scale is None:
+        v_global_scale = make_nvfp4_global_scale(v, nvfp4_4over6_config=nvfp4_4over6)
+    P, D = k.shape[0], k.shape[3]
+    kd = torch.empty(k.shape[:3] + (D // 2,), dtype=torch.uint8, device=k.device)
+    vd = torch.empty_like(kd)
+    ks = torch.empty(k.shape[:3] + (D // 16,), dtype=torch.uint8, device=k.device)
+    vs = torch.empty_like(ks)
+    cache = B.PagedCache(kd, vd, ks, vs, layout)
+    recipe = nvfp4_4over6._recipe() if nvfp4_4over6 is not None else None
+    B.kv_quantize_paged_cache(cache, k, v, k_global_scale, v_global_scale, recipe, v_sf_interleaved)
+    return kd, vd, ks, vs, k_global_scale, v_global_scale

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libkvfp4.so")
-SOURCES = ["abi.hip", "append.hip", "dequant.hip", "materialize.hip", "global_scale.hip"]
+SOURCES = ["abi.hip", "append.hip", "dequant.hip", "materialize.hip", "global_scale.hip", "codec.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

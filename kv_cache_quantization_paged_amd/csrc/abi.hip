@@ -56,6 +56,21 @@ kvfp4_status_t check_cache(const kvfp4_paged_cache_t *c)
 
 kvfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? KVFP4_OK : KVFP4_ELAUNCH; }
 
+kvfp4_status_t check_recipe(const kvfp4_recipe_t *recipe)
+{
+    if (!recipe)
+        return KVFP4_OK;
+    if (!(recipe->e4m3_max > 0.0f && recipe->e4m3_max <= 448.0f) || !is_finite_e4m3_value(recipe->e4m3_max))
+        return KVFP4_EINVAL;
+    if (recipe->err_mode != KVFP4_ERR_MSE && recipe->err_mode != KVFP4_ERR_MAE)
+        return KVFP4_EINVAL;
+    if (recipe->err_use_fast_math != 0)
+        return KVFP4_EUNSUPPORTED;
+    return KVFP4_OK;
+}
+
+constexpr int64_t kMaxBlocks = ((int64_t)1 << 31) - 1;   // blocks of 16 per quantize call and tensor
+
 }  // namespace
 
 extern "C" {
@@ -76,14 +91,9 @@ kvfp4_status_t kv_quantize_append(const kvfp4_paged_cache_t *cache, const void *
         return KVFP4_EINVAL;
     if (!(k_scale > 0.0f) || !isfinite(k_scale) || !(v_scale > 0.0f) || !isfinite(v_scale))
         return KVFP4_EINVAL;
-    if (recipe) {
-        if (!(recipe->e4m3_max > 0.0f && recipe->e4m3_max <= 448.0f) || !is_finite_e4m3_value(recipe->e4m3_max))
-            return KVFP4_EINVAL;
-        if (recipe->err_mode != KVFP4_ERR_MSE && recipe->err_mode != KVFP4_ERR_MAE)
-            return KVFP4_EINVAL;
-        if (recipe->err_use_fast_math != 0)
-            return KVFP4_EUNSUPPORTED;
-    }
+    s = check_recipe(recipe);
+    if (s != KVFP4_OK)
+        return s;
     if (nnz == 0)
         return KVFP4_OK;
     if (batch_size == 0 || !append_key || !append_value || !batch_indices || !positions || !kv_indices ||
@@ -170,6 +180,73 @@ kvfp4_status_t kv_global_scale(const void *x, int32_t dtype, int64_t n, float e4
     if (((uintptr_t)g_out & 3u) != 0)
         return KVFP4_EALIGN;
     return from_hip(launch_global_scale(x, dtype == KVFP4_BF16, n, e4m3_max, g_out, (hipStream_t)stream));
+}
+
+kvfp4_status_t kv_quantize(const void *input, int32_t in_dtype, int64_t rows, int64_t cols,
+                           const float *global_scale, const kvfp4_recipe_t *recipe,
+                           void *fp4_data, void *block_scales, void *stream)
+{
+    if (in_dtype != KVFP4_F16 && in_dtype != KVFP4_BF16)
+        return KVFP4_EINVAL;
+    if (rows < 0 || cols < 0 || cols % 16 != 0)
+        return KVFP4_EINVAL;
+    kvfp4_status_t s = check_recipe(recipe);
+    if (s != KVFP4_OK)
+        return s;
+    if (rows == 0 || cols == 0)
+        return KVFP4_OK;
+    if (!input || !global_scale || !fp4_data || !block_scales)
+        return KVFP4_EINVAL;
+    if (cols / 16 > kMaxBlocks / rows)
+        return KVFP4_EUNSUPPORTED;
+    if (!aligned16(input) || !aligned16(fp4_data))
+        return KVFP4_EALIGN;
+    return from_hip(launch_quantize_contiguous(input, in_dtype == KVFP4_BF16, rows, cols, global_scale, recipe,
+                                               fp4_data, block_scales, (hipStream_t)stream));
+}
+
+kvfp4_status_t kv_dequantize(const void *fp4_data, const void *block_scales, int64_t rows, int64_t cols,
+                             const float *global_scale, void *output, int32_t out_dtype, void *stream)
+{
+    if (out_dtype != KVFP4_F16 && out_dtype != KVFP4_BF16)
+        return KVFP4_EINVAL;
+    if (rows < 0 || cols < 0 || cols % 16 != 0)
+        return KVFP4_EINVAL;
+    if (rows == 0 || cols == 0)
+        return KVFP4_OK;
+    if (!fp4_data || !block_scales || !global_scale || !output)
+        return KVFP4_EINVAL;
+    if (cols / 8 > ((int64_t)1 << 40) / rows)
+        return KVFP4_EUNSUPPORTED;
+    if (!aligned16(fp4_data) || !aligned16(output))
+        return KVFP4_EALIGN;
+    return from_hip(launch_dequantize_contiguous(fp4_data, block_scales, rows, cols, global_scale, output,
+                                                 out_dtype == KVFP4_BF16, (hipStream_t)stream));
+}
+
+kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const void *k_in, const void *v_in,
+                                       int32_t in_dtype, const float *k_scale, const float *v_scale,
+                                       const kvfp4_recipe_t *recipe, int32_t v_sf_interleaved, void *stream)
+{
+    kvfp4_status_t s = check_cache(cache);
+    if (s != KVFP4_OK)
+        return s;
+    if (in_dtype != KVFP4_F16 && in_dtype != KVFP4_BF16)
+        return KVFP4_EINVAL;
+    s = check_recipe(recipe);
+    if (s != KVFP4_OK)
+        return s;
+    if (v_sf_interleaved && (cache->layout != KVFP4_HND || cache->page_size % 4 != 0))
+        return KVFP4_EINVAL;
+    if (!k_in || !v_in || !k_scale || !v_scale)
+        return KVFP4_EINVAL;
+    const int64_t blocks_per_page = (int64_t)cache->page_size * cache->num_kv_heads * (cache->head_dim / 16);
+    if (blocks_per_page > kMaxBlocks / cache->num_pages)
+        return KVFP4_EUNSUPPORTED;
+    if (!aligned16(k_in) || !aligned16(v_in))
+        return KVFP4_EALIGN;
+    return from_hip(launch_quantize_paged_cache(*cache, k_in, v_in, in_dtype == KVFP4_BF16, k_scale, v_scale,
+                                                recipe, v_sf_interleaved != 0, (hipStream_t)stream));
 }
 
 const char *kvfp4_status_string(kvfp4_status_t status)

@@ -32,4 +32,14 @@ hipError_t launch_materialize_fp8(const kvfp4_paged_cache_t &c, bool v_interleav
 hipError_t launch_global_scale(const void *x, bool bf16, int64_t n, float e4m3_max, float *g_out,
                                hipStream_t st);
 
+hipError_t launch_quantize_contiguous(const void *x, bool in_bf16, int64_t rows, int64_t cols, const float *g,
+                                      const kvfp4_recipe_t *recipe, void *codes, void *scales, hipStream_t st);
+
+hipError_t launch_dequantize_contiguous(const void *codes, const void *scales, int64_t rows, int64_t cols,
+                                        const float *g, void *out, bool out_bf16, hipStream_t st);
+
+hipError_t launch_quantize_paged_cache(const kvfp4_paged_cache_t &c, const void *k_in, const void *v_in,
+                                       bool in_bf16, const float *k_scale, const float *v_scale,
+                                       const kvfp4_recipe_t *recipe, bool v_interleaved, hipStream_t st);
+
 }  // namespace kvfp4

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
-                            "kvfp4_status_string"])
+                            "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -130,6 +130,53 @@ def test_global_scale_rejects_bad_arguments(B):
     assert lib.kv_global_scale(P(64), 1, 10, 448.0, None, None) == B.KVFP4_EINVAL
     assert lib.kv_global_scale(P(72), 1, 10, 448.0, P(64), None) == B.KVFP4_EALIGN
     assert lib.kv_global_scale(None, 1, 10, 448.0, P(64), None) == B.KVFP4_EINVAL
+
+
+def test_contiguous_codec_rejects_bad_arguments(B):
+    lib = B.load_library()
+    P = C.c_void_p
+
+    def q(x=P(4096), dt=1, rows=4, cols=64, g=P(64), recipe=None, d=P(8192), s=P(64)):
+        return lib.kv_quantize(x, dt, rows, cols, g, recipe, d, s, None)
+
+    def dq(d=P(8192), s=P(64), rows=4, cols=64, g=P(64), out=P(4096), dt=1):
+        return lib.kv_dequantize(d, s, rows, cols, g, out, dt, None)
+    assert q(dt=7) == B.KVFP4_EINVAL
+    assert q(cols=40) == B.KVFP4_EINVAL                                          # not a multiple of 16
+    assert q(rows=-1) == B.KVFP4_EINVAL
+    assert q(rows=0, x=None, d=None, s=None, g=None) == B.KVFP4_OK               # empty: nothing to do
+    assert q(g=None) == B.KVFP4_EINVAL
+    assert q(x=P(4104)) == B.KVFP4_EALIGN
+    assert q(d=P(8200)) == B.KVFP4_EALIGN
+    assert q(rows=1 << 40, cols=1 << 10) == B.KVFP4_EUNSUPPORTED                 # more than 2^31 blocks
+    bad = B.RecipeDesc(300.0, 0, 0)
+    assert q(recipe=C.byref(bad)) == B.KVFP4_EINVAL
+    fast = B.RecipeDesc(256.0, 0, 1)
+    assert q(recipe=C.byref(fast)) == B.KVFP4_EUNSUPPORTED
+    assert dq(dt=3) == B.KVFP4_EINVAL
+    assert dq(cols=24) == B.KVFP4_EINVAL
+    assert dq(rows=0, d=None, s=None, g=None, out=None) == B.KVFP4_OK
+    assert dq(s=None) == B.KVFP4_EINVAL
+    assert dq(out=P(4100)) == B.KVFP4_EALIGN
+    assert dq(d=P(8196)) == B.KVFP4_EALIGN
+
+
+def test_pool_quantizer_rejects_bad_arguments(B):
+    lib = B.load_library()
+    P = C.c_void_p
+
+    def call(cache, k=P(4096), v=P(8192), dt=1, ks=P(64), vs=P(64), recipe=None, inter=1):
+        return lib.kv_quantize_paged_cache(C.byref(cache), k, v, dt, ks, vs, recipe, inter, None)
+    hnd = dict(layout=1)
+    assert call(_cache(B)) == B.KVFP4_EINVAL                                     # interleave needs HND
+    assert call(_cache(B), inter=0, dt=2) == B.KVFP4_EINVAL
+    assert call(_cache(B, page_size=6, k_page_stride=3072, v_page_stride=3072, **hnd)) == B.KVFP4_EINVAL
+    assert call(_cache(B, **hnd), k=None) == B.KVFP4_EINVAL
+    assert call(_cache(B, **hnd), vs=None) == B.KVFP4_EINVAL
+    assert call(_cache(B, **hnd), v=P(8200)) == B.KVFP4_EALIGN
+    assert call(_cache(B, k_page_stride=100), inter=0) == B.KVFP4_EINVAL       # stride below a compact page
+    fast = B.RecipeDesc(256.0, 1, 1)
+    assert call(_cache(B, **hnd), recipe=C.byref(fast)) == B.KVFP4_EUNSUPPORTED
 
 
 def test_package_refuses_to_run_without_library(tmp_path, monkeypatch):
