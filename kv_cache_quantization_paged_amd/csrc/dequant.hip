@@ -1,7 +1,7 @@
 // dequant.hip - paged NVFP4 gather-dequantize for gfx950
 // (FlashInfer page flashinfer.quantization.nvfp4_kv_dequantize_paged).
 //
-// Work item: up to kUnit chunks (kBatch per lane) of one logical page j of
+// Work item: up to kBatch * 256 chunks (kBatch per lane) of one logical page j of
 // one request b, K and V together (one block-table lookup for both). The
 // page's output rows out[b, j*ps + t, h, :] (t < tokens of the page, every
 // head) are one contiguous run of n_tok*H*D 16-bit values, so lane l of a
@@ -30,8 +30,15 @@ namespace kvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 8;            // chunks in flight per lane and tensor
-constexpr int kUnit = kBatch * kThreads;   // chunks per work item
+// chunks in flight per lane and tensor. Smaller work items keep the output
+// window that the resident workgroups write at any moment narrower, which
+// the write stream rewards (NHD: 8 KiB of each output per item; 4 KiB items
+// are too short to cover their own latency); HND pages are read as H
+// separate head runs, which longer items keep whole.
+constexpr int kBatchNhd = 2;
+constexpr int kBatchHnd = 8;
+template <bool HND>
+constexpr int batch_of() { return HND ? kBatchHnd : kBatchNhd; }
 constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid size in work-items stays below 2^32)
 
 struct DequantArgs {
@@ -43,7 +50,7 @@ struct DequantArgs {
     uint16_t *out[2];
     int32_t ps, H, D, T;
     int32_t pages_per_req;   // ceil(T / ps)
-    int32_t parts;           // work items per page: ceil(ps * H * D / 8 / kUnit)
+    int32_t parts;           // work items per page: ceil(ps * H * D / 8 / (kBatch * kThreads))
     int32_t num_items;       // B * pages_per_req * parts
 };
 
@@ -76,6 +83,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const 
                                                            const float *__restrict__ k_scale,
                                                            const float *__restrict__ v_scale)
 {
+    constexpr int kBatch = batch_of<HND>();
+    constexpr int kUnit = kBatch * kThreads;   // chunks per work item
     const int cpr = a.D >> 3;                  // chunks per (token, head) row
     const int nb = a.D >> 4;
     const int tid = threadIdx.x;
@@ -219,7 +228,8 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
     a.T = max_seq_len;
     a.pages_per_req = (max_seq_len + c.page_size - 1) / c.page_size;
     const int64_t page_chunks = (int64_t)c.page_size * c.num_kv_heads * (c.head_dim / 8);
-    a.parts = (int32_t)((page_chunks + kUnit - 1) / kUnit);
+    const int64_t unit = (int64_t)(c.layout == KVFP4_HND ? kBatchHnd : kBatchNhd) * kThreads;
+    a.parts = (int32_t)((page_chunks + unit - 1) / unit);
     const int64_t items = (int64_t)batch * a.pages_per_req * a.parts;
     if (items == 0)
         return hipSuccess;

@@ -14,16 +14,15 @@
 // block then needs one 8-byte LDS read and a few v_perm byte selects per 8
 // elements. The sign is code sign XOR scale sign.
 //
-// Work item: output page p + 1 for p < kv_page_indptr[B], one per workgroup.
-// It belongs to the request b with indptr[b] <= p < indptr[b + 1] (a binary
-// search over the indptr in scalar registers) and is that request's page
-// j = p - indptr[b]; it is written only when j < ceil(seq_len / ps), so
+// Work item: a part of output page p + 1 for p < kv_page_indptr[B], one per
+// workgroup. The page belongs to the request b with
+// indptr[b] <= p < indptr[b + 1] (a binary search over the indptr in scalar
+// registers) and is that request's page j = p - indptr[b]; it is written only when j < ceil(seq_len / ps), so
 // reserved-but-unused pages and everything past kv_page_indptr[B] stay
 // untouched. Indexing reserved pages rather than the B x max_pages_per_seq
-// table gives every workgroup the same work however lengths are spread. A
-// round issues every load of the page (K and V) before its first store and
-// builds the table while the loads are in flight. Workgroup 0 also zeroes
-// output page 0.
+// table gives every workgroup the same work however lengths are spread. An
+// item issues all its loads (K and V) before its first store and builds the
+// table while the loads are in flight. Workgroup 0 also zeroes output page 0.
 #include "kvfp4_internal.h"
 #include "nvfp4_device.h"
 
@@ -32,7 +31,10 @@ namespace kvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRound = 4;                  // blocks per lane and tensor in one round
+// blocks per lane and tensor in one work item: a whole page (32 KiB of FP8
+// output per tensor) at 16 tokens x 8 heads x 128; half pages measured the
+// same, quarter pages slower. Larger pages split into several items.
+constexpr int kRound = 4;
 constexpr int64_t kMaxGrid = 1 << 20;      // work items past the grid loop round
 
 struct MatArgs {
@@ -46,6 +48,7 @@ struct MatArgs {
     int32_t ps, H, D;
     int32_t maxp;          // max_pages_per_seq: columns of the FP8 block table
     int32_t batch;
+    int32_t parts;         // work items per page: ceil(blocks per half page / (kRound * kThreads))
 };
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
@@ -80,16 +83,18 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const 
             buf_store_u32x4(u32x4{0u, 0u, 0u, 0u}, z, i * 16u);
     }
 
-    // block q = tid + k * kThreads of a half page is (h, t, c) with
-    // q = (h * ps + t) * nb + c; the lane advances it by kThreads blocks
+    // block q of a half page is (h, t, c) with q = (h * ps + t) * nb + c; the
+    // lane advances it by kThreads blocks
     const int c_step = kThreads % nb;
     const int t_all = kThreads / nb;
     const int t_step = t_all % a.ps, h_step = t_all / a.ps;
-    const int c0 = tid % nb, t0 = (tid / nb) % a.ps, h0 = tid / (nb * a.ps);
 
     bool have_lut = false;
-    const int n_work = a.batch > 0 ? indptr[a.batch] : 0;
-    for (int p = blockIdx.x; p < n_work; p += gridDim.x) {
+    const int64_t n_work = a.batch > 0 ? indptr[a.batch] : 0;
+    const int64_t n_items = n_work * a.parts;
+    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int p = (int)(item / a.parts);
+        const int part = (int)(item - (int64_t)p * a.parts);
         int lo = 0, hi = a.batch;              // indptr[lo] <= p < indptr[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const 
         const int64_t dst = (int64_t)p + 1;
         const int32_t *row = bt + b * a.bt_row_stride;
         const int64_t pg[2] = {row[j], SHARED ? row[j] : row[a.bt_kv_stride + j]};
-        if (tid == 0)
+        if (part == 0 && tid == 0)
             a.table[(int64_t)b * a.maxp + j] = (int32_t)dst;
         rsrc_t src[2], sfs[2], dsts[2];
 #pragma unroll
@@ -115,64 +120,64 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const 
             sfs[kv] = make_rsrc(a.sf[kv] + pg[kv] * a.sf_stride[kv], (uint32_t)bph);
             dsts[kv] = make_rsrc(a.out + (dst * 2 + kv) * (int64_t)half_bytes, half_bytes);
         }
-        int c = c0, t = t0, h = h0;
-        for (int base = 0; base < bph; base += kRound * kThreads) {
-            // every load of the round first: a wait for a load also waits for
-            // all earlier stores. Blocks past the page read zeros and their
-            // stores are dropped by the range checks.
-            u32x2 code[2][kRound];
-            uint32_t sb[2][kRound];
+        const int base = part * kRound * kThreads;
+        const int q0 = base + tid;
+        int c = q0 % nb, t = (q0 / nb) % a.ps, h = q0 / (nb * a.ps);
+        // every load of the item first: a wait for a load also waits for all
+        // earlier stores. Blocks past the page read zeros and their stores
+        // are dropped by the range checks.
+        u32x2 code[2][kRound];
+        uint32_t sb[2][kRound];
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) {
+            const uint32_t q = (uint32_t)(base + u * kThreads + tid);
+            const uint32_t vq = INTERLEAVED ? (uint32_t)((h * a.ps + (t & ~3)) * nb + c * 4 + (t & 3)) : q;
+            code[0][u] = buf_load_u32x2(src[0], q * 8u);
+            sb[0][u] = buf_load_u8(sfs[0], q);
+            code[1][u] = buf_load_u32x2(src[1], q * 8u);
+            sb[1][u] = buf_load_u8(sfs[1], vq);
+            if (INTERLEAVED) {
+                c += c_step;
+                const int carry = c >= nb;
+                c -= carry ? nb : 0;
+                t += t_step + carry;
+                h += h_step;
+                if (t >= a.ps) {
+                    t -= a.ps;
+                    h += 1;
+                }
+            }
+        }
+        if (!have_lut) {
+            // output magnitude byte for (scale byte = tid, code magnitude k),
+            // computed while this item's loads are in flight
+            const float sv = e4m3_to_f32((uint32_t)tid & 0x7Fu);
+            uint32_t lo4 = 0u, hi4 = 0u;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float prod = e2m1_code_to_mag((uint32_t)k) * sv;
+                const uint32_t byte = f32_to_e4m3_satfinite(prod, 0u);
+                if (k < 4)
+                    lo4 |= byte << (8 * k);
+                else
+                    hi4 |= byte << (8 * (k - 4));
+            }
+            lut[tid] = u32x2{lo4, hi4};
+            __syncthreads();
+            have_lut = true;
+        }
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
 #pragma unroll
             for (int u = 0; u < kRound; ++u) {
                 const uint32_t q = (uint32_t)(base + u * kThreads + tid);
-                const uint32_t vq = INTERLEAVED ? (uint32_t)((h * a.ps + (t & ~3)) * nb + c * 4 + (t & 3)) : q;
-                code[0][u] = buf_load_u32x2(src[0], q * 8u);
-                sb[0][u] = buf_load_u8(sfs[0], q);
-                code[1][u] = buf_load_u32x2(src[1], q * 8u);
-                sb[1][u] = buf_load_u8(sfs[1], vq);
-                if (INTERLEAVED) {
-                    c += c_step;
-                    const int carry = c >= nb;
-                    c -= carry ? nb : 0;
-                    t += t_step + carry;
-                    h += h_step;
-                    if (t >= a.ps) {
-                        t -= a.ps;
-                        h += 1;
-                    }
-                }
-            }
-            if (!have_lut) {
-                // output magnitude byte for (scale byte = tid, code magnitude k),
-                // computed while this round's loads are in flight
-                const float sv = e4m3_to_f32((uint32_t)tid & 0x7Fu);
-                uint32_t lo4 = 0u, hi4 = 0u;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float prod = e2m1_code_to_mag((uint32_t)k) * sv;
-                    const uint32_t byte = f32_to_e4m3_satfinite(prod, 0u);
-                    if (k < 4)
-                        lo4 |= byte << (8 * k);
-                    else
-                        hi4 |= byte << (8 * (k - 4));
-                }
-                lut[tid] = u32x2{lo4, hi4};
-                __syncthreads();
-                have_lut = true;
-            }
-#pragma unroll
-            for (int kv = 0; kv < 2; ++kv) {
-#pragma unroll
-                for (int u = 0; u < kRound; ++u) {
-                    const uint32_t q = (uint32_t)(base + u * kThreads + tid);
-                    const uint32_t s = sb[kv][u];
-                    const u32x2 l = lut[s];
-                    const uint32_t smask = (s & 0x80u) ? 0x80808080u : 0u;
-                    const uint2 lo8 = convert8(code[kv][u].x, l, smask);
-                    const uint2 hi8 = convert8(code[kv][u].y, l, smask);
-                    // the FP8 copy is read by a later kernel only
-                    buf_store_u32x4_nt(u32x4{lo8.x, lo8.y, hi8.x, hi8.y}, dsts[kv], q * 16u);
-                }
+                const uint32_t s = sb[kv][u];
+                const u32x2 l = lut[s];
+                const uint32_t smask = (s & 0x80u) ? 0x80808080u : 0u;
+                const uint2 lo8 = convert8(code[kv][u].x, l, smask);
+                const uint2 hi8 = convert8(code[kv][u].y, l, smask);
+                // the FP8 copy is read by a later kernel only
+                buf_store_u32x4_nt(u32x4{lo8.x, lo8.y, hi8.x, hi8.y}, dsts[kv], q * 16u);
             }
         }
     }
@@ -214,7 +219,9 @@ hipError_t launch_materialize_fp8(const kvfp4_paged_cache_t &c, bool v_interleav
     a.batch = batch;
     // kv_page_indptr[B] lives on the device; num_out_pages - 1 bounds it. At
     // least one workgroup runs, which zeroes page 0 for an empty batch.
-    const int64_t want = num_out_pages - 1 > 0 ? num_out_pages - 1 : 1;
+    const int bph = c.num_kv_heads * c.page_size * (c.head_dim / 16);
+    a.parts = (bph + kRound * kThreads - 1) / (kRound * kThreads);
+    const int64_t want = num_out_pages - 1 > 0 ? (num_out_pages - 1) * a.parts : 1;
     const int grid = (int)(want < kMaxGrid ? want : kMaxGrid);
     if (v_interleaved) {
         if (shared)
