@@ -37,7 +37,7 @@ class _Cache(C.Structure):
 
 
 class _Recipe(C.Structure):
-    _fields_ = [("four_over_six", C.c_int), ("e4m3_max", C.c_float), ("err_mode", C.c_int)]
+    _fields_ = [("four_over_six", C.c_int), ("e4m3_max", C.c_float), ("err_mode", C.c_int), ("err_fp16", C.c_int)]
 
 
 @dataclass(frozen=True)
@@ -47,16 +47,17 @@ class Recipe:
     four_over_six: bool = False
     e4m3_max: float = 448.0
     err_mode: int = MSE
+    err_fp16: bool = False
 
     def _c(self):
-        return _Recipe(int(self.four_over_six), float(self.e4m3_max), int(self.err_mode))
+        return _Recipe(int(self.four_over_six), float(self.e4m3_max), int(self.err_mode), int(self.err_fp16))
 
 
 STANDARD = Recipe()
 
 
-def four_over_six(err_mode: int = MSE, e4m3_max: float = 256.0) -> Recipe:
-    return Recipe(True, e4m3_max, err_mode)
+def four_over_six(err_mode: int = MSE, e4m3_max: float = 256.0, fast_math: bool = False) -> Recipe:
+    return Recipe(True, e4m3_max, err_mode, fast_math)
 
 
 def _load():

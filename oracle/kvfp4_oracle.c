@@ -57,6 +57,11 @@
  *       the "FP4 KV Cache Quantization" section take the same global decode
  *       scale g and the same block arithmetic (R1-R7) as the paged calls;
  *       blocks of 16 run along the last dimension, scales are linear.
+ *   R12 4over6 "err_use_fast_math" [R46]: the page says the error is then
+ *       evaluated in fp16 instead of exactly in fp32. Read as: x and the fp32
+ *       reconstruction rounded to fp16, then the difference, the square
+ *       (MSE) and each pairwise sum rounded to fp16 (RNE, overflow to inf);
+ *       the candidates compare as in R5.
  *   R11 whole-pool quantizer [KV] (nvfp4_quantize_paged_kv_cache, "for the
  *       trtllm-gen MHA kernel"): quantizes every slot of every page with
  *       R1-R5, K scales linear, V scales in the R9 interleave, which is the
@@ -194,18 +199,19 @@ double orc_half_value(uint16_t bits, int is_bf16)
     return s ? -v : v;
 }
 
-/* fp32 -> 16-bit float, round to nearest, ties to even, by the definition:
- * find the representable neighbours below and above |x| at the spacing of
- * its binade (or the subnormal spacing), take the nearer, on a tie the one
- * with an even last mantissa bit; past the largest finite value -> inf.     */
-uint16_t orc_round_half(float x, int is_bf16)
+/* real number (held exactly in a double) -> 16-bit float, round to nearest,
+ * ties to even, by the definition: find the representable neighbours below
+ * and above |x| at the spacing of its binade (or the subnormal spacing), take
+ * the nearer, on a tie the one with an even last mantissa bit; past the
+ * largest finite value -> inf.                                              */
+static uint16_t round_half_exact(double x, int is_bf16)
 {
     const struct half_fmt *f = is_bf16 ? &FMT_BF16 : &FMT_F16;
     uint16_t sign = signbit(x) ? 0x8000u : 0u;
     uint16_t exp_ones = (uint16_t)(((1u << f->ebits) - 1u) << f->p);
     if (isnan(x))
         return (uint16_t)(sign | exp_ones | (1u << (f->p - 1)));
-    double a = fabs((double)x);
+    double a = fabs(x);
     if (isinf(a))
         return (uint16_t)(sign | exp_ones);
     int e;
@@ -232,6 +238,18 @@ uint16_t orc_round_half(float x, int is_bf16)
     uint16_t mant = (uint16_t)(val / ldexp(1.0, ev - f->p) - ldexp(1.0, f->p));
     uint16_t ef = (uint16_t)(ev + f->bias);
     return (uint16_t)(sign | (uint16_t)(ef << f->p) | mant);
+}
+
+/* fp32 -> 16-bit float (RNE) */
+uint16_t orc_round_half(float x, int is_bf16)
+{
+    return round_half_exact((double)x, is_bf16);
+}
+
+/* the IEEE binary16 value nearest to v (ties to even), as a double */
+static double f16_round(double v)
+{
+    return orc_half_value(round_half_exact(v, 0), 0);
 }
 
 void orc_e2m1_encode_array(const float *v, int64_t n, uint8_t *out)
@@ -296,6 +314,25 @@ static float candidate_error(const float *x, const uint8_t *codes, float dec, in
     return t[0];
 }
 
+/* R12: the same error in IEEE binary16 arithmetic ("fast math"): the input
+ * and the fp32 reconstruction are each rounded to fp16, then the difference,
+ * the square (MSE) and every sum of the pairwise tree are rounded to fp16.
+ * Each operation is done exactly in double (the operands are fp16 values, so
+ * differences, squares and sums are exact there) and rounded once.          */
+static float candidate_error_fp16(const float *x, const uint8_t *codes, float dec, int err_mode)
+{
+    double t[16];
+    for (int i = 0; i < 16; i++) {
+        float deq = dec * (float)orc_e2m1_value(codes[i]);
+        double d = f16_round(f16_round((double)x[i]) - f16_round((double)deq));
+        t[i] = (err_mode == 0) ? f16_round(d * d) : fabs(d);
+    }
+    for (int w = 16; w > 1; w /= 2)
+        for (int j = 0; j < w / 2; j++)
+            t[j] = f16_round(t[2 * j] + t[2 * j + 1]);
+    return (float)t[0];
+}
+
 static int recipe_ok(const orc_recipe_t *r)
 {
     if (!r)
@@ -333,9 +370,9 @@ static void quantize_block_unchecked(const float *x, float g, const orc_recipe_t
     float d6, d4;
     int s6 = quantize_candidate(x, amax, g, 6.0f, e4m3_max, c6, &d6);   /* R4 */
     int s4 = quantize_candidate(x, amax, g, 4.0f, 448.0f, c4, &d4);     /* R4 */
-    float e6 = candidate_error(x, c6, d6, r->err_mode);
-    float e4 = candidate_error(x, c4, d4, r->err_mode);
-    int take4 = e4 < e6;                                                 /* R5 */
+    float e6 = r->err_fp16 ? candidate_error_fp16(x, c6, d6, r->err_mode) : candidate_error(x, c6, d6, r->err_mode);
+    float e4 = r->err_fp16 ? candidate_error_fp16(x, c4, d4, r->err_mode) : candidate_error(x, c4, d4, r->err_mode);
+    int take4 = e4 < e6;                          /* R5; an inf or NaN error never wins */
     memcpy(codes, take4 ? c4 : c6, 16);
     *scale = (uint8_t)(take4 ? s4 : s6);
     if (err6) *err6 = e6;

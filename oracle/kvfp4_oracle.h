@@ -38,11 +38,13 @@ void orc_round_half_array(const float *x, int64_t n, int is_bf16, uint16_t *out)
 
 /* ---- recipe ------------------------------------------------------------ */
 /* four_over_six = 0: standard amax/6 block scale clamped at e4m3_max.
- * four_over_six = 1: two-candidate search, err_mode 0 = MSE, 1 = MAE.   */
+ * four_over_six = 1: two-candidate search, err_mode 0 = MSE, 1 = MAE;
+ * err_fp16 = 1 evaluates the error in fp16 ("err_use_fast_math").       */
 typedef struct {
     int   four_over_six;
     float e4m3_max;
     int   err_mode;
+    int   err_fp16;
 } orc_recipe_t;
 
 /* One 16-element block. Writes the 16 codes and the chosen scale byte.
