@@ -280,7 +280,8 @@ def four_over_six_replica(env, seed=1005):
     sl = env.i32(np.full(B, T))
     fns = {}
     for name, recipe in (("mse", K.Recipe(256.0, K.KVFP4_ERR_MSE)), ("mae", K.Recipe(256.0, K.KVFP4_ERR_MAE)),
-                         ("standard", None)):
+                         ("mse16", K.Recipe(256.0, K.KVFP4_ERR_MSE, True)),
+                         ("mae16", K.Recipe(256.0, K.KVFP4_ERR_MAE, True)), ("standard", None)):
         fns["append_" + name] = (lambda r=recipe: K.kv_quantize_append(cache, key, val, bi, pos, ind, ptr, last,
                                                                        gkf, gvf, r))
     fns["dequant"] = lambda: K.kv_dequantize_paged(cache, bt, sl, gk, gv, ok, ov)
@@ -295,7 +296,8 @@ def leg_four_over_six(env, iters, warmup):
     res = {}
     ab = append_bytes(B * T, H, D)
     for name, recipe in (("mse", "4over6 e4m3_max=256 MSE"), ("mae", "4over6 e4m3_max=256 MAE"),
-                         ("standard", "standard amax/6")):
+                         ("mse16", "4over6 e4m3_max=256 MSE, error in fp16"),
+                         ("mae16", "4over6 e4m3_max=256 MAE, error in fp16"), ("standard", "standard amax/6")):
         r = env.steady([rep[0]["append_" + name] for rep in reps], iters, warmup)
         res["append_" + name] = dict(kernel="kv_quantize_append", recipe=recipe, bytes=ab, **rates(ab, r))
     db = dequant_bytes(np.full(B, T), ps, H, D, 4)

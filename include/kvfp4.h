@@ -72,8 +72,11 @@ enum { KVFP4_ERR_MSE = 0, KVFP4_ERR_MAE = 1 };        /* 4over6 error metrics */
  * A NULL recipe pointer selects standard NVFP4: amax/6 clamped at 448.
  *   e4m3_max           a finite E4M3 value in (0, 448]; 256 is the page's knob
  *   err_mode           KVFP4_ERR_MSE or KVFP4_ERR_MAE
- *   err_use_fast_math  must be 0: the fp16 error recipe is not implemented
- *                      (KVFP4_EUNSUPPORTED)
+ *   err_use_fast_math  nonzero: the error is evaluated in IEEE fp16 (the
+ *                      page's distinct "fast math" recipe): the input and the
+ *                      fp32 reconstruction rounded to fp16, then the
+ *                      difference, the square and every pairwise sum rounded
+ *                      to fp16; an inf or NaN error never wins
  */
 typedef struct {
     float e4m3_max;
@@ -211,7 +214,7 @@ kvfp4_status_t kv_global_scale(const void *x, int32_t dtype, int64_t n, float e4
  * arithmetic is the append's: amax / (6 g) clamped at 448, or at the recipe's
  * e4m3_max with the two-candidate 4over6 search (recipe non-NULL). input and
  * fp4_data must be 16-byte aligned; rows * cols / 16 < 2^31. rows == 0 is a
- * no-op. Rejects err_use_fast_math like kv_quantize_append.
+ * no-op.
  */
 kvfp4_status_t kv_quantize(const void *input, int32_t in_dtype, int64_t rows, int64_t cols,
                            const float *global_scale, const kvfp4_recipe_t *recipe,

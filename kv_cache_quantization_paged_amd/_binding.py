@@ -99,6 +99,18 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+def _stride(t, dim):
+    """Element stride of dimension `dim`; a dimension of size 1 may carry any
+    stride (torch and numpy give 0 to an inserted axis), so it reports the
+    stride it would have in a contiguous tensor instead."""
+    if t.shape[dim] == 1:
+        n = 1
+        for d in range(dim + 1, t.dim()):
+            n *= t.shape[d]
+        return n
+    return t.stride(dim)
+
+
 def _stream(stream=None):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -136,9 +148,7 @@ class PagedCache:
         for t, n in ((k_data, "k_data"), (v_data, "v_data"), (k_sf, "k_sf"), (v_sf, "v_sf")):
             if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 4:
                 raise TypeError(f"{n} must be a 4-D uint8 CUDA tensor")
-            inner = t.shape[1:]
-            want = (inner[1] * inner[2], inner[2], 1)
-            if tuple(t.stride()[1:]) != want:
+            if any(_stride(t, d) != want for d, want in ((1, t.shape[2] * t.shape[3]), (2, t.shape[3]), (3, 1))):
                 raise ValueError(f"{n}: each page must be compact (strides {t.stride()})")
         if k_data.shape != v_data.shape or k_sf.shape != v_sf.shape or k_data.shape[:3] != k_sf.shape[:3]:
             raise ValueError("K/V data and scale shapes disagree")
@@ -153,7 +163,7 @@ class PagedCache:
         self.tensors = (k_data, v_data, k_sf, v_sf)
         self.num_pages = min(k_data.shape[0], v_data.shape[0])
         self.desc = PagedCacheDesc(k_data.data_ptr(), v_data.data_ptr(), k_sf.data_ptr(), v_sf.data_ptr(),
-                                   k_data.stride(0), v_data.stride(0), k_sf.stride(0), v_sf.stride(0),
+                                   _stride(k_data, 0), _stride(v_data, 0), _stride(k_sf, 0), _stride(v_sf, 0),
                                    self.num_pages, self.page_size, self.num_kv_heads, self.head_dim, layout)
 
 
@@ -205,7 +215,7 @@ def kv_dequantize_paged(cache: PagedCache, block_tables, seq_lens, k_scale, v_sc
     lib = load_library()
     if block_tables.dtype not in (torch.int32, torch.int64) or block_tables.dim() != 2 or not block_tables.is_cuda:
         raise TypeError("block_tables must be a 2-D int32/int64 CUDA tensor")
-    if block_tables.stride(1) != 1:
+    if _stride(block_tables, 1) != 1:
         raise ValueError("block_tables rows must be contiguous")
     _need_i32(seq_lens, "seq_lens")
     for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
@@ -222,7 +232,7 @@ def kv_dequantize_paged(cache: PagedCache, block_tables, seq_lens, k_scale, v_sc
         raise ValueError("block_tables / seq_lens batch size disagrees with the outputs")
     st = lib.kv_dequantize_paged(C.byref(cache.desc), _ptr(block_tables),
                                  KVFP4_I64 if block_tables.dtype == torch.int64 else KVFP4_I32,
-                                 block_tables.stride(0), block_tables.shape[1], _ptr(seq_lens), B,
+                                 _stride(block_tables, 0), block_tables.shape[1], _ptr(seq_lens), B,
                                  _ptr(k_scale), _ptr(v_scale), _ptr(output_k), _ptr(output_v),
                                  _half_enum(output_k.dtype), T, _stream(stream))
     _check(st, "kv_dequantize_paged")
@@ -234,17 +244,17 @@ def kv_materialize_fp8(cache: PagedCache, block_tables, seq_lens, kv_page_indptr
     _need_i32(seq_lens, "seq_lens")
     _need_i32(kv_page_indptr, "kv_page_indptr")
     _need_i32(fp8_block_tables, "fp8_block_tables")
-    if block_tables.dtype != torch.int32 or not block_tables.is_cuda or block_tables.stride(-1) != 1:
+    if block_tables.dtype != torch.int32 or not block_tables.is_cuda or _stride(block_tables, block_tables.dim() - 1) != 1:
         raise TypeError("block_tables must be an int32 CUDA tensor with contiguous rows")
     B = seq_lens.numel()
     if uses_shared_paged_kv_idx:
         if block_tables.dim() != 2:
             raise ValueError("shared block_tables are [batch, max_num_pages]")
-        cols, row, kvs = block_tables.shape[1], block_tables.stride(0), 0
+        cols, row, kvs = block_tables.shape[1], _stride(block_tables, 0), 0
     else:
         if block_tables.dim() != 3 or block_tables.shape[1] != 2:
             raise ValueError("separate block_tables are [batch, 2, max_num_pages]")
-        cols, row, kvs = block_tables.shape[2], block_tables.stride(0), block_tables.stride(1)
+        cols, row, kvs = block_tables.shape[2], _stride(block_tables, 0), _stride(block_tables, 1)
     if block_tables.shape[0] != B or kv_page_indptr.numel() != B + 1 or fp8_block_tables.shape[0] != B:
         raise ValueError("batch sizes disagree")
     if out.dim() != 5 or out.shape[1:] != (2, cache.num_kv_heads, cache.page_size, cache.head_dim):

@@ -33,8 +33,8 @@ CacheArg = Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]
 @dataclass(frozen=True)
 class NVFP44Over6Config:
     """4over6 block-scale recipe: e4m3_max (256 by default), err_mode "MSE"
-    or "MAE". ``err_use_fast_math=True`` (fp16 error evaluation, a distinct
-    recipe on the page) is rejected by the library."""
+    or "MAE". ``err_use_fast_math=True`` evaluates the candidates' error in
+    fp16 (a distinct recipe on the page: near-ties can go the other way)."""
     e4m3_max: float = 256.0
     err_mode: str = "MSE"
     err_use_fast_math: bool = False

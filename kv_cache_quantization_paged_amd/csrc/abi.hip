@@ -64,8 +64,6 @@ kvfp4_status_t check_recipe(const kvfp4_recipe_t *recipe)
         return KVFP4_EINVAL;
     if (recipe->err_mode != KVFP4_ERR_MSE && recipe->err_mode != KVFP4_ERR_MAE)
         return KVFP4_EINVAL;
-    if (recipe->err_use_fast_math != 0)
-        return KVFP4_EUNSUPPORTED;
     return KVFP4_OK;
 }
 
@@ -255,7 +253,7 @@ const char *kvfp4_status_string(kvfp4_status_t status)
     case KVFP4_OK: return "ok";
     case KVFP4_EINVAL: return "invalid argument (null pointer, enum, extent, stride or scale)";
     case KVFP4_EALIGN: return "misaligned pointer or stride (16-byte alignment required)";
-    case KVFP4_EUNSUPPORTED: return "unsupported request (fp16 4over6 error evaluation is not implemented)";
+    case KVFP4_EUNSUPPORTED: return "unsupported request (sizes beyond the library's 32-bit index limits)";
     case KVFP4_ELAUNCH: return "HIP kernel launch failed (is the device gfx950?)";
     default: return "unknown status";
     }

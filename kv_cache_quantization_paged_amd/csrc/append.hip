@@ -125,11 +125,13 @@ hipError_t launch2(bool hnd, const AppendArgs &a, int grid, hipStream_t st)
 template <bool BF16>
 hipError_t launch1(int recipe, bool hnd, const AppendArgs &a, int grid, hipStream_t st)
 {
-    if (recipe == 1)
-        return launch2<BF16, 1>(hnd, a, grid, st);
-    if (recipe == 2)
-        return launch2<BF16, 2>(hnd, a, grid, st);
-    return launch2<BF16, 0>(hnd, a, grid, st);
+    switch (recipe) {
+    case 1: return launch2<BF16, 1>(hnd, a, grid, st);
+    case 2: return launch2<BF16, 2>(hnd, a, grid, st);
+    case 3: return launch2<BF16, 3>(hnd, a, grid, st);
+    case 4: return launch2<BF16, 4>(hnd, a, grid, st);
+    default: return launch2<BF16, 0>(hnd, a, grid, st);
+    }
 }
 
 }  // namespace
@@ -175,7 +177,7 @@ hipError_t launch_quantize_append(const kvfp4_paged_cache_t &c, const void *key,
     const int64_t cap = recipe == nullptr ? ((int64_t)1 << 24) : kPersistentWorkgroups;
     const int grid = (int)(wgs < cap ? wgs : cap);
     const bool hnd = c.layout == KVFP4_HND;
-    const int rk = recipe == nullptr ? 0 : (recipe->err_mode == KVFP4_ERR_MSE ? 1 : 2);
+    const int rk = recipe_kind(recipe);
     return in_bf16 ? launch1<true>(rk, hnd, a, grid, st) : launch1<false>(rk, hnd, a, grid, st);
 }
 

@@ -111,12 +111,13 @@ template <bool BF16>
 void launch_bq_recipe(int rk, int nt, bool v_ilv, const BlockQuantArgs &a, const float *g0, const float *g1,
                       int grid, hipStream_t st)
 {
-    if (rk == 1)
-        launch_bq<BF16, 1>(nt, v_ilv, a, g0, g1, grid, st);
-    else if (rk == 2)
-        launch_bq<BF16, 2>(nt, v_ilv, a, g0, g1, grid, st);
-    else
-        launch_bq<BF16, 0>(nt, v_ilv, a, g0, g1, grid, st);
+    switch (rk) {
+    case 1: launch_bq<BF16, 1>(nt, v_ilv, a, g0, g1, grid, st); break;
+    case 2: launch_bq<BF16, 2>(nt, v_ilv, a, g0, g1, grid, st); break;
+    case 3: launch_bq<BF16, 3>(nt, v_ilv, a, g0, g1, grid, st); break;
+    case 4: launch_bq<BF16, 4>(nt, v_ilv, a, g0, g1, grid, st); break;
+    default: launch_bq<BF16, 0>(nt, v_ilv, a, g0, g1, grid, st); break;
+    }
 }
 
 hipError_t run_block_quant(bool bf16, const kvfp4_recipe_t *recipe, int nt, bool v_ilv, const BlockQuantArgs &a,
@@ -125,7 +126,7 @@ hipError_t run_block_quant(bool bf16, const kvfp4_recipe_t *recipe, int nt, bool
     if (a.n_blocks == 0)
         return hipSuccess;
     const int grid = (int)(((int64_t)a.n_blocks + kThreads - 1) / kThreads);
-    const int rk = recipe == nullptr ? 0 : (recipe->err_mode == KVFP4_ERR_MSE ? 1 : 2);
+    const int rk = recipe_kind(recipe);
     if (bf16)
         launch_bq_recipe<true>(rk, nt, v_ilv, a, g0, g1, grid, st);
     else

@@ -15,6 +15,7 @@
 // the 127 finite non-negative scale bytes (in LDS) and pass the table.
 #pragma once
 
+#include "../../include/kvfp4.h"
 #include "nvfp4_device.h"
 
 namespace kvfp4 {
@@ -77,8 +78,72 @@ __device__ __forceinline__ float block_error(const float x[16], uint2 codes, flo
     return t[0] + t[1];
 }
 
-// RECIPE: 0 standard, 1 4over6 MSE, 2 4over6 MAE. x holds the block, amax
-// its largest magnitude; returns the packed codes and sets the scale byte.
+// fp32 value -> nearest fp16 value (ties to even), back in fp32 (exact)
+__device__ __forceinline__ float round_f16(float v) { return (float)(_Float16)v; }
+
+// the same error in IEEE fp16 ("err_use_fast_math"): the input and the fp32
+// reconstruction are rounded to fp16, then the difference, the square and
+// every sum of the tree are fp16 operations (each rounds to nearest-even,
+// overflowing to inf). Each fp16 operation is done in fp32 and rounded once
+// to fp16: fp32 carries 24 >= 2 * 11 + 2 significant bits, so for +, - and *
+// that double rounding gives exactly the correctly rounded fp16 result.
+// the input in fp16, as pairs xh[j] = (x_j, x_{j+8}): this pairing puts
+// every level of the index-order tree except the last in packed fp16 adds
+// (the empty asm pins the converted pairs, so that the subtraction below
+// cannot be folded back into the conversions: that rewrite trips an
+// instruction-selection failure when packed fp32 instructions are disabled)
+__device__ __forceinline__ void inputs_fp16(const float x[16], f16x2 xh[8])
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x[j], x[j + 8]}, f16x2));
+        asm volatile("" : "+v"(b));
+        xh[j] = __builtin_bit_cast(f16x2, b);
+    }
+}
+
+// the same error in IEEE fp16 ("err_use_fast_math"): the input and the fp32
+// reconstruction are rounded to fp16, then the difference, the square and
+// every sum of the tree are fp16 operations, each rounding to nearest-even
+// (overflow gives inf). Lane pairs (j, j+8) go through packed fp16 math:
+// V_j = (d_j, d_{j+8}), then V_{2k} + V_{2k+1} = (p_k, p_{k+4}) are the
+// first-level sums, (q_m, q_{m+2}) the second, (r_0, r_1) the third.
+template <bool MSE>
+__device__ __forceinline__ float block_error_fp16(const f16x2 xh[8], uint2 codes, float dec)
+{
+    f16x2 t[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f32x2 lo = k == 0 ? fp4x2_to_f32x2<0>(codes.x) : k == 1 ? fp4x2_to_f32x2<1>(codes.x)
+                       : k == 2 ? fp4x2_to_f32x2<2>(codes.x) : fp4x2_to_f32x2<3>(codes.x);
+        const f32x2 hi = k == 0 ? fp4x2_to_f32x2<0>(codes.y) : k == 1 ? fp4x2_to_f32x2<1>(codes.y)
+                       : k == 2 ? fp4x2_to_f32x2<2>(codes.y) : fp4x2_to_f32x2<3>(codes.y);
+        // elements 2k, 2k+1 (lo) and 2k+8, 2k+9 (hi). The fp32 reconstruction
+        // is rounded to fp32 first: the empty asm keeps the compiler from
+        // fusing multiply and conversion into one v_fma_mix, whose single
+        // rounding of the exact product to fp16 differs from rounding the
+        // fp32 product (a 26-bit value).
+        float r0 = dec * lo.x, r1 = dec * lo.y, r8 = dec * hi.x, r9 = dec * hi.y;
+        asm volatile("" : "+v"(r0), "+v"(r1), "+v"(r8), "+v"(r9));
+        const f16x2 ra = __builtin_convertvector((f32x2){r0, r8}, f16x2);
+        const f16x2 rb = __builtin_convertvector((f32x2){r1, r9}, f16x2);
+        // reconstruction minus input: the negated difference, same square and |d|
+        const f16x2 da = ra - xh[2 * k], db = rb - xh[2 * k + 1];
+        t[2 * k] = MSE ? da * da : __builtin_elementwise_abs(da);
+        t[2 * k + 1] = MSE ? db * db : __builtin_elementwise_abs(db);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = t[2 * k] + t[2 * k + 1];       // (p_k, p_{k+4})
+    t[0] = t[0] + t[1];                                                // (q_0, q_2)
+    t[1] = t[2] + t[3];                                                // (q_1, q_3)
+    t[0] = t[0] + t[1];                                                // (r_0, r_1)
+    const _Float16 e = t[0].x + t[0].y;
+    return (float)e;
+}
+
+// RECIPE: 0 standard, 1 4over6 MSE, 2 4over6 MAE, 3 MSE in fp16, 4 MAE in
+// fp16. x holds the block, amax its largest magnitude; returns the packed
+// codes and sets the scale byte.
 template <int RECIPE>
 __device__ __forceinline__ uint2 quantize_block(const float x[16], float amax, float g, float clamp6,
                                                 const float *dec_tab, const float *inv_tab, uint32_t &s_out)
@@ -92,15 +157,33 @@ __device__ __forceinline__ uint2 quantize_block(const float x[16], float amax, f
         const uint32_t s4 = f32_to_e4m3_hw(fminf(sf4, 448.0f));
         const float dec4 = dec_tab[s4];
         const uint2 codes4 = encode16(x, inv_tab[s4]);
-        const float e6 = block_error<RECIPE == 1>(x, codes, dec);
-        const float e4 = block_error<RECIPE == 1>(x, codes4, dec4);
-        if (e4 < e6) {
+        constexpr bool kMse = RECIPE == 1 || RECIPE == 3;
+        float e6, e4;
+        if (RECIPE >= 3) {
+            f16x2 xh[8];
+            inputs_fp16(x, xh);
+            e6 = block_error_fp16<kMse>(xh, codes, dec);
+            e4 = block_error_fp16<kMse>(xh, codes4, dec4);
+        } else {
+            e6 = block_error<kMse>(x, codes, dec);
+            e4 = block_error<kMse>(x, codes4, dec4);
+        }
+        if (e4 < e6) {                     // an inf or NaN error never wins
             s = s4;
             codes = codes4;
         }
     }
     s_out = s;
     return codes;
+}
+
+// kernel recipe index of a (checked) recipe: 0 standard, 1/2 MSE/MAE in
+// fp32, 3/4 MSE/MAE in fp16
+inline int recipe_kind(const kvfp4_recipe_t *recipe)
+{
+    if (recipe == nullptr)
+        return 0;
+    return (recipe->err_mode == KVFP4_ERR_MSE ? 1 : 2) + (recipe->err_use_fast_math ? 2 : 0);
 }
 
 }  // namespace kvfp4

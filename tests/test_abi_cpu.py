@@ -78,8 +78,6 @@ def test_append_rejects_bad_arguments(B):
     assert _append(B, _cache(B), recipe=C.byref(bad)) == B.KVFP4_EINVAL
     bad = B.RecipeDesc(256.0, 5, 0)
     assert _append(B, _cache(B), recipe=C.byref(bad)) == B.KVFP4_EINVAL
-    fm = B.RecipeDesc(256.0, 0, 1)
-    assert _append(B, _cache(B), recipe=C.byref(fm)) == B.KVFP4_EUNSUPPORTED
     # nnz == 0 is a no-op that launches nothing, even with null row pointers
     assert _append(B, _cache(B), nnz=0, key=None, value=None, bi=None) == B.KVFP4_OK
 
@@ -151,8 +149,8 @@ def test_contiguous_codec_rejects_bad_arguments(B):
     assert q(rows=1 << 40, cols=1 << 10) == B.KVFP4_EUNSUPPORTED                 # more than 2^31 blocks
     bad = B.RecipeDesc(300.0, 0, 0)
     assert q(recipe=C.byref(bad)) == B.KVFP4_EINVAL
-    fast = B.RecipeDesc(256.0, 0, 1)
-    assert q(recipe=C.byref(fast)) == B.KVFP4_EUNSUPPORTED
+    bad_fast = B.RecipeDesc(256.0, 7, 1)
+    assert q(recipe=C.byref(bad_fast)) == B.KVFP4_EINVAL
     assert dq(dt=3) == B.KVFP4_EINVAL
     assert dq(cols=24) == B.KVFP4_EINVAL
     assert dq(rows=0, d=None, s=None, g=None, out=None) == B.KVFP4_OK
@@ -175,8 +173,8 @@ def test_pool_quantizer_rejects_bad_arguments(B):
     assert call(_cache(B, **hnd), vs=None) == B.KVFP4_EINVAL
     assert call(_cache(B, **hnd), v=P(8200)) == B.KVFP4_EALIGN
     assert call(_cache(B, k_page_stride=100), inter=0) == B.KVFP4_EINVAL       # stride below a compact page
-    fast = B.RecipeDesc(256.0, 1, 1)
-    assert call(_cache(B, **hnd), recipe=C.byref(fast)) == B.KVFP4_EUNSUPPORTED
+    bad_fast = B.RecipeDesc(300.0, 1, 1)
+    assert call(_cache(B, **hnd), recipe=C.byref(bad_fast)) == B.KVFP4_EINVAL
 
 
 def test_package_refuses_to_run_without_library(tmp_path, monkeypatch):

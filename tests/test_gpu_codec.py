@@ -29,7 +29,9 @@ def say(*a):
 def recipes(K, orc):
     return {"standard": (None, orc.STANDARD, 448.0),
             "mse": (K.Recipe(256.0, K.KVFP4_ERR_MSE), orc.four_over_six(orc.MSE), 256.0),
-            "mae": (K.Recipe(256.0, K.KVFP4_ERR_MAE), orc.four_over_six(orc.MAE), 256.0)}
+            "mae": (K.Recipe(256.0, K.KVFP4_ERR_MAE), orc.four_over_six(orc.MAE), 256.0),
+            "mse16": (K.Recipe(256.0, K.KVFP4_ERR_MSE, True), orc.four_over_six(orc.MSE, fast_math=True), 256.0),
+            "mae16": (K.Recipe(256.0, K.KVFP4_ERR_MAE, True), orc.four_over_six(orc.MAE, fast_math=True), 256.0)}
 
 
 def values(rng, shape, kind):
@@ -49,7 +51,7 @@ def g_dev(g):
 
 
 @pytest.mark.parametrize("shape", [(1, 16), (3, 48), (257, 128), (5, 7, 256), (2049, 1024)])
-@pytest.mark.parametrize("recipe", ["standard", "mse", "mae"])
+@pytest.mark.parametrize("recipe", ["standard", "mse", "mae", "mse16", "mae16"])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_contiguous_quantize_parity(K, orc, shape, recipe, bf16):
     rng = np.random.default_rng(zlib.crc32(repr((shape, recipe, bf16)).encode()))
@@ -117,7 +119,7 @@ def pool_case(rng, layout, ps, H, D, P, bf16, kind, pad):
     (W.NHD, 16, 8, 128, 11, False, 32),
     (W.NHD, 5, 3, 16, 7, False, 8),
 ])
-@pytest.mark.parametrize("recipe", ["standard", "mse"])
+@pytest.mark.parametrize("recipe", ["standard", "mse", "mae16"])
 def test_pool_quantizer_parity(K, orc, layout, ps, H, D, P, inter, pad, recipe):
     rng = np.random.default_rng(ps * 131 + H * 7 + D + P + pad + (recipe == "mse"))
     say(f"pool quantize layout={layout} ps={ps} H={H} D={D} P={P} interleaved={inter} pad={pad} {recipe}")
@@ -158,3 +160,19 @@ def test_pool_quantizer_then_materialize(K, orc):
     orc.materialize_fp8(cache, bt, lens, indptr, want, wtab, shared=True, v_sf_interleaved=True)
     assert np.array_equal(out.view(torch.uint8).cpu().numpy(), want)
     assert np.array_equal(tab.cpu().numpy(), wtab)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_contiguous_dequant_rounds_the_fp32_product(K, orc, bf16):
+    from test_gpu_parity import double_rounding_scales
+    rng = np.random.default_rng(4343 + bf16)
+    s_all = np.arange(0x00, 0x7F, dtype=np.uint8)
+    codes = np.arange(16, dtype=np.uint8)
+    packed = np.tile(codes[0::2] | (codes[1::2] << 4), (len(s_all), 1)).astype(np.uint8)
+    sc = s_all[:, None].copy()
+    dt = torch.bfloat16 if bf16 else torch.float16
+    for g in double_rounding_scales(rng, bf16):
+        out = torch.empty((len(s_all), 16), dtype=dt, device="cuda")
+        K.kv_dequantize(torch.from_numpy(packed).cuda(), torch.from_numpy(sc).cuda(), g_dev(g), out)
+        want = orc.dequantize_contiguous(packed, sc, g, bf16)
+        assert np.array_equal(tensor_bits(out), want), g

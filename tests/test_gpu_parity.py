@@ -99,15 +99,18 @@ def run_append_both(K, orc, seed, layout, ps, H, D, in_bf16, recipe_o, recipe_k,
 
 
 def recipes(K, orc, name):
+    """standard, mse, mae, and mse16 / mae16 (the error evaluated in fp16)"""
     if name == "standard":
         return orc.STANDARD, None
-    mode = orc.MSE if name == "mse" else orc.MAE
-    return orc.four_over_six(mode), K.Recipe(256.0, K.KVFP4_ERR_MSE if mode == orc.MSE else K.KVFP4_ERR_MAE)
+    mode = orc.MSE if name.startswith("mse") else orc.MAE
+    fast = name.endswith("16")
+    return (orc.four_over_six(mode, fast_math=fast),
+            K.Recipe(256.0, K.KVFP4_ERR_MSE if mode == orc.MSE else K.KVFP4_ERR_MAE, err_use_fast_math=fast))
 
 
 # --------------------------------------------------------------------------- append
 @pytest.mark.parametrize("layout", [W.NHD, W.HND])
-@pytest.mark.parametrize("recipe", ["standard", "mse", "mae"])
+@pytest.mark.parametrize("recipe", ["standard", "mse", "mae", "mse16", "mae16"])
 @pytest.mark.parametrize("in_bf16", [True, False])
 def test_append_parity(K, orc, layout, recipe, in_bf16):
     ro, rk = recipes(K, orc, recipe)
@@ -123,7 +126,7 @@ def test_append_geometries(K, orc, geom, recipe):
 
 
 @pytest.mark.parametrize("kind", ["special", "normal"])
-@pytest.mark.parametrize("recipe", ["standard", "mse", "mae"])
+@pytest.mark.parametrize("recipe", ["standard", "mse", "mae", "mse16", "mae16"])
 def test_append_special_values_and_clamp(K, orc, kind, recipe):
     ro, rk = recipes(K, orc, recipe)
     # scale_mult < 1 pushes block scales past the clamps (mismatched global scale)
@@ -335,7 +338,7 @@ def test_global_scale_parity(K, orc, n, is_bf16, emax):
 
 
 @pytest.mark.parametrize("in_bf16", [True, False])
-@pytest.mark.parametrize("recipe", ["standard", "mse", "mae"])
+@pytest.mark.parametrize("recipe", ["standard", "mse", "mae", "mse16", "mae16"])
 def test_append_encoder_sweeps_every_16bit_value(K, orc, in_bf16, recipe):
     """Every bf16 / fp16 value in [-6, 6] passes through the E2M1 encoder
     with a unit decode factor (g = 1 and a block amax of 6 give s = 1.0), so
@@ -371,3 +374,63 @@ def test_append_encoder_sweeps_every_16bit_value(K, orc, in_bf16, recipe):
     got = dev.to_host()
     for a, b in zip((got.k_data, got.v_data, got.k_sf, got.v_sf), (host.k_data, host.v_data, host.k_sf, host.v_sf)):
         assert np.array_equal(a, b), first_mismatch(a, b)
+
+
+def double_rounding_scales(rng, is_bf16, want=12):
+    """Global scales g for which some product fp32(E4M3(s) * g) * e2m1 has an
+    exact value whose direct rounding to 16 bits differs from rounding its
+    fp32 rounding: the definition rounds twice, a fused multiply-convert
+    (one rounding of the exact product) would not."""
+    from test_oracle_ops import E4M3_TORCH
+    S = E4M3_TORCH[0x08:0x7F].astype(np.float32)
+    E = np.array([0.5, 1.5, 3.0, 6.0], np.float32)
+    bits = 8 if is_bf16 else 11                       # significant bits (normal range)
+
+    def rne(p):
+        """nearest value with `bits` significant bits, ties to even (the
+        normal range of the 16-bit type is all these products reach)"""
+        e = np.floor(np.log2(np.abs(p)))
+        ulp = np.exp2(e - (bits - 1))
+        return np.rint(p / ulp) * ulp                 # exact scaling; rint is ties-to-even
+
+    found = []
+    while len(found) < want:
+        g = np.float32(np.exp(rng.uniform(-9, 2)))
+        dec = (S * g).astype(np.float32)
+        p = dec.astype(np.float64)[:, None] * E.astype(np.float64)[None, :]        # exact
+        if np.any(rne(p.astype(np.float32).astype(np.float64)) != rne(p)):
+            found.append(float(g))
+    return found
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_dequant_rounds_the_fp32_product(K, orc, bf16):
+    """Near-midpoint products: the device output must round the fp32 product
+    (as the definition does), not the exact one."""
+    rng = np.random.default_rng(4242 + bf16)
+    gs = double_rounding_scales(rng, bf16)
+    ps, H, D = 16, 1, 128
+    s_all = np.arange(0x00, 0x7F, dtype=np.uint8)
+    n_tok = len(s_all) * 2
+    pages = (n_tok + ps - 1) // ps
+    cache = W.make_cache(rng, pages, ps, H, D, W.NHD, fill="zero")
+    codes = np.arange(16, dtype=np.uint8)
+    row = np.tile(codes[0::2] | (codes[1::2] << 4), D // 16)
+    for a in (cache.k_data, cache.v_data):
+        a[...] = np.tile(row, (pages, ps))
+    for a in (cache.k_sf, cache.v_sf):
+        a[...] = np.resize(np.repeat(s_all, D // 16), a.size).reshape(a.shape)
+    bt = np.arange(pages, dtype=np.int32)[None, :]
+    lens = np.array([pages * ps], np.int32)
+    dev = DeviceCache(cache)
+    dt = torch.bfloat16 if bf16 else torch.float16
+    for g in gs:
+        ok = torch.empty((1, pages * ps, H, D), dtype=dt, device="cuda")
+        ov = torch.empty_like(ok)
+        K.kv_dequantize_paged(dev.cache, i32(bt), i32(lens), torch.tensor([g], device="cuda"),
+                              torch.tensor([g], device="cuda"), ok, ov)
+        wk = np.zeros((1, pages * ps, H, D), np.uint16)
+        wv = wk.copy()
+        orc.dequantize_paged(cache, bt, lens, g, g, wk, wv, bf16)
+        got = tensor_bits(ok)
+        assert np.array_equal(got, wk), (g, first_mismatch(got, wk))
