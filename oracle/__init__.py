@@ -108,6 +108,9 @@ def _load():
     lib.orc_quantize_paged_cache.restype = C.c_int
     lib.orc_quantize_paged_cache.argtypes = [C.POINTER(_Cache), P, P, C.c_int, f32, f32, C.POINTER(_Recipe),
                                              C.c_int, C.c_int]
+    lib.orc_decode_attention.restype = C.c_int
+    lib.orc_decode_attention.argtypes = [C.POINTER(_Cache), P, C.c_int, i32, P, i64, i32, P, i32, f32, f32, f32, P,
+                                         C.c_int]
     _lib = lib
     return lib
 
@@ -326,3 +329,23 @@ def quantize_paged_cache(cache, k_in_bits, v_in_bits, in_is_bf16, k_scale, v_sca
                                           int(threads))
     if rc != 0:
         raise ValueError(f"oracle quantize_paged_cache rejected its arguments ({rc})")
+
+
+def decode_attention(cache, q_bits, q_is_bf16, block_tables, seq_lens, k_scale, v_scale, sm_scale,
+                     threads: int = 1) -> np.ndarray:
+    """R13: q [B, Hq, D] fp16/bf16 bits -> float64 [B, Hq, D]."""
+    cs = _cache_struct(cache.k_data, cache.v_data, cache.k_sf, cache.v_sf, cache.page_size,
+                       cache.num_heads, cache.head_dim, cache.layout)
+    q = _need(np.asarray(q_bits), np.uint16, "q")
+    bt = _need(np.asarray(block_tables), np.int32, "block_tables")
+    sl = _need(np.asarray(seq_lens), np.int32, "seq_lens")
+    B, Hq, D = q.shape
+    if D != cache.head_dim or bt.shape[0] != B or sl.shape[0] != B:
+        raise ValueError("shapes disagree")
+    out = np.zeros((B, Hq, D), np.float64)
+    rc = _load().orc_decode_attention(C.byref(cs), _ptr(q), int(bool(q_is_bf16)), Hq, _ptr(bt), bt.shape[1],
+                                      bt.shape[1], _ptr(sl), B, float(k_scale), float(v_scale), float(sm_scale),
+                                      _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle decode_attention rejected its arguments ({rc})")
+    return out

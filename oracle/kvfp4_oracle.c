@@ -67,6 +67,13 @@
  *       R1-R5, K scales linear, V scales in the R9 interleave, which is the
  *       layout [MF] says this function produces.
  *
+ *   R13 decode attention over the NVFP4 cache [DQ: "consumed by the NVFP4
+ *       attention kernels", values e2m1 * block_scale * global_scale]:
+ *       scaled dot-product attention of one query token per request over
+ *       the exact dequantized K and V (no 16-bit rounding, as a fused
+ *       consumer has none), grouped-query heads hq -> hq / (Hq / H); an
+ *       empty request gives zeros.
+ *
  * [KV] flashinfer.quantization module page, "FP4 KV Cache Quantization"
  *      (nvfp4_kv_quantize, nvfp4_kv_dequantize, nvfp4_quantize_paged_kv_cache).
  */
@@ -897,5 +904,106 @@ int orc_quantize_paged_cache(const orc_cache_t *cache, const uint16_t *k_in, con
             return -3;
     struct pool_ctx ctx = {cache, k_in, v_in, in_is_bf16, k_scale, v_scale, recipe, v_sf_interleaved};
     parallel_for(cache->num_pages, threads, quantize_pages, &ctx);
+    return 0;
+}
+
+/* ======================================================================== */
+/* decode attention over the paged cache, R13                               */
+/* ======================================================================== */
+struct attn_ctx {
+    const orc_cache_t *c;
+    const uint16_t *q;
+    int bf16;
+    int64_t hq;
+    const int32_t *bt;
+    int64_t bt_row_stride;
+    const int32_t *seq_lens;
+    double gk, gv, sm;
+    double *out;
+};
+
+/* exact dequantized value of element e of (page, slot, h) */
+static double cache_value(const orc_cache_t *c, int kv, int64_t page, int64_t slot, int64_t h, int64_t e, double g)
+{
+    const int64_t D = c->head_dim;
+    const uint8_t *data = (kv ? c->v_data : c->k_data) + page * (kv ? c->v_page_stride : c->k_page_stride);
+    const uint8_t *sf = (kv ? c->v_sf : c->k_sf) + page * (kv ? c->v_sf_page_stride : c->k_sf_page_stride);
+    int64_t row = page_row(c, slot, h);
+    uint8_t byte = data[row * (D / 2) + e / 2];
+    int code = (e & 1) ? (byte >> 4) : (byte & 15);
+    return orc_e2m1_value(code) * orc_e4m3_value(sf[row * (D / 16) + e / 16]) * g;
+}
+
+static void attention_requests(void *vctx, int64_t lo, int64_t hi)
+{
+    const struct attn_ctx *a = (const struct attn_ctx *)vctx;
+    const orc_cache_t *c = a->c;
+    const int64_t H = c->num_heads, D = c->head_dim, ps = c->page_size, group = a->hq / H;
+    for (int64_t b = lo; b < hi; b++) {
+        int64_t len = a->seq_lens[b];
+        double *s = (double *)malloc(sizeof(double) * (size_t)(len > 0 ? len : 1));
+        for (int64_t qh = 0; qh < a->hq; qh++) {
+            int64_t h = qh / group;
+            const uint16_t *qv = a->q + (b * a->hq + qh) * D;
+            double *o = a->out + (b * a->hq + qh) * D;
+            for (int64_t e = 0; e < D; e++)
+                o[e] = 0.0;
+            if (len <= 0)
+                continue;
+            double m = -INFINITY;
+            for (int64_t t = 0; t < len; t++) {
+                int64_t page = a->bt[b * a->bt_row_stride + t / ps];
+                double dot = 0.0;
+                for (int64_t e = 0; e < D; e++)
+                    dot += orc_half_value(qv[e], a->bf16) * cache_value(c, 0, page, t % ps, h, e, a->gk);
+                s[t] = a->sm * dot;
+                if (s[t] > m)
+                    m = s[t];
+            }
+            double denom = 0.0;
+            for (int64_t t = 0; t < len; t++) {
+                s[t] = exp(s[t] - m);
+                denom += s[t];
+            }
+            for (int64_t t = 0; t < len; t++) {
+                int64_t page = a->bt[b * a->bt_row_stride + t / ps];
+                double p = s[t] / denom;
+                for (int64_t e = 0; e < D; e++)
+                    o[e] += p * cache_value(c, 1, page, t % ps, h, e, a->gv);
+            }
+        }
+        free(s);
+    }
+}
+
+int orc_decode_attention(const orc_cache_t *cache, const uint16_t *q, int q_is_bf16, int32_t num_qo_heads,
+                         const int32_t *block_tables, int64_t bt_row_stride, int32_t bt_cols,
+                         const int32_t *seq_lens, int32_t batch_size, float k_scale, float v_scale,
+                         float sm_scale, double *out, int threads)
+{
+    if (!cache_ok(cache) || batch_size < 0 || num_qo_heads <= 0 || num_qo_heads % cache->num_heads != 0)
+        return -1;
+    if (batch_size == 0)
+        return 0;
+    if (!q || !block_tables || !seq_lens || !out || bt_row_stride < bt_cols)
+        return -1;
+    if (!isfinite(k_scale) || !isfinite(v_scale) || !isfinite(sm_scale))
+        return -2;
+    const int64_t ps = cache->page_size;
+    for (int64_t b = 0; b < batch_size; b++) {
+        if (seq_lens[b] < 0)
+            return -4;
+        int64_t pages = (seq_lens[b] + ps - 1) / ps;
+        if (pages > bt_cols)
+            return -4;
+        for (int64_t j = 0; j < pages; j++) {
+            int64_t page = block_tables[b * bt_row_stride + j];
+            if (page < 0 || page >= cache->num_pages)
+                return -4;
+        }
+    }
+    struct attn_ctx ctx = {cache, q, q_is_bf16, num_qo_heads, block_tables, bt_row_stride, seq_lens,
+                           (double)k_scale, (double)v_scale, (double)sm_scale, out};
+    parallel_for(batch_size, threads, attention_requests, &ctx);
     return 0;
 }

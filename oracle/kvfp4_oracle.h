@@ -106,6 +106,18 @@ int orc_quantize_paged_cache(const orc_cache_t *cache, const uint16_t *k_in, con
                              int in_is_bf16, float k_scale, float v_scale, const orc_recipe_t *recipe,
                              int v_sf_interleaved, int threads);
 
+/* ---- decode attention over the paged NVFP4 cache ------------------------ */
+/* One query token per request: for query head hq (kv head hq / (Hq / H)),
+ *   s_t = sm_scale * sum_e q[b, hq, e] * K[b, t, e],  t < seq_lens[b]
+ *   out[b, hq, :] = sum_t softmax(s)_t * V[b, t, :]
+ * with K, V the exact dequantized values e2m1 * E4M3(s) * g (no rounding).
+ * q is [B, Hq, D] fp16/bf16 bits; out [B, Hq, D] double. A request of length
+ * 0 gives zeros. Computed in double. */
+int orc_decode_attention(const orc_cache_t *cache, const uint16_t *q, int q_is_bf16, int32_t num_qo_heads,
+                         const int32_t *block_tables, int64_t bt_row_stride, int32_t bt_cols,
+                         const int32_t *seq_lens, int32_t batch_size, float k_scale, float v_scale,
+                         float sm_scale, double *out, int threads);
+
 #ifdef __cplusplus
 }
 #endif
