@@ -371,6 +371,48 @@ def leg_pool_quantize(env, iters, warmup):
     return res
 
 
+def attention_bytes(lens, ps, H, D, Hq):
+    """K and V codes and scales of every valid (token, kv head), q in and out
+    (bf16), the block-table entries used and seq_lens"""
+    tokens = int(np.sum(lens))
+    pages = int(np.sum((np.asarray(lens) + ps - 1) // ps))
+    B = len(lens)
+    return 2 * tokens * H * (D // 2 + D // 16) + 2 * B * Hq * D * 2 + 4 * pages + 4 * B
+
+
+def leg_attention(env, iters, warmup, G=4):
+    """kv_decode_attention on the decode workload's cache (64 requests,
+    124,503 tokens, page 16, 8 kv heads x 4 query heads, NHD, bf16), and on
+    an HND pool with the same lengths and pages."""
+    torch, K = env.torch, env.K
+    reps = [Decode(env) for _ in range(replicas_for(144_000_000))]
+    r0 = reps[0]
+    Hq = r0.H * G
+    sm = 1.0 / float(np.sqrt(r0.D))
+    nb = attention_bytes(r0.lens, r0.ps, r0.H, r0.D, Hq)
+    res = {"workload": "decode attention: the decode workload's cache (64 requests, 124,503 tokens, page_size 16, "
+                       "8 kv heads, head_dim 128), 4 query heads per kv head, bf16 q/out, sm_scale 1/sqrt(128)"}
+    fns = []
+    for i, r in enumerate(reps):
+        g = env.gen(5000 + i)
+        r.q = torch.randn((r.B, Hq, r.D), generator=g, device=env.dev).to(torch.bfloat16)
+        r.att_out = torch.empty_like(r.q)
+        r.ws = torch.empty(K.kv_decode_attention_workspace_size(r.B, r.H, Hq, r.bt.shape[1], r.ps), dtype=torch.uint8,
+                           device=env.dev)
+        fns.append(lambda r=r: K.kv_decode_attention(r.cache, r.q, r.bt, r.seq_lens, r.gk_t, r.gv_t, sm, r.att_out,
+                                                     r.ws))
+    res["nhd"] = dict(kernel="kv_decode_attention", bytes=nb, **rates(nb, env.steady(fns, iters, warmup)))
+    fns = []
+    for i, r in enumerate(reps):
+        r.hnd_cache, r.hnd_keep = env.cache(20000, r.ps, r.H, r.D, K.KVFP4_HND, 6000 + i)
+        fns.append(lambda r=r: K.kv_decode_attention(r.hnd_cache, r.q, r.bt, r.seq_lens, r.gk_t, r.gv_t, sm,
+                                                     r.att_out, r.ws))
+    res["hnd"] = dict(kernel="kv_decode_attention", bytes=nb, **rates(nb, env.steady(fns, iters, warmup)))
+    del reps, fns
+    torch.cuda.empty_cache()
+    return res
+
+
 def page_order_replica(env, order, seed):
     """64 full 4096-token requests in decode geometry (page_size 16, 8 heads,
     head_dim 128, NHD, bf16 out); `order` "random" shuffles the 16,384 pages
@@ -547,7 +589,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--leg-iters", type=int, default=50)
-    ap.add_argument("--legs", default="prefill,materialize,four_over_six,contiguous,pool_quantize,page_order,copy",
+    ap.add_argument("--legs", default="prefill,materialize,four_over_six,contiguous,pool_quantize,attention,"
+                                      "page_order,copy",
                     help="comma list of legs to run after the headline step (empty: none)")
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -621,6 +664,8 @@ def main():
     if "pool_quantize" in chosen:
         legs["pool_quantize"] = leg_pool_quantize(env, args.leg_iters, 5)
         torch.cuda.empty_cache()
+    if "attention" in chosen:
+        legs["decode_attention"] = leg_attention(env, args.leg_iters, 5)
     if "page_order" in chosen:
         legs["page_order_context"] = leg_page_order(env, args.leg_iters, 5)
     if "copy" in chosen:

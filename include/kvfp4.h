@@ -11,6 +11,8 @@
  *   kv_dequantize        contiguous NVFP4 with linear scales -> fp16/bf16
  *   kv_quantize_paged_cache  a whole 16-bit page pool -> NVFP4 cache, V
  *                        scales optionally 4-token interleaved
+ *   kv_decode_attention  one-token-per-request attention read straight
+ *                        from the NVFP4 pages
  *
  * Sources (FlashInfer 0.7.4 documentation): the API pages
  * flashinfer.page.nvfp4_quantize_append_paged_kv_cache,
@@ -249,6 +251,42 @@ kvfp4_status_t kv_dequantize(const void *fp4_data, const void *block_scales, int
 kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const void *k_in, const void *v_in,
                                        int32_t in_dtype, const float *k_scale, const float *v_scale,
                                        const kvfp4_recipe_t *recipe, int32_t v_sf_interleaved, void *stream);
+
+/*
+ * kv_decode_attention - the NVFP4 attention consumer of the paged cache
+ * (flashinfer.quantization.nvfp4_kv_dequantize_paged page: k_scale and
+ * v_scale are "the global decode scales consumed by the NVFP4 attention
+ * kernels", values e2m1 * block_scale * global_scale). For each request b
+ * and query head hq (kv head hq / (num_qo_heads / num_kv_heads)):
+ *   out[b, hq, :] = sum_t softmax_t(sm_scale * q[b, hq, :] . K[b, t, h, :]) V[b, t, h, :]
+ * over t < seq_lens[b], K and V decoded from the cache (page
+ * block_tables[b * bt_row_stride + t / page_size], slot t % page_size) times
+ * *k_scale / *v_scale (device fp32). A request of length 0 gives zeros.
+ * q and out are [batch_size, num_qo_heads, 128] of q_dtype (bf16 or fp16),
+ * contiguous, 16-byte aligned; block_tables and seq_lens int32. head_dim
+ * must be 128 and num_qo_heads / num_kv_heads at most 16
+ * (KVFP4_EUNSUPPORTED otherwise); scale bases and scale page strides must be
+ * even. Scores and the softmax are fp32. The products run in fp16: decoded
+ * K and V are exact there; a bf16 query row is scaled by a power of two that
+ * puts its largest magnitude in [2^14, 2^15) and converted (exact except for
+ * components more than 2^38 below that largest one); the probabilities are
+ * rounded to fp16 for the value product; out is rounded once to q_dtype.
+ * The sequence is split into 256-token pieces whose partial softmax results
+ * go to `workspace` (caller-owned device memory, 16-byte aligned, at least
+ * kv_decode_attention_workspace_size(batch_size, num_kv_heads, num_qo_heads,
+ * bt_cols, page_size) bytes, no initial contents needed; it is scratch for the
+ * duration of the call's stream work, so concurrent calls need their own).
+ */
+kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void *q, int32_t q_dtype,
+                                   int32_t num_qo_heads, const int32_t *block_tables, int64_t bt_row_stride,
+                                   int32_t bt_cols, const int32_t *seq_lens, int32_t batch_size,
+                                   const float *k_scale, const float *v_scale, float sm_scale, void *out,
+                                   void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace kv_decode_attention needs for these sizes (-1 for
+ * invalid sizes). */
+int64_t kv_decode_attention_workspace_size(int32_t batch_size, int32_t num_kv_heads, int32_t num_qo_heads,
+                                           int32_t bt_cols, int32_t page_size);
 
 /* Static description of a status code. */
 const char *kvfp4_status_string(kvfp4_status_t status);

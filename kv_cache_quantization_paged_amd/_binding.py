@@ -23,7 +23,8 @@ KVFP4_I32, KVFP4_I64 = 0, 1
 KVFP4_ERR_MSE, KVFP4_ERR_MAE = 0, 1
 
 EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
-            "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kvfp4_status_string")
+            "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
+            "kv_decode_attention_workspace_size", "kvfp4_status_string")
 
 
 class PagedCacheDesc(C.Structure):
@@ -80,6 +81,11 @@ def load_library():
     lib.kv_quantize_paged_cache.restype = i32
     lib.kv_quantize_paged_cache.argtypes = [C.POINTER(PagedCacheDesc), P, P, i32, P, P, C.POINTER(RecipeDesc),
                                             i32, P]
+    lib.kv_decode_attention.restype = i32
+    lib.kv_decode_attention.argtypes = [C.POINTER(PagedCacheDesc), P, i32, i32, P, i64, i32, P, i32, P, P, f32, P, P,
+                                        i64, P]
+    lib.kv_decode_attention_workspace_size.restype = i64
+    lib.kv_decode_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.kvfp4_status_string.restype = C.c_char_p
     lib.kvfp4_status_string.argtypes = [i32]
     _lib = lib
@@ -342,3 +348,36 @@ def kv_quantize_paged_cache(cache: PagedCache, k_in, v_in, k_scale, v_scale, rec
                                      _ptr(k_scale), _ptr(v_scale), C.byref(rd) if rd is not None else None,
                                      int(bool(v_sf_interleaved)), _stream(stream))
     _check(st, "kv_quantize_paged_cache")
+
+
+def kv_decode_attention_workspace_size(batch: int, num_kv_heads: int, num_qo_heads: int, max_pages: int,
+                                       page_size: int) -> int:
+    return int(load_library().kv_decode_attention_workspace_size(batch, num_kv_heads, num_qo_heads, max_pages,
+                                                                 page_size))
+
+
+def kv_decode_attention(cache: PagedCache, q, block_tables, seq_lens, k_scale, v_scale, sm_scale: float, out,
+                        workspace, stream=None):
+    """q, out [batch, num_qo_heads, head_dim] bf16/fp16; block_tables int32
+    [batch, max_pages]; k_scale / v_scale 1-element float32 CUDA tensors;
+    workspace a CUDA byte tensor of kv_decode_attention_workspace_size()."""
+    lib = load_library()
+    _need_i32(seq_lens, "seq_lens")
+    _need_scale(k_scale, "k_scale")
+    _need_scale(v_scale, "v_scale")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_cuda:
+        raise TypeError("block_tables must be a 2-D int32 CUDA tensor")
+    if _stride(block_tables, 1) != 1:
+        raise ValueError("block_tables rows must be contiguous")
+    if q.dim() != 3 or q.shape != out.shape or q.dtype != out.dtype or q.shape[2] != cache.head_dim:
+        raise ValueError("q and out must be matching [batch, num_qo_heads, head_dim] tensors")
+    if not (q.is_cuda and q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous CUDA tensors")
+    B = q.shape[0]
+    if block_tables.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("batch sizes disagree")
+    st = lib.kv_decode_attention(C.byref(cache.desc), _ptr(q), _half_enum(q.dtype), q.shape[1], _ptr(block_tables),
+                                 _stride(block_tables, 0), block_tables.shape[1], _ptr(seq_lens), B, _ptr(k_scale),
+                                 _ptr(v_scale), float(sm_scale), _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "kv_decode_attention")

@@ -12,13 +12,17 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libkvfp4.so")
-SOURCES = ["abi.hip", "append.hip", "dequant.hip", "materialize.hip", "global_scale.hip", "codec.hip"]
+SOURCES = ["abi.hip", "append.hip", "dequant.hip", "materialize.hip", "global_scale.hip", "codec.hip",
+           "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the attention kernel rescales and
+    # stores them with vector ALU work, which AGPRs would turn into copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-Wl,-rpath,/opt/rocm/lib",
 ]

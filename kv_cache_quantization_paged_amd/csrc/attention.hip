@@ -1,0 +1,699 @@
+// attention.hip - decode attention straight from the paged NVFP4 cache, for
+// gfx950. The cache is the one that the flashinfer.page append page fills and
+// that the flashinfer.quantization dequantize page says "the NVFP4 attention
+// kernels" consume: K and V are e2m1 * block_scale * global_scale.
+//
+// out[b, hq, :] = softmax_t(sm_scale * q[b, hq] . K[b, t]) V[b, t] over
+// t < seq_lens[b], with kv head h = hq / G (G = Hq / H query heads per kv
+// head), head_dim 128.
+//
+// Split over the sequence: a work item is (request, kv head, split of
+// kSplitTokens tokens), handled by one workgroup of kWaves wavefronts. The
+// workgroups are persistent (as many as stay resident); each builds the list
+// of live items from seq_lens and takes its share, XCD by XCD (see the split
+// kernel). Each wave takes kWaveTiles tiles of 32 tokens of an item with all
+// their loads in flight (the page id of a 16-token half tile is one
+// wave-uniform scalar load when the page size is a multiple of 16, and every
+// lane address is then a scalar base plus a per-lane constant), and keeps an
+// online softmax for the G (<= 16) query heads of its kv head. The waves
+// merge in LDS and write (max, sum, unnormalised output) to the caller's
+// workspace; a second kernel merges the splits of each (request, kv head).
+//
+// Both products run on v_mfma_f32_16x16x32_f16 (A 16x32, B 32x16; lane l
+// holds A[l%16][8(l/16)..+8], B[8(l/16)..+8][l%16], D[4(l/16)..+4][l%16]):
+//  * scores, S^T[token][g] = K[token][d] . Q^T[d][g]: 16 tokens per MFMA
+//    row block, the 128 channels in 4 MFMAs of 32. Lane group q = l/16
+//    takes channels 32q..32q+31 (one 16-byte code load and one 2-byte scale
+//    load per lane and token), and Q^T follows the same channel map.
+//  * output, O^T[d][g] += V^T[d][token] . P^T[token][g]: the 32 tokens of a
+//    tile in one MFMA, 8 MFMAs for the 128 channels, MFMA j covering
+//    channels 8m + j. The lane that holds P for tokens {4q + i, 16 + 4q + i}
+//    (its own scores) loads V code chunk l%16 of those 8 tokens.
+// Decoding runs in packed fp16: an E2M1 code times its E4M3 block scale has
+// at most 6 significant bits and lies in [2^-10, 2688], so code (converted
+// exactly) times scale (converted exactly) is exact in one v_pk_mul_f16.
+// V pairs two tokens per 32-bit word: a nibble interleave of the two
+// tokens' code words puts each channel's two codes in one byte, so one
+// conversion and one multiply by the two tokens' scales give the transposed
+// operand. A bf16 query row is moved into fp16 exactly, after scaling the
+// row by a power of two 2^k that puts its largest magnitude in [2^14, 2^15)
+// (components more than 2^38 below it round on fp16's subnormal grid); the
+// score factor carries 2^-k. The global scales are applied to the scores
+// (K) and to the output (V) in fp32; the probabilities are rounded to fp16
+// (11 significant bits) for the second MFMA.
+#include "kvfp4_internal.h"
+#include "nvfp4_device.h"
+
+namespace kvfp4 {
+
+namespace {
+
+constexpr int kD = 128;                     // head_dim
+constexpr int kTile = 32;                   // tokens per MFMA tile
+constexpr int kWaves = 4;                   // wavefronts per workgroup
+constexpr int kWaveTiles = 2;               // tiles per wave
+constexpr int kSplitTokens = kTile * kWaveTiles * kWaves;
+constexpr int kMaxPagesPerSplit = kSplitTokens + 1;
+constexpr float kSlack = 8.0f;              // log2 headroom of the softmax reference
+constexpr int kMaxBatchPerLaunch = 2048;    // requests whose split counts one workgroup keeps in LDS
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct AttnArgs {
+    const uint8_t *data[2];
+    const uint8_t *sf[2];
+    int64_t stride[2];
+    int64_t sf_stride[2];
+    const uint16_t *q;
+    uint16_t *out;
+    float *ws;                // [B][H][splits] partials: m[G], l[G], o[G][128]
+    int64_t bt_row_stride;
+    int32_t ps, H, G, Hq;
+    int32_t tok_rows;         // rows between consecutive tokens of a page (HND 1, NHD H)
+    int32_t head_rows;        // rows between consecutive kv heads of a page (HND ps, NHD 1)
+    int32_t splits;           // per (request, kv head)
+    int32_t batch;            // requests of this launch (bt, seq_lens, q and ws start at its first)
+    float sm_scale_log2;      // sm_scale * log2(e)
+};
+
+// floats per partial result of a split: max and sum per query head, then the
+// unnormalised output rows [G][128]
+__host__ __device__ constexpr int partial_floats(int G) { return 2 * G + G * kD; }
+
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3)
+{
+    const u32x4 w = {w0, w1, w2, w3};
+    return __builtin_bit_cast(f16x8, w);
+}
+
+// two E2M1 codes (byte SEL of w, low nibble first) -> fp16x2, exact
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_f16(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+}
+
+// two E4M3 bytes (bytes 0 and 1 of w) -> fp16x2, exact
+__device__ __forceinline__ uint32_t fp8x2_f16(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+
+// packed fp16 product (exact for the operands used here)
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b)
+{
+    const f16x2 r = __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 codes of one dword times the block scale (s, s) -> 8 fp16 values
+__device__ __forceinline__ f16x8 decode8(uint32_t codes, uint32_t ss)
+{
+    return as_f16x8(mul_f16x2(fp4x2_f16<0>(codes), ss), mul_f16x2(fp4x2_f16<1>(codes), ss),
+                    mul_f16x2(fp4x2_f16<2>(codes), ss), mul_f16x2(fp4x2_f16<3>(codes), ss));
+}
+
+// reductions over the 4 lanes l, l^16, l^32, l^48 (lane swaps, no LDS)
+__device__ __forceinline__ float max4(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum4(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ uint32_t max4_u32(uint32_t v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(r[0], r[1]);
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(s[0], s[1]);
+}
+
+// raw bytes of one 32-token tile for one lane
+struct TileLoads {
+    u32x4 kc[2];      // K codes: token 16 eta + n, channels 32 q .. 32 q + 31
+    uint32_t ks[2];   // their two scale bytes (blocks 2q, 2q + 1)
+    uint32_t vc[8];   // V codes: channels 8n .. 8n + 7 of token 16 (i / 4) + 4 q + i % 4
+    uint32_t vs[8];   // its scale byte (block n / 2)
+};
+
+// per-lane byte offsets inside a page for the fast loader
+struct LaneOffsets {
+    uint32_t k, ks, v, vs;
+};
+
+// page size a multiple of 16: each 16-token half of a tile lies in one page,
+// so a half is a scalar base (page, first slot) plus per-lane constants.
+__device__ __forceinline__ void load_half_fast(const AttnArgs &a, int64_t page, int row0, const LaneOffsets &o,
+                                               int eta, TileLoads &r)
+{
+    const uint8_t *kd = a.data[0] + page * a.stride[0] + (int64_t)row0 * (kD / 2);
+    const uint8_t *ksf = a.sf[0] + page * a.sf_stride[0] + (int64_t)row0 * (kD / 16);
+    const uint8_t *vd = a.data[1] + page * a.stride[1] + (int64_t)row0 * (kD / 2);
+    const uint8_t *vsf = a.sf[1] + page * a.sf_stride[1] + (int64_t)row0 * (kD / 16);
+    r.kc[eta] = *(const u32x4 *)(kd + o.k);
+    r.ks[eta] = *(const uint16_t *)(ksf + o.ks);
+    const int64_t tc = (int64_t)a.tok_rows * (kD / 2), ts = (int64_t)a.tok_rows * (kD / 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.vc[4 * eta + i] = *(const uint32_t *)(vd + i * tc + o.v);
+        r.vs[4 * eta + i] = vsf[i * ts + o.vs];
+    }
+}
+
+// any page size: per-token page ids from the split's LDS copy; a token past
+// the end reads the split's first token (always valid) and is masked later
+__device__ __forceinline__ void load_tile_any(const AttnArgs &a, const int *pages, int h, int t0, int t_base,
+                                              int len, int n, int qg, TileLoads &r)
+{
+    auto addr = [&](int t, int &row) -> int64_t {
+        t = t < len ? t : t_base;
+        const int pi = (t / a.ps) - (t_base / a.ps);
+        const int slot = t - (t / a.ps) * a.ps;
+        row = slot * a.tok_rows + h * a.head_rows;
+        return pages[pi];
+    };
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) {
+        int row;
+        const int64_t page = addr(t0 + 16 * eta + n, row);
+        r.kc[eta] = *(const u32x4 *)(a.data[0] + page * a.stride[0] + (int64_t)row * (kD / 2) + 16 * qg);
+        r.ks[eta] = *(const uint16_t *)(a.sf[0] + page * a.sf_stride[0] + (int64_t)row * (kD / 16) + 2 * qg);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int row;
+        const int64_t page = addr(t0 + 16 * (i >> 2) + 4 * qg + (i & 3), row);
+        r.vc[i] = *(const uint32_t *)(a.data[1] + page * a.stride[1] + (int64_t)row * (kD / 2) + 4 * n);
+        r.vs[i] = a.sf[1][page * a.sf_stride[1] + (int64_t)row * (kD / 16) + (n >> 1)];
+    }
+}
+
+// one 32-token tile: scores, online softmax update, value product
+template <bool first>
+__device__ __forceinline__ void attend_tile(TileLoads cur, const f16x8 qv[4], int t0, int len, int qg, float c,
+                                            float &m_run, float &l_run, f32x4 o[8])
+{
+    const bool partial = t0 + kTile > len;           // wave-uniform
+    if (partial) {
+        // a masked token's V scale becomes 0 so that its (finite) codes add
+        // nothing; its score becomes -inf below
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            cur.vs[i] = t0 + 16 * (i >> 2) + 4 * qg + (i & 3) < len ? cur.vs[i] : 0u;
+    }
+
+    // ---- scores: S^T[16 eta + 4 qg + i][n]
+    float s[8];
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) {
+        const uint32_t sc = fp8x2_f16(cur.ks[eta]);
+        const uint32_t s_lo = __builtin_amdgcn_perm(sc, sc, 0x01000100u);   // (s_lo, s_lo)
+        const uint32_t s_hi = __builtin_amdgcn_perm(sc, sc, 0x03020302u);   // (s_hi, s_hi)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma(decode8(cur.kc[eta].x, s_lo), qv[0], acc);
+        acc = mfma(decode8(cur.kc[eta].y, s_lo), qv[1], acc);
+        acc = mfma(decode8(cur.kc[eta].z, s_hi), qv[2], acc);
+        acc = mfma(decode8(cur.kc[eta].w, s_hi), qv[3], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[4 * eta + i] = acc[i] * c;
+    }
+    if (partial) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            s[i] = t0 + 16 * (i >> 2) + 4 * qg + (i & 3) < len ? s[i] : -INFINITY;
+    }
+
+    // ---- online softmax for head n (the 4 lanes n, n+16, n+32, n+48). The
+    // reference m_run moves only when a score exceeds it by more than
+    // kSlack, so p <= 2^kSlack (fine for fp16) and (o, l) are rarely
+    // rescaled; any reference gives the same o / l.
+    float tmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, s[i]);
+    tmax = max4(tmax);                                      // finite: the tile holds a valid token
+    const float m_new = tmax > m_run + kSlack ? tmax : m_run;   // always taken on the first tile
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 if kept, 0 on the first tile
+    float p[8], psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
+        psum += p[i];
+    }
+    l_run = l_run * alpha + sum4(psum);
+    m_run = m_new;
+    if (!first && __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // o is still zero on the first tile
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] *= alpha;
+    }
+
+    // ---- output: O^T[8 m + j][n] += V^T[8 m + j][token] P^T[token][n]
+    const f16x8 pv = as_f16x8(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
+                              pack_f16x2(p[6], p[7]));
+    // token pair i2 = (2 i2, 2 i2 + 1): byte b of ev[i2] holds channel 2b of both
+    // tokens (low nibble: the first), od[i2] channel 2b + 1; ss[i2] = their scales
+    uint32_t ev[4], od[4], ss[4];
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+        const uint32_t wa = cur.vc[2 * i2], wb = cur.vc[2 * i2 + 1];
+        ev[i2] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
+        od[i2] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+        ss[i2] = fp8x2_f16(cur.vs[2 * i2] | (cur.vs[2 * i2 + 1] << 8));
+    }
+    // one channel (MFMA) at a time keeps few decoded words live
+#define KVFP4_PV(J, SRC, SEL)                                                                                   \
+    o[J] = mfma(as_f16x8(mul_f16x2(fp4x2_f16<SEL>(SRC[0]), ss[0]), mul_f16x2(fp4x2_f16<SEL>(SRC[1]), ss[1]),        \
+                         mul_f16x2(fp4x2_f16<SEL>(SRC[2]), ss[2]), mul_f16x2(fp4x2_f16<SEL>(SRC[3]), ss[3])),       \
+                pv, o[J])
+    KVFP4_PV(0, ev, 0);
+    KVFP4_PV(1, od, 0);
+    KVFP4_PV(2, ev, 1);
+    KVFP4_PV(3, od, 1);
+    KVFP4_PV(4, ev, 2);
+    KVFP4_PV(5, od, 2);
+    KVFP4_PV(6, ev, 3);
+    KVFP4_PV(7, od, 3);
+#undef KVFP4_PV
+}
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_bits_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_bits_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// one work item: kv head h of request b over tokens [split * kSplitTokens,
+// + kSplitTokens) (len > split * kSplitTokens). All waves of the workgroup
+// call it together; it ends with the partial result in the workspace.
+template <bool BF16, bool FAST16>
+__device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__restrict__ bt,
+                                            const float *__restrict__ k_scale, int b, int h, int split, int len,
+                                            int *pages, float (*red_m)[16], float (*red_l)[16], float *red_o)
+{
+    const int tid = threadIdx.x, l = tid & 63, n = l & 15, qg = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform by construction
+
+    // the query rows first: their loads need no sequence length
+    // Q^T operands: head n of this kv head's group, channels 32 qg + 8 kappa .. +8
+    u32x4 qraw[4];
+    {
+        const bool live = n < a.G;
+        const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.G + (live ? n : 0)) * kD + 32 * qg;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qraw[k] = *(const u32x4 *)(qrow + 8 * k);
+    }
+
+    const int t_split = split * kSplitTokens;
+    const int t_w = t_split + w * (kTile * kWaveTiles);   // this wave's first token
+    const int32_t *row_bt = bt + b * a.bt_row_stride;
+
+    if (!FAST16) {
+        // the split's page ids, once, into LDS (a page may hold tokens of
+        // several tiles and halves)
+        const int t_end = min(len, t_split + kSplitTokens);
+        const int p0 = t_split / a.ps, p1 = (t_end - 1) / a.ps;
+        for (int p = p0 + tid; p <= p1; p += 64 * kWaves)
+            pages[p - p0] = row_bt[p];
+        __syncthreads();
+    }
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (t_w < len) {
+        TileLoads ld[2];
+        // fast loader state: the page index and slot of the next half to load
+        int pi = 0, slot = 0, pi_w = 0, slot_w = 0;
+        LaneOffsets lo;
+        if (FAST16) {
+            pi_w = t_w / a.ps;
+            slot_w = t_w - pi_w * a.ps;
+            pi = pi_w;
+            slot = slot_w;
+            const uint32_t tr = (uint32_t)a.tok_rows;
+            lo.k = n * tr * (kD / 2) + 16 * qg;
+            lo.ks = n * tr * (kD / 16) + 2 * qg;
+            lo.v = 4 * qg * tr * (kD / 2) + 4 * n;
+            lo.vs = 4 * qg * tr * (kD / 16) + (n >> 1);
+        }
+        auto issue = [&](int k) {
+            const int t0 = t_w + kTile * k;
+            if (t0 >= len)
+                return;
+            if (FAST16) {
+#pragma unroll
+                for (int eta = 0; eta < 2; ++eta) {
+                    // a half past the end reads the wave's first half
+                    const bool valid = t0 + 16 * eta < len;
+                    const int ppi = valid ? pi : pi_w, pslot = valid ? slot : slot_w;
+                    load_half_fast(a, row_bt[ppi], pslot * a.tok_rows + h * a.head_rows, lo, eta, ld[k & 1]);
+                    slot += 16;
+                    if (slot == a.ps) {
+                        slot = 0;
+                        ++pi;
+                    }
+                }
+            } else {
+                load_tile_any(a, pages, h, t0, t_split, len, n, qg, ld[k & 1]);
+            }
+        };
+        issue(0);
+        if (kWaveTiles > 1)
+            issue(1);
+
+        // the query rows into fp16 while the tiles load
+        f16x8 qv[4];
+        float c = a.sm_scale_log2 * *k_scale;         // scores to log2 units
+        if (n >= a.G) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) qraw[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+        if (BF16) {
+            // largest magnitude of the row (bf16 magnitudes order as integers)
+            uint32_t mx = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t v = qraw[k][e] & 0x7FFF7FFFu;
+                    mx = max(mx, max(v & 0xFFFFu, v >> 16));
+                }
+            mx = max4_u32(mx);
+            const int E = max((int)(mx >> 7), 1);      // biased exponent of the largest |q|
+            int ec;
+            (void)frexpf(c, &ec);                       // c = f 2^ec, f in [0.5, 1)
+            // 2^kk moves the largest |q| into [2^14, 2^15), kept so that
+            // c 2^-kk stays a normal fp32 number
+            const int kk = min(max(141 - E, ec - 126), ec + 125);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                u32x4 o16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o16[e] = pack_f16x2(ldexpf(bf16_bits_lo(qraw[k][e]), kk), ldexpf(bf16_bits_hi(qraw[k][e]), kk));
+                qv[k] = __builtin_bit_cast(f16x8, o16);
+            }
+            c = ldexpf(c, -kk);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) qv[k] = __builtin_bit_cast(f16x8, qraw[k]);
+        }
+
+#pragma unroll
+        for (int k = 0; k < kWaveTiles; ++k) {
+            const int t0 = t_w + kTile * k;
+            if (t0 < len) {
+                if (k == 0)
+                    attend_tile<true>(ld[k & 1], qv, t0, len, qg, c, m_run, l_run, o);
+                else
+                    attend_tile<false>(ld[k & 1], qv, t0, len, qg, c, m_run, l_run, o);
+            }
+            if (k + 2 < kWaveTiles)
+                issue(k + 2);
+        }
+    }
+
+    // ---- merge the waves: lane (qg, n) holds O^T[8 (4 qg + i) + j][n], that
+    // is channels 32 qg + 8 i .. + 8 of head n
+    if (qg == 0) {
+        red_m[w][n] = m_run;
+        red_l[w][n] = l_run;
+    }
+    if (n < a.G) {
+        float *orow = red_o + (w * a.G + n) * kD + 32 * qg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *(f32x4 *)(orow + 8 * i) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+            *(f32x4 *)(orow + 8 * i + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+        }
+    }
+    __syncthreads();
+    const int pf = partial_floats(a.G);
+    float *ws = a.ws + (((int64_t)b * a.H + h) * a.splits + split) * pf;
+    for (int idx = tid; idx < a.G * (kD / 4); idx += 64 * kWaves) {
+        const int g = idx / (kD / 4), d0 = (idx - g * (kD / 4)) * 4;
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, red_m[v][g]);
+        float L = 0.0f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const float f = __builtin_amdgcn_exp2f(red_m[v][g] - M);   // 0 for a wave without tokens
+            L += red_l[v][g] * f;
+            acc += *(const f32x4 *)(red_o + (v * a.G + g) * kD + d0) * f;
+        }
+        if (d0 == 0) {
+            ws[g] = M;
+            ws[a.G + g] = L;
+        }
+        *(f32x4 *)(ws + 2 * a.G + g * kD + d0) = acc;
+    }
+    __syncthreads();                                   // LDS is reused by the next item
+}
+
+// block-wide exclusive prefix sum of one int per thread (blockDim 64 * kWaves)
+__device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot, int &total)
+{
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (l >= d)
+            x += y;
+    }
+    if (l == 63)
+        wave_tot[w] = x;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        before += k < w ? wave_tot[k] : 0;
+        total += wave_tot[k];
+    }
+    __syncthreads();
+    return before + x - v;
+}
+
+// Persistent workgroups. The live work items are the (request b, split,
+// kv head h) with split * kSplitTokens < seq_lens[b]; every workgroup
+// builds the same list from seq_lens (cum[b] = live splits of the requests
+// before b, in LDS), so no item is launched dead. Item groups (b, split)
+// are dealt to the 8 XCDs by index mod 8 (workgroup x runs on XCD x mod 8
+// under the round-robin dispatch), and the H heads of a group go to H
+// workgroups of that XCD in the same round, so a page's lines shared by
+// several heads (NHD rows, scale rows) are fetched into one L2 once.
+template <bool BF16, bool FAST16>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void attention_split_kernel(AttnArgs a, const int32_t *__restrict__ bt,
+                                                                      const int32_t *__restrict__ seq_lens,
+                                                                      const float *__restrict__ k_scale)
+{
+    __shared__ int pages[FAST16 ? 1 : kMaxPagesPerSplit];
+    __shared__ float red_m[kWaves][16], red_l[kWaves][16];
+    __shared__ int wave_tot[kWaves];
+    __shared__ int4 items[64 * kWaves];              // (b, split, h, len)
+    extern __shared__ float dyn[];                   // red_o [kWaves][G][128], then cum [batch + 1]
+    float *red_o = dyn;
+    int *cum = (int *)(dyn + kWaves * a.G * kD);
+    const int tid = threadIdx.x, nthr = 64 * kWaves;
+
+    // ---- cum[b]: live splits of the requests before b
+    const int per = (a.batch + nthr - 1) / nthr;      // <= kMaxBatchPerLaunch / nthr
+    int mine = 0;
+    for (int k = 0; k < per; ++k) {
+        const int bb = tid * per + k;
+        mine += bb < a.batch ? (seq_lens[bb] + kSplitTokens - 1) / kSplitTokens : 0;
+    }
+    int total;
+    int run = block_exclusive_scan(mine, wave_tot, total);
+    for (int k = 0; k < per; ++k) {
+        const int bb = tid * per + k;
+        if (bb < a.batch) {
+            cum[bb] = run;
+            run += (seq_lens[bb] + kSplitTokens - 1) / kSplitTokens;
+        }
+    }
+    if (tid == 0)
+        cum[a.batch] = total;
+    __syncthreads();
+
+    // ---- this workgroup's share: groups g = xcd + 8 r, items m = r H + h,
+    // taken m = j, j + per_xcd, ...
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    const int64_t ngx = total > xcd ? (total - xcd + 7) / 8 : 0;
+    const int64_t nix = ngx * a.H;
+    for (int64_t base = j; base < nix; base += (int64_t)per_xcd * nthr) {
+        const int64_t m = base + (int64_t)per_xcd * tid;
+        if (m < nix) {
+            const int64_t r = m / a.H;
+            const int h = (int)(m - r * a.H);
+            const int g = (int)(xcd + 8 * r);
+            int lo = 0, hi = a.batch;                 // the request whose splits hold group g
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (cum[mid] <= g)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            items[tid] = int4{lo, g - cum[lo], h, seq_lens[lo]};
+        }
+        __syncthreads();
+        const int count = (int)min((int64_t)nthr, (nix - base + per_xcd - 1) / per_xcd);
+        for (int t = 0; t < count; ++t) {
+            const int4 it = items[t];
+            attend_item<BF16, FAST16>(a, bt, k_scale, it.x, it.z, it.y, it.w, pages, red_m, red_l, red_o);
+        }
+    }
+}
+
+// merge the live splits of one (request, kv head); thread -> (head g, 4
+// channels). Splits are taken 8 at a time, all their loads in flight, with
+// a running (max, sum, output) rescaled per group.
+template <bool BF16>
+__global__ __launch_bounds__(512) void attention_merge_kernel(AttnArgs a, const int32_t *__restrict__ seq_lens,
+                                                              const float *__restrict__ v_scale)
+{
+    constexpr int kGroup = 8;
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const int g = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
+    const int len = seq_lens[b];
+    const int live = min(a.splits, (len + kSplitTokens - 1) / kSplitTokens);
+    const int pf = partial_floats(a.G);
+    const float *ws = a.ws + (int64_t)bh * a.splits * pf;
+    float M = -INFINITY, L = 0.0f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < live; s0 += kGroup) {
+        float ms[kGroup], ls[kGroup];
+        f32x4 os[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const float *p = ws + min(s0 + u, live - 1) * pf;   // a repeat of the last split is dropped below
+            ms[u] = p[g];
+            ls[u] = p[a.G + g];
+            os[u] = *(const f32x4 *)(p + 2 * a.G + g * kD + d0);
+        }
+        float mx = M;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u)
+            if (s0 + u < live)
+                mx = fmaxf(mx, ms[u]);
+        const float f0 = __builtin_amdgcn_exp2f(M - mx);          // 0 on the first group
+        L *= f0;
+        acc *= f0;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u)
+            if (s0 + u < live) {
+                const float f = __builtin_amdgcn_exp2f(ms[u] - mx);
+                L += ls[u] * f;
+                acc += os[u] * f;
+            }
+        M = mx;
+    }
+    const float scale = L > 0.0f ? *v_scale / L : 0.0f;        // an empty request gives zeros
+    const uint32_t w0 = BF16 ? pack_bf16x2(acc[0] * scale, acc[1] * scale) : pack_f16x2(acc[0] * scale, acc[1] * scale);
+    const uint32_t w1 = BF16 ? pack_bf16x2(acc[2] * scale, acc[3] * scale) : pack_f16x2(acc[2] * scale, acc[3] * scale);
+    *(u32x2 *)(a.out + ((int64_t)b * a.Hq + h * a.G + g) * kD + d0) = u32x2{w0, w1};
+}
+
+}  // namespace
+
+int64_t decode_attention_splits(int32_t bt_cols, int32_t page_size)
+{
+    const int64_t tokens = (int64_t)bt_cols * page_size;
+    return tokens > 0 ? (tokens + kSplitTokens - 1) / kSplitTokens : 1;
+}
+
+int64_t decode_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_qo_heads, int32_t bt_cols,
+                                         int32_t page_size)
+{
+    const int G = num_qo_heads / num_kv_heads;
+    return (int64_t)batch * num_kv_heads * decode_attention_splits(bt_cols, page_size) * partial_floats(G) * 4;
+}
+
+hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, bool bf16, int32_t num_qo_heads,
+                                   const int32_t *bt, int64_t bt_row_stride, int32_t bt_cols,
+                                   const int32_t *seq_lens, int32_t batch, const float *k_scale,
+                                   const float *v_scale, float sm_scale, void *out, void *workspace,
+                                   hipStream_t st)
+{
+    AttnArgs a;
+    a.data[0] = (const uint8_t *)c.k_data;
+    a.data[1] = (const uint8_t *)c.v_data;
+    a.sf[0] = (const uint8_t *)c.k_sf;
+    a.sf[1] = (const uint8_t *)c.v_sf;
+    a.stride[0] = c.k_page_stride;
+    a.stride[1] = c.v_page_stride;
+    a.sf_stride[0] = c.k_sf_page_stride;
+    a.sf_stride[1] = c.v_sf_page_stride;
+    a.q = (const uint16_t *)q;
+    a.out = (uint16_t *)out;
+    a.ws = (float *)workspace;
+    a.bt_row_stride = bt_row_stride;
+    a.ps = c.page_size;
+    a.H = c.num_kv_heads;
+    a.Hq = num_qo_heads;
+    a.G = num_qo_heads / c.num_kv_heads;
+    a.tok_rows = c.layout == KVFP4_HND ? 1 : c.num_kv_heads;
+    a.head_rows = c.layout == KVFP4_HND ? c.page_size : 1;
+    a.splits = (int32_t)decode_attention_splits(bt_cols, c.page_size);
+    a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+    const int64_t bh = (int64_t)batch * c.num_kv_heads;
+    if (bh == 0)
+        return hipSuccess;
+    typedef void (*split_fn)(AttnArgs, const int32_t *, const int32_t *, const float *);
+    const bool fast = c.page_size % 16 == 0;
+    const split_fn kernel = bf16 ? (fast ? attention_split_kernel<true, true> : attention_split_kernel<true, false>)
+                                 : (fast ? attention_split_kernel<false, true> : attention_split_kernel<false, false>);
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    const int64_t pf = partial_floats(a.G);
+    for (int64_t b0 = 0; b0 < batch; b0 += kMaxBatchPerLaunch) {
+        AttnArgs ac = a;
+        ac.batch = (int32_t)(batch - b0 < kMaxBatchPerLaunch ? batch - b0 : kMaxBatchPerLaunch);
+        ac.q = a.q + b0 * a.Hq * kD;
+        ac.ws = a.ws + b0 * a.H * a.splits * pf;
+        const size_t lds = (size_t)kWaves * a.G * kD * sizeof(float) + (size_t)(ac.batch + 1) * sizeof(int);
+        // as many workgroups as stay resident, a multiple of the 8 XCDs, and
+        // no more than there can be items
+        int occ = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 64 * kWaves, lds);
+        if (e != hipSuccess)
+            return e;
+        const int64_t most = ((int64_t)ac.batch * a.H * a.splits + 7) / 8 * 8;
+        int64_t grid = (int64_t)(occ > 0 ? occ : 1) * cus / 8 * 8;
+        grid = grid < 8 ? 8 : (grid > most ? most : grid);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * kWaves), lds, st, ac, bt + b0 * bt_row_stride,
+                           seq_lens + b0, k_scale);
+    }
+    const dim3 merge_threads((unsigned)(32 * a.G));           // one thread per (query head, 4 channels)
+    if (bf16)
+        hipLaunchKernelGGL((attention_merge_kernel<true>), dim3((unsigned)bh), merge_threads, 0, st, a, seq_lens,
+                           v_scale);
+    else
+        hipLaunchKernelGGL((attention_merge_kernel<false>), dim3((unsigned)bh), merge_threads, 0, st, a, seq_lens,
+                           v_scale);
+    return hipGetLastError();
+}
+
+}  // namespace kvfp4

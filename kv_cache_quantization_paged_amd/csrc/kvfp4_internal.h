@@ -42,4 +42,13 @@ hipError_t launch_quantize_paged_cache(const kvfp4_paged_cache_t &c, const void 
                                        bool in_bf16, const float *k_scale, const float *v_scale,
                                        const kvfp4_recipe_t *recipe, bool v_interleaved, hipStream_t st);
 
+hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, bool bf16, int32_t num_qo_heads,
+                                   const int32_t *bt, int64_t bt_row_stride, int32_t bt_cols,
+                                   const int32_t *seq_lens, int32_t batch, const float *k_scale,
+                                   const float *v_scale, float sm_scale, void *out, void *workspace,
+                                   hipStream_t st);
+int64_t decode_attention_splits(int32_t bt_cols, int32_t page_size);
+int64_t decode_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_qo_heads, int32_t bt_cols,
+                                         int32_t page_size);
+
 }  // namespace kvfp4

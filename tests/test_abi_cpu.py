@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
-                            "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kvfp4_status_string"])
+                            "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
+                            "kv_decode_attention_workspace_size", "kvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -175,6 +176,33 @@ def test_pool_quantizer_rejects_bad_arguments(B):
     assert call(_cache(B, k_page_stride=100), inter=0) == B.KVFP4_EINVAL       # stride below a compact page
     bad_fast = B.RecipeDesc(300.0, 1, 1)
     assert call(_cache(B, **hnd), recipe=C.byref(bad_fast)) == B.KVFP4_EINVAL
+
+
+def test_decode_attention_rejects_bad_arguments(B):
+    lib = B.load_library()
+    P = C.c_void_p
+
+    def call(cache, q=P(4096), dt=1, hq=16, bt=P(64), row=8, cols=8, sl=P(64), batch=2, ks=P(64), vs=P(64),
+             sm=0.1, out=P(8192), ws=P(1 << 20), wsb=1 << 30):
+        return lib.kv_decode_attention(C.byref(cache), q, dt, hq, bt, row, cols, sl, batch, ks, vs, sm, out, ws, wsb,
+                                       None)
+    assert call(_cache(B), dt=4) == B.KVFP4_EINVAL
+    assert call(_cache(B), hq=12) == B.KVFP4_EINVAL                           # not a multiple of 8 kv heads
+    assert call(_cache(B), hq=8 * 17) == B.KVFP4_EUNSUPPORTED                 # group of 17
+    assert call(_cache(B, head_dim=64, k_page_stride=4096, v_page_stride=4096, k_sf_page_stride=512,
+                       v_sf_page_stride=512)) == B.KVFP4_EUNSUPPORTED
+    assert call(_cache(B), sm=float("nan")) == B.KVFP4_EINVAL
+    assert call(_cache(B), row=4) == B.KVFP4_EINVAL
+    assert call(_cache(B), batch=0, q=None, bt=None, sl=None, out=None) == B.KVFP4_OK
+    assert call(_cache(B), vs=None) == B.KVFP4_EINVAL
+    assert call(_cache(B), out=P(8200)) == B.KVFP4_EALIGN
+    assert call(_cache(B, k_sf=49)) == B.KVFP4_EALIGN                          # 2-byte scale loads
+    need = lib.kv_decode_attention_workspace_size(2, 8, 16, 8, 16)
+    assert need > 0 and lib.kv_decode_attention_workspace_size(-1, 8, 16, 8, 16) == -1
+    assert lib.kv_decode_attention_workspace_size(2, 8, 12, 8, 16) == -1
+    assert call(_cache(B), wsb=need - 1) == B.KVFP4_EINVAL                     # workspace too small
+    assert call(_cache(B), ws=None) == B.KVFP4_EINVAL
+    assert call(_cache(B), ws=P((1 << 20) + 8)) == B.KVFP4_EALIGN
 
 
 def test_package_refuses_to_run_without_library(tmp_path, monkeypatch):
