@@ -88,7 +88,7 @@ typedef struct {
 
 /*
  * A paged NVFP4 cache (append and dequantize pages: paged_kv_cache and
- * kv_cache_sf, "tuple or stacked" format). Per page, the data holds
+ * kv_cache_sf, as a tuple or a stacked tensor). Per page, the data holds
  * [page_size, num_kv_heads, head_dim/2] bytes (NHD) or
  * [num_kv_heads, page_size, head_dim/2] (HND), compact inside the page; the
  * scales the same with head_dim/16 bytes per row. Page p of K data starts at
@@ -254,9 +254,9 @@ kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const v
 
 /*
  * kv_decode_attention - the NVFP4 attention consumer of the paged cache
- * (flashinfer.quantization.nvfp4_kv_dequantize_paged page: k_scale and
- * v_scale are "the global decode scales consumed by the NVFP4 attention
- * kernels", values e2m1 * block_scale * global_scale). For each request b
+ * (flashinfer.quantization.nvfp4_kv_dequantize_paged page, which names
+ * FlashInfer's NVFP4 attention kernels as users of its global decode scales
+ * k_scale and v_scale; values e2m1 * block_scale * global_scale). For each request b
  * and query head hq (kv head hq / (num_qo_heads / num_kv_heads)):
  *   out[b, hq, :] = sum_t softmax_t(sm_scale * q[b, hq, :] . K[b, t, h, :]) V[b, t, h, :]
  * over t < seq_lens[b], K and V decoded from the cache (page

@@ -1,7 +1,8 @@
 // attention.hip - decode attention straight from the paged NVFP4 cache, for
-// gfx950. The cache is the one that the flashinfer.page append page fills and
-// that the flashinfer.quantization dequantize page says "the NVFP4 attention
-// kernels" consume: K and V are e2m1 * block_scale * global_scale.
+// gfx950. The cache is the one that the flashinfer.page append page fills;
+// the flashinfer.quantization dequantize page names FlashInfer's NVFP4
+// attention kernels as the consumers of its global decode scales. K and V
+// are e2m1 * block_scale * global_scale.
 //
 // out[b, hq, :] = softmax_t(sm_scale * q[b, hq] . K[b, t]) V[b, t] over
 // t < seq_lens[b], with kv head h = hq / G (G = Hq / H query heads per kv

@@ -27,7 +27,7 @@
  * representable value with ties going to the even code.
  *
  * Precision: the quantizer decides integer codes from fp32 values and the
- * 4over6 page says the error is evaluated "exactly in fp32", so every step of
+ * 4over6 page fixes the error evaluation at exact fp32, so every step of
  * the method is an fp32 operation here; the file is built with
  * -ffp-contract=off so that no multiply-add is fused, and on x86-64 each
  * float operation rounds to fp32. Only the format definitions themselves
@@ -40,8 +40,8 @@
  *   R3  E2M1 rounding: nearest, ties to even, saturating at +-6; the sign of
  *       v is kept, so negative values that round to zero give code 0x8.
  *   R4  4over6 clamps: the amax/6 candidate is clamped at the recipe's
- *       e4m3_max, the amax/4 candidate at 448 (the page says its 1.5x larger
- *       value 384 "still fits E4M3").
+ *       e4m3_max, the amax/4 candidate at 448 (the page notes that its 1.5x
+ *       larger value 384 stays inside the E4M3 range).
  *   R5  4over6 error: reconstruction versus the input, in fp32, per element
  *       d = x - fp32(dec * e2m1); term d*d (MSE) or |d| (MAE); summed by a
  *       balanced pairwise tree in index order; amax/4 kept only when its
@@ -62,13 +62,14 @@
  *       reconstruction rounded to fp16, then the difference, the square
  *       (MSE) and each pairwise sum rounded to fp16 (RNE, overflow to inf);
  *       the candidates compare as in R5.
- *   R11 whole-pool quantizer [KV] (nvfp4_quantize_paged_kv_cache, "for the
- *       trtllm-gen MHA kernel"): quantizes every slot of every page with
+ *   R11 whole-pool quantizer [KV] (nvfp4_quantize_paged_kv_cache, which the
+ *       page ties to the trtllm-gen MHA kernel): quantizes every slot of every page with
  *       R1-R5, K scales linear, V scales in the R9 interleave, which is the
  *       layout [MF] says this function produces.
  *
- *   R13 decode attention over the NVFP4 cache [DQ: "consumed by the NVFP4
- *       attention kernels", values e2m1 * block_scale * global_scale]:
+ *   R13 decode attention over the NVFP4 cache [DQ: the page names the NVFP4
+ *       attention kernels as users of its global decode scales; values
+ *       e2m1 * block_scale * global_scale]:
  *       scaled dot-product attention of one query token per request over
  *       the exact dequantized K and V (no 16-bit rounding, as a fused
  *       consumer has none), grouped-query heads hq -> hq / (Hq / H); an

@@ -1,6 +1,7 @@
 """Pins for the oracle's decode attention over the paged NVFP4 cache (the
-dequantized values e2m1 * block_scale * global_scale "consumed by the NVFP4
-attention kernels", flashinfer.quantization.nvfp4_kv_dequantize_paged page).
+dequantized values e2m1 * block_scale * global_scale, whose global scales the
+flashinfer.quantization.nvfp4_kv_dequantize_paged page names as inputs of the
+NVFP4 attention kernels).
 
 The reference here is torch's scaled_dot_product_attention in float64 on K
 and V decoded independently of the oracle (E4M3 values from torch's
