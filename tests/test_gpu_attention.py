@@ -147,3 +147,16 @@ def test_attention_batch_beyond_one_launch(K, orc):
     lens = [int(x) for x in rng.integers(0, 40, size=2100)]
     check = [0, 1, 2046, 2047, 2048, 2049, 2099]
     run_case(K, orc, 651, W.HND, 16, 1, 2, lens, True, check=check)
+
+
+@pytest.mark.parametrize("sm", [0.0, -0.25, 3.0])
+def test_attention_sm_scale_edge_values(K, orc, sm):
+    """sm_scale 0 (every weight equal: the plain mean of V), a negative scale
+    (the softmax of reversed scores) and a large one, on fp16 and bf16"""
+    for bf16 in (True, False):
+        run_case(K, orc, 660 + int(sm * 8) + bf16, W.HND, 16, 2, 4, [1, 47, 260], bf16, sm=sm)
+
+
+def test_attention_split_boundaries(K, orc):
+    """lengths at and next to the 256-token split and 64-token wave edges"""
+    run_case(K, orc, 670, W.NHD, 16, 2, 4, [256, 512, 768, 255, 511, 64, 65, 192, 193], True)
