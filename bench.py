@@ -598,7 +598,7 @@ def main():
                     help="minimum host time spent timing the oracle (whole decode steps)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the paged NVFP4 path needs no collectives and this build has no "
+        print("bench.py measures one GPU only: the paged NVFP4 path needs no collectives and this library has no "
               "multi-GPU step (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

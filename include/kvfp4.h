@@ -55,7 +55,7 @@ enum {
     KVFP4_OK = 0,
     KVFP4_EINVAL = 1,        /* null pointer, bad enum, bad extent or scale */
     KVFP4_EALIGN = 2,        /* a base pointer or stride is not 16-byte aligned */
-    KVFP4_EUNSUPPORTED = 3,  /* a valid request this build does not implement */
+    KVFP4_EUNSUPPORTED = 3,  /* a valid request the library does not implement */
     KVFP4_ELAUNCH = 4        /* the HIP runtime refused a launch */
 };
 
