@@ -9,8 +9,10 @@
 // instruction writes 1 KiB of contiguous HBM whatever the cache layout. A
 // lane owns 8 consecutive outputs per chunk: 4 code bytes and its block's
 // scale byte in, 16 bytes out. NHD vs HND only changes where a chunk's code
-// bytes are read. The grid has one workgroup per (request, page, part) of the
-// B * ceil(T/ps) table, so large pages still spread over many workgroups;
+// bytes are read (HND pages whose geometry allows it are staged through LDS
+// instead, see dequant_hnd_lds_kernel). The grid has one workgroup per
+// (request, page, part) of the B * ceil(T/ps) table, so large pages still
+// spread over many workgroups;
 // workgroups past a request's length exit at once. Active pages are scattered
 // through that table when lengths differ, and a persistent loop over it
 // leaves some workgroups with several times the work of others; one
@@ -185,6 +187,99 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const 
     }
 }
 
+// HND pages through LDS. When a token's H * D / 8 chunks divide the item
+// (kBatchLds * 256 chunks: then H, D / 8 and the item's tokens ti are powers
+// of two) and ti divides the page, an item is tokens [t_a, t_a + ti) of one
+// page for every head. The workgroup reads each head's run of ti rows (ti * D / 2
+// code bytes, ti * D / 16 scale bytes, contiguous in the page) with 16- and
+// 4-byte loads in address order, parks them in LDS, and each lane then takes
+// its chunks in output order from there: reads as contiguous as the writes.
+// Each head's code block in LDS is padded by kLdsPad bytes so that the four
+// 16-lane groups of a wave, which read four heads, start on different banks.
+constexpr int kLdsPad = 64;
+// chunks per lane and tensor in an LDS-staged item: 1024-chunk items (8
+// tokens of 8 heads x 128) measured fastest on the prefill workload, ahead
+// of 512, 2048 and 4096
+constexpr int kBatchLds = 4;
+
+struct HndLdsShape {
+    int32_t ti;                  // tokens per item
+    int32_t s_cpt, s_cpr;        // log2 of chunks per token (H * D / 8) and per row (D / 8)
+};
+
+template <bool BF16, bool BT64>
+__global__ __launch_bounds__(kThreads) void dequant_hnd_lds_kernel(DequantArgs a, HndLdsShape sh,
+                                                                   const void *__restrict__ block_tables,
+                                                                   const int32_t *__restrict__ seq_lens,
+                                                                   const float *__restrict__ k_scale,
+                                                                   const float *__restrict__ v_scale)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int ti = sh.ti, half_row = a.D >> 1, nb = a.D >> 4;
+    const int code_head = ti * half_row + kLdsPad, code_tensor = a.H * code_head;
+    const int sf_head = ti * nb, sf_tensor = a.H * sf_head;
+    uint8_t *lc = lds, *ls = lds + 2 * code_tensor;
+    const int pieces_head = ti * half_row / 16, pieces = a.H * pieces_head;   // 16-byte code pieces
+    const int spieces_head = sf_head / 4, spieces = a.H * spieces_head;       // 4-byte scale pieces
+    const int cpt_mask = (1 << sh.s_cpt) - 1, cpr_mask = (1 << sh.s_cpr) - 1;
+    const float g[2] = {*k_scale, *v_scale};
+    const uint32_t page_bytes = (uint32_t)(a.ps * a.H * half_row);
+    const uint32_t page_sf_bytes = (uint32_t)(a.ps * a.H * nb);
+
+    for (int item = blockIdx.x; item < a.num_items; item += gridDim.x) {
+        const int pair = item / a.parts;
+        const int part = item - pair * a.parts;
+        const int b = pair / a.pages_per_req;
+        const int j = pair - b * a.pages_per_req;
+        const int len = min(seq_lens[b], a.T);
+        const int t_a = part * ti;                        // the item's first token in the page
+        const int t_first = j * a.ps + t_a;
+        if (t_first >= len)
+            continue;                                     // workgroup-uniform
+        const int n_tok = min(ti, len - t_first);
+        const int64_t page = BT64 ? ((const int64_t *)block_tables)[b * a.bt_row_stride + j]
+                                  : (int64_t)((const int32_t *)block_tables)[b * a.bt_row_stride + j];
+        const rsrc_t src[2] = {make_rsrc(a.data[0] + page * a.stride[0], page_bytes),
+                               make_rsrc(a.data[1] + page * a.stride[1], page_bytes)};
+        const rsrc_t sfs[2] = {make_rsrc(a.sf[0] + page * a.sf_stride[0], page_sf_bytes),
+                               make_rsrc(a.sf[1] + page * a.sf_stride[1], page_sf_bytes)};
+        // head runs into LDS (rows past the valid tokens are read too: they
+        // lie in the page, and their outputs are never stored)
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
+            for (int q = tid; q < pieces; q += kThreads) {
+                const int h = q / pieces_head, o = q - h * pieces_head;
+                const u32x4 v = buf_load_u32x4(src[kv], (uint32_t)((h * a.ps + t_a) * half_row + o * 16));
+                *(u32x4 *)(lc + kv * code_tensor + h * code_head + o * 16) = v;
+            }
+            for (int q = tid; q < spieces; q += kThreads) {
+                const int h = q / spieces_head, o = q - h * spieces_head;
+                const uint32_t v = buf_load_u32(sfs[kv], (uint32_t)((h * a.ps + t_a) * nb + o * 4));
+                *(uint32_t *)(ls + kv * sf_tensor + h * sf_head + o * 4) = v;
+            }
+        }
+        __syncthreads();
+        const int64_t out_off = ((int64_t)b * a.T + t_first) * a.H * a.D;
+        const uint32_t n_bytes = (uint32_t)n_tok * a.H * (a.D >> 3) * 16u;
+        const rsrc_t dst[2] = {make_rsrc(a.out[0] + out_off, n_bytes), make_rsrc(a.out[1] + out_off, n_bytes)};
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
+            for (int u = 0; u < kBatchLds; ++u) {
+                const int ci = tid + u * kThreads;            // chunk of the item, output order (t, h, cc)
+                const int tl = ci >> sh.s_cpt, rem = ci & cpt_mask;
+                const int h = rem >> sh.s_cpr, cc = rem & cpr_mask;
+                const uint32_t code = *(const uint32_t *)(lc + kv * code_tensor + h * code_head + tl * half_row + cc * 4);
+                const uint32_t sbyte = ls[kv * sf_tensor + h * sf_head + tl * nb + (cc >> 1)];
+                const float dec = e4m3_byte_to_f32(sbyte) * g[kv];
+                buf_store_u32x4_nt(decode_chunk<BF16>(code, dec), dst[kv], (uint32_t)ci * 16u);
+            }
+        }
+        __syncthreads();                                  // LDS is reused by the next item of this workgroup
+    }
+}
+
 struct DequantPtrs {
     const void *block_tables;
     const int32_t *seq_lens;
@@ -239,6 +334,44 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
     const DequantPtrs p = {block_tables, seq_lens, k_scale, v_scale};
     const int grid = (int)(items < kMaxGrid ? items : kMaxGrid);
     const bool hnd = c.layout == KVFP4_HND;
+    if (hnd) {
+        // the LDS path: chunks per token a power of two dividing the item,
+        // the item's tokens dividing the page, at most 64 heads, rows of at
+        // least 16 code bytes (16-byte aligned head runs)
+        const int64_t cpt = (int64_t)c.num_kv_heads * (c.head_dim / 8);
+        const int64_t unit_lds = (int64_t)kBatchLds * kThreads;
+        if ((cpt & (cpt - 1)) == 0 && cpt <= unit_lds && c.page_size % (unit_lds / cpt) == 0 &&
+            c.num_kv_heads <= 64 && c.head_dim >= 32) {
+            HndLdsShape sh;
+            sh.ti = (int32_t)(unit_lds / cpt);
+            a.parts = (int32_t)(c.page_size / sh.ti);
+            const int64_t items_lds = (int64_t)batch * a.pages_per_req * a.parts;
+            if (items_lds > INT32_MAX)
+                return hipErrorInvalidValue;
+            a.num_items = (int32_t)items_lds;
+            const int grid_lds = (int)(items_lds < kMaxGrid ? items_lds : kMaxGrid);
+            sh.s_cpt = __builtin_ctzll((unsigned long long)cpt);
+            sh.s_cpr = __builtin_ctz((unsigned)(c.head_dim / 8));
+            const size_t lds = (size_t)2 * c.num_kv_heads * (sh.ti * (c.head_dim / 2) + kLdsPad) +
+                               (size_t)2 * c.num_kv_heads * sh.ti * (c.head_dim / 16);
+            if (bt64) {
+                if (out_bf16)
+                    hipLaunchKernelGGL((dequant_hnd_lds_kernel<true, true>), dim3(grid_lds), dim3(kThreads), lds, st, a,
+                                       sh, block_tables, seq_lens, k_scale, v_scale);
+                else
+                    hipLaunchKernelGGL((dequant_hnd_lds_kernel<false, true>), dim3(grid_lds), dim3(kThreads), lds, st, a,
+                                       sh, block_tables, seq_lens, k_scale, v_scale);
+            } else {
+                if (out_bf16)
+                    hipLaunchKernelGGL((dequant_hnd_lds_kernel<true, false>), dim3(grid_lds), dim3(kThreads), lds, st, a,
+                                       sh, block_tables, seq_lens, k_scale, v_scale);
+                else
+                    hipLaunchKernelGGL((dequant_hnd_lds_kernel<false, false>), dim3(grid_lds), dim3(kThreads), lds, st,
+                                       a, sh, block_tables, seq_lens, k_scale, v_scale);
+            }
+            return hipGetLastError();
+        }
+    }
     if (hnd)
         return out_bf16 ? launch3<true, true>(bt64, a, p, grid, st) : launch3<true, false>(bt64, a, p, grid, st);
     return out_bf16 ? launch3<false, true>(bt64, a, p, grid, st) : launch3<false, false>(bt64, a, p, grid, st);

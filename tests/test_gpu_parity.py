@@ -172,7 +172,7 @@ def dequant_case(seed, layout, ps, H, D, B=7, pool=60, neg_scales=True, stacked=
 @pytest.mark.parametrize("layout", [W.NHD, W.HND])
 @pytest.mark.parametrize("out_bf16", [True, False])
 @pytest.mark.parametrize("bt64", [False, True])
-@pytest.mark.parametrize("geom", [(16, 8, 128), (32, 2, 64), (5, 3, 48), (1, 16, 256)])
+@pytest.mark.parametrize("geom", [(16, 8, 128), (32, 2, 64), (5, 3, 48), (1, 16, 256), (64, 4, 128), (32, 8, 64)])
 def test_dequant_parity(K, orc, layout, out_bf16, bt64, geom):
     ps, H, D = geom
     seed = 500 + layout + 2 * out_bf16 + 4 * bt64 + ps
@@ -197,9 +197,13 @@ def test_dequant_parity(K, orc, layout, out_bf16, bt64, geom):
     assert np.array_equal(gv_bits, ov), first_mismatch(gv_bits, ov)
 
 
-def test_dequant_stacked_padded_and_empty(K, orc):
-    cache, bt, lens, T = dequant_case(77, W.HND, 16, 4, 128, stacked=True, data_pad=64)
-    B, H, D = len(lens), 4, 128
+@pytest.mark.parametrize("geom", [(16, 4, 128), (32, 8, 128)])
+def test_dequant_stacked_padded_and_empty(K, orc, geom):
+    """HND page 16 x 4 heads (read head row by head row) and page 32 x 8
+    heads (whole head runs staged through LDS, two items per page)"""
+    ps, H, D = geom
+    cache, bt, lens, T = dequant_case(77 + ps, W.HND, ps, H, D, stacked=True, data_pad=64)
+    B = len(lens)
     ok = np.full((B, T, H, D), W.SENTINEL_16, np.uint16)
     ov = ok.copy()
     orc.dequantize_paged(cache, bt, lens, 0.5, 0.25, ok, ov, True)
