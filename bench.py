@@ -94,26 +94,37 @@ class Env:
         sview = [b.view((pages,) + inner_s) for b in sfs]
         return self.K.PagedCache(dview[0], dview[1], sview[0], sview[1], layout), (bufs, sfs, dview, sview)
 
-    def steady(self, fns, iters, warmup):
+    def steady(self, fns, iters, warmup, batches=3):
         """Launch fns[i % len(fns)] back to back (replicas in disjoint memory,
-        so nothing is reused from the 256 MB Infinity Cache) and return the
-        (mean, median) in ms of the per-launch HIP-event times. In this
-        steady state each launch also pays the write-back its predecessor left
-        dirty in the cache, as a serving loop does; a kernel timed alone after
-        a flush would leave up to 256 MB of its own output unwritten when its
-        end event fires."""
+        so nothing is reused from the 256 MB Infinity Cache) in `batches`
+        runs, each bracketed by one pair of HIP events on the current stream
+        (the stream the library launches on), and return (mean, median) in ms
+        per launch: the mean over all launches and the median of the batch
+        averages. An event pair around every launch would add the events' own
+        few microseconds to each launch; around a batch it is spread over
+        the batch, and the per-launch time matches the profiler's kernel
+        durations. In this steady state each launch also pays the write-back
+        its predecessor left dirty in the cache, as a serving loop does; a
+        kernel timed alone after a flush would leave up to 256 MB of its own
+        output unwritten when its end event fires."""
         torch = self.torch
         for i in range(warmup):
             fns[i % len(fns)]()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        batches = max(1, min(batches, iters))
+        sizes = [iters // batches + (1 if b < iters % batches else 0) for b in range(batches)]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sizes]
         torch.cuda.synchronize()
-        for i in range(iters):
-            evs[i][0].record()
-            fns[i % len(fns)]()
-            evs[i][1].record()
+        i = 0
+        for (ev0, ev1), n in zip(evs, sizes):
+            ev0.record()
+            for _ in range(n):
+                fns[i % len(fns)]()
+                i += 1
+            ev1.record()
         torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) for a, b in evs]
-        return statistics.mean(ts), statistics.median(ts)
+        per = [a.elapsed_time(b) / n for (a, b), n in zip(evs, sizes)]
+        total = sum(a.elapsed_time(b) for a, b in evs)
+        return total / iters, statistics.median(per)
 
 
 def student_t3(env, shape, gen):
@@ -628,20 +639,11 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    # the dequant's own launch time, for the roofline: the same steps again,
-    # with HIP events around each dequant on the stream it is launched on
-    log(f"bench: timing the dequant launches of {args.steps} steps")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        r = reps[i % n_rep]
-        r.append()
-        evs[i][0].record()
-        r.dequant()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    deq_ms = [a.elapsed_time(b) for a, b in evs]
-    deq_avg = sum(deq_ms) / len(deq_ms)
+    # the dequant's own launch time, for the roofline: as many dequant
+    # launches as timed steps, over the same replicas, back to back in three
+    # batches bracketed by HIP events on the stream they are launched on
+    log(f"bench: timing {args.steps} dequant launches")
+    deq_avg, deq_med = env.steady([r.dequant for r in reps], args.steps, 0)
     step_bytes = reps[0].append_bytes + reps[0].dequant_bytes
     value = step_bytes / (ms_step * 1e6)
     achieved = reps[0].dequant_bytes / (deq_avg * 1e6)
@@ -653,7 +655,7 @@ def main():
     app_ms = graph_latency(env, [r.append for r in reps], 20, 10)
     legs = {"decode_append_us": app_ms * 1e3, "decode_append_us_eager": app_eager_ms * 1e3,
             "decode_dequant": {"kernel": "kv_dequantize_paged", "bytes": reps[0].dequant_bytes,
-                               "us_avg": deq_avg * 1e3, "us_median": statistics.median(deq_ms) * 1e3,
+                               "us_avg": deq_avg * 1e3, "us_median": deq_med * 1e3,
                                "GBps": achieved, "frac": achieved / PEAK_GBS}}
     del reps
     torch.cuda.empty_cache()
