@@ -197,6 +197,32 @@ def test_dequant_parity(K, orc, layout, out_bf16, bt64, geom):
     assert np.array_equal(gv_bits, ov), first_mismatch(gv_bits, ov)
 
 
+# HND geometries on both sides of the LDS-staged path's conditions (H * D / 8
+# a power of two up to 1024 whose item tokens divide the page, H <= 64,
+# D >= 32): staged (16,16,64) (64,4,32) (16,32,32) (8,64,128) (32,1,256)
+# (16,2,256); read in place (8,2,256) (16,64,256) (24,4,64) (16,8,16)
+@pytest.mark.parametrize("geom", [(16, 16, 64), (64, 4, 32), (16, 32, 32), (8, 64, 128), (32, 1, 256),
+                                  (16, 2, 256), (8, 2, 256), (16, 64, 256), (24, 4, 64), (16, 8, 16)])
+def test_dequant_hnd_geometry_sweep(K, orc, geom):
+    ps, H, D = geom
+    seed = 900 + ps + 3 * H + D
+    cache, bt, lens, T = dequant_case(seed, W.HND, ps, H, D, B=5, pool=24)
+    B = len(lens)
+    ok = np.full((B, T, H, D), W.SENTINEL_16, np.uint16)
+    ov = ok.copy()
+    orc.dequantize_paged(cache, bt, lens, 0.0625, 3.0, ok, ov, True, threads=oracle_threads())
+    dev = DeviceCache(cache)
+    dk = torch.full((B, T, H, D), W.SENTINEL_16 - 65536, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dv = dk.clone()
+    one = lambda v: torch.tensor([v], dtype=torch.float32, device="cuda")  # noqa: E731
+    say(f"dequant HND sweep geom={geom} seed={seed} T={T}")
+    K.kv_dequantize_paged(dev.cache, i32(bt), i32(lens), one(0.0625), one(3.0), dk, dv)
+    torch.cuda.synchronize()
+    gk_bits, gv_bits = tensor_bits(dk), tensor_bits(dv)
+    assert np.array_equal(gk_bits, ok), first_mismatch(gk_bits, ok)
+    assert np.array_equal(gv_bits, ov), first_mismatch(gv_bits, ov)
+
+
 @pytest.mark.parametrize("geom", [(16, 4, 128), (32, 8, 128)])
 def test_dequant_stacked_padded_and_empty(K, orc, geom):
     """HND page 16 x 4 heads (read head row by head row) and page 32 x 8
