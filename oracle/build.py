@@ -12,17 +12,18 @@ SRC = os.path.join(HERE, "kvfp4_oracle.c")
 LIB = os.path.join(HERE, "libkvfp4_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
+    """Compile ``src`` (by default the oracle) into ``lib``."""
     cmd = [
         "gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
         "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra", "-Wno-unused-parameter",
-        SRC, "-o", LIB + ".tmp", "-lm",
+        src, "-o", lib + ".tmp", "-lm",
     ]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
