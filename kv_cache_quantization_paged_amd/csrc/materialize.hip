@@ -132,10 +132,10 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const 
         for (int u = 0; u < kRound; ++u) {
             const uint32_t q = (uint32_t)(base + u * kThreads + tid);
             const uint32_t vq = INTERLEAVED ? (uint32_t)((h * a.ps + (t & ~3)) * nb + c * 4 + (t & 3)) : q;
-            code[0][u] = buf_load_u32x2(src[0], q * 8u);
-            sb[0][u] = buf_load_u8(sfs[0], q);
-            code[1][u] = buf_load_u32x2(src[1], q * 8u);
-            sb[1][u] = buf_load_u8(sfs[1], vq);
+            code[0][u] = buf_load_u32x2_nt(src[0], q * 8u);
+            sb[0][u] = buf_load_u8_nt(sfs[0], q);
+            code[1][u] = buf_load_u32x2_nt(src[1], q * 8u);
+            sb[1][u] = buf_load_u8_nt(sfs[1], vq);
             if (INTERLEAVED) {
                 c += c_step;
                 const int carry = c >= nb;
