@@ -19,6 +19,11 @@
 // online softmax for the G (<= 16) query heads of its kv head. The waves
 // merge in LDS and write (max, sum, unnormalised output) to the caller's
 // workspace; a second kernel merges the splits of each (request, kv head).
+// On NHD pools (a token's heads interleaved, so one head's row is 64 bytes
+// every H rows) the waves instead fetch whole row pieces with 16-byte loads in
+// lane order and permute them into operand order through a per-wave LDS
+// buffer; a tile then holds 18 registers instead of 26, which leaves room to
+// issue the next item's first tile before the merge.
 //
 // Both products run on v_mfma_f32_16x16x32_f16 (A 16x32, B 32x16; lane l
 // holds A[l%16][8(l/16)..+8], B[8(l/16)..+8][l%16], D[4(l/16)..+4][l%16]):
@@ -156,6 +161,75 @@ struct LaneOffsets {
     uint32_t k, ks, v, vs;
 };
 
+// one tile as the staged loader fetches it: K and V in row pieces (token
+// 16 eta + l / 4, bytes 16 (l % 4) .. + 16), their scales one dword per lane
+// (token l / 2, bytes 4 (l % 2) .. + 4)
+struct RawTile {
+    u32x4 kw[2];
+    uint32_t ksw;
+    u32x4 vw[2];
+    uint32_t vsw;
+};
+
+// a wave's LDS buffer: V rows [32 tokens][80 bytes], V scales [8 blocks][32
+// tokens], then K rows [32][80] and K scales [32][8]. The 80-byte pitch puts
+// the operand-order reads on 64 distinct banks.
+constexpr int kVPitch = 80;
+constexpr int kKOff = 32 * kVPitch + 32 * (kD / 16);
+constexpr int kVtBytes = 2 * kKOff;
+
+__device__ __forceinline__ void load_tile_staged(const AttnArgs &a, const int64_t page[2], const int row0[2],
+                                               const LaneOffsets &o, int l, RawTile &r)
+{
+    const uint8_t *vs_half[2], *ks_half[2];
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) {
+        const uint8_t *kd = a.data[0] + page[eta] * a.stride[0] + (int64_t)row0[eta] * (kD / 2);
+        ks_half[eta] = a.sf[0] + page[eta] * a.sf_stride[0] + (int64_t)row0[eta] * (kD / 16);
+        const uint8_t *vd = a.data[1] + page[eta] * a.stride[1] + (int64_t)row0[eta] * (kD / 2);
+        vs_half[eta] = a.sf[1] + page[eta] * a.sf_stride[1] + (int64_t)row0[eta] * (kD / 16);
+        r.kw[eta] = *(const u32x4 *)(kd + o.v);
+        r.vw[eta] = *(const u32x4 *)(vd + o.v);
+    }
+    r.ksw = *(const uint32_t *)((l < 32 ? ks_half[0] : ks_half[1]) + o.vs);
+    r.vsw = *(const uint32_t *)((l < 32 ? vs_half[0] : vs_half[1]) + o.vs);
+}
+
+// a staged tile into this wave's LDS buffer, from which K (per lane: token
+// 16 eta + n, channels 32 qg ..) and V (chunk n of the tokens
+// 16 (i / 4) + 4 qg + i % 4) are read back in MFMA operand order. One wave's
+// LDS operations complete in issue order, so only the compiler has to be
+// kept from moving them across each other.
+__device__ __forceinline__ void stage_tile(const RawTile &r, uint8_t *vt, int l)
+{
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) {
+        *(u32x4 *)(vt + (16 * eta + (l >> 2)) * kVPitch + 16 * (l & 3)) = r.vw[eta];
+        *(u32x4 *)(vt + kKOff + (16 * eta + (l >> 2)) * kVPitch + 16 * (l & 3)) = r.kw[eta];
+    }
+    // V scales block-major ([block][token]), so that two tokens' bytes of a
+    // block are one 16-bit read
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        vt[32 * kVPitch + (4 * (l & 1) + j) * 32 + (l >> 1)] = (uint8_t)(r.vsw >> (8 * j));
+    *(uint32_t *)(vt + kKOff + 32 * kVPitch + 4 * l) = r.ksw;
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void read_v(const uint8_t *vt, int n, int qg, uint32_t vc[8], uint32_t vsp[4])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int T = 16 * (i >> 2) + 4 * qg + (i & 3);
+        vc[i] = *(const uint32_t *)(vt + T * kVPitch + 4 * n);
+    }
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2)
+        vsp[i2] = *(const uint16_t *)(vt + 32 * kVPitch + (n >> 1) * 32 + 16 * (i2 >> 1) + 4 * qg + 2 * (i2 & 1));
+    asm volatile("" ::: "memory");
+}
+
+
 // page size a multiple of 16: each 16-token half of a tile lies in one page,
 // so a half is a scalar base (page, first slot) plus per-lane constants.
 __device__ __forceinline__ void load_half_fast(const AttnArgs &a, int64_t page, int row0, const LaneOffsets &o,
@@ -204,18 +278,11 @@ __device__ __forceinline__ void load_tile_any(const AttnArgs &a, const int *page
 }
 
 // one 32-token tile: scores, online softmax update, value product
-template <bool first>
-__device__ __forceinline__ void attend_tile(TileLoads cur, const f16x8 qv[4], int t0, int len, int qg, float c,
+template <bool first, class VFetch>
+__device__ __forceinline__ void attend_tile(TileLoads cur, VFetch fetch_v, const f16x8 qv[4], int t0, int len, int qg, float c,
                                             float &m_run, float &l_run, f32x4 o[8])
 {
     const bool partial = t0 + kTile > len;           // wave-uniform
-    if (partial) {
-        // a masked token's V scale becomes 0 so that its (finite) codes add
-        // nothing; its score becomes -inf below
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            cur.vs[i] = t0 + 16 * (i >> 2) + 4 * qg + (i & 3) < len ? cur.vs[i] : 0u;
-    }
 
     // ---- scores: S^T[16 eta + 4 qg + i][n]
     float s[8];
@@ -266,13 +333,24 @@ __device__ __forceinline__ void attend_tile(TileLoads cur, const f16x8 qv[4], in
                               pack_f16x2(p[6], p[7]));
     // token pair i2 = (2 i2, 2 i2 + 1): byte b of ev[i2] holds channel 2b of both
     // tokens (low nibble: the first), od[i2] channel 2b + 1; ss[i2] = their scales
+    uint32_t vc[8], vsp[4];
+    fetch_v(vc, vsp);
+    if (partial) {
+        // a masked token's V scale becomes 0 so that its (finite) codes add
+        // nothing; its score is -inf
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            const int T = t0 + 16 * (i2 >> 1) + 4 * qg + 2 * (i2 & 1);
+            vsp[i2] = (T < len ? vsp[i2] & 0xFFu : 0u) | (T + 1 < len ? vsp[i2] & 0xFF00u : 0u);
+        }
+    }
     uint32_t ev[4], od[4], ss[4];
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) {
-        const uint32_t wa = cur.vc[2 * i2], wb = cur.vc[2 * i2 + 1];
+        const uint32_t wa = vc[2 * i2], wb = vc[2 * i2 + 1];
         ev[i2] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
         od[i2] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
-        ss[i2] = fp8x2_f16(cur.vs[2 * i2] | (cur.vs[2 * i2 + 1] << 8));
+        ss[i2] = fp8x2_f16(vsp[i2]);
     }
     // one channel (MFMA) at a time keeps few decoded words live
 #define KVFP4_PV(J, SRC, SEL)                                                                                   \
@@ -417,10 +495,17 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
         for (int k = 0; k < kWaveTiles; ++k) {
             const int t0 = t_w + kTile * k;
             if (t0 < len) {
+                const TileLoads &tl = ld[k & 1];
+                auto fv = [&](uint32_t *vc, uint32_t *vsp) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) vc[i] = tl.vc[i];
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) vsp[i2] = tl.vs[2 * i2] | (tl.vs[2 * i2 + 1] << 8);
+                };
                 if (k == 0)
-                    attend_tile<true>(ld[k & 1], qv, t0, len, qg, c, m_run, l_run, o);
+                    attend_tile<true>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o);
                 else
-                    attend_tile<false>(ld[k & 1], qv, t0, len, qg, c, m_run, l_run, o);
+                    attend_tile<false>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o);
             }
             if (k + 2 < kWaveTiles)
                 issue(k + 2);
@@ -466,6 +551,179 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
     __syncthreads();                                   // LDS is reused by the next item
 }
 
+// staged loader, one tile: tile k of wave w in item it = (b, split, h, len)
+// into r; false (nothing issued) when the wave has no tokens there. A half
+// past the end reads the wave's first half (masked later).
+__device__ __forceinline__ bool issue_staged(const AttnArgs &a, const int32_t *__restrict__ bt, int4 it, int w, int k,
+                                           const LaneOffsets &lo, int l, RawTile &r)
+{
+    const int t_w = it.y * kSplitTokens + w * (kTile * kWaveTiles);
+    const int t0 = t_w + kTile * k;
+    if (t0 >= it.w)
+        return false;
+    const int32_t *row_bt = bt + (int64_t)it.x * a.bt_row_stride;
+    int64_t pg[2];
+    int rw[2];
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) {
+        const int t = t0 + 16 * eta < it.w ? t0 + 16 * eta : t_w;
+        const int pi = t / a.ps;
+        pg[eta] = row_bt[pi];
+        rw[eta] = (t - pi * a.ps) * a.tok_rows + it.z * a.head_rows;
+    }
+    load_tile_staged(a, pg, rw, lo, l, r);
+    return true;
+}
+
+// the query rows of item it into fp16 MFMA operands and the score factor
+template <bool BF16>
+__device__ __forceinline__ float load_query(const AttnArgs &a, const float *__restrict__ k_scale, int b, int h, int n,
+                                            int qg, f16x8 qv[4])
+{
+    u32x4 qraw[4];
+    const bool live = n < a.G;
+    const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.G + (live ? n : 0)) * kD + 32 * qg;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qraw[k] = live ? *(const u32x4 *)(qrow + 8 * k) : u32x4{0u, 0u, 0u, 0u};
+    float c = a.sm_scale_log2 * *k_scale;
+    if (BF16) {
+        uint32_t mx = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t v = qraw[k][e] & 0x7FFF7FFFu;
+                mx = max(mx, max(v & 0xFFFFu, v >> 16));
+            }
+        mx = max4_u32(mx);
+        const int E = max((int)(mx >> 7), 1);
+        int ec;
+        (void)frexpf(c, &ec);
+        const int kk = min(max(141 - E, ec - 126), ec + 125);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            u32x4 o16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o16[e] = pack_f16x2(ldexpf(bf16_bits_lo(qraw[k][e]), kk), ldexpf(bf16_bits_hi(qraw[k][e]), kk));
+            qv[k] = __builtin_bit_cast(f16x8, o16);
+        }
+        c = ldexpf(c, -kk);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qv[k] = __builtin_bit_cast(f16x8, qraw[k]);
+    }
+    return c;
+}
+
+// one work item on the staged loader. pre holds this wave's first tile of the
+// item when have_pre is set; the first tile of the next item (if any) is
+// issued into pre before the merge, so that its loads are in flight through
+// the merge and the next item's start.
+template <bool BF16>
+__device__ __forceinline__ void attend_item_fast(const AttnArgs &a, const int32_t *__restrict__ bt,
+                                                 const float *__restrict__ k_scale, int4 it, int4 next, bool has_next,
+                                                 RawTile &pre, bool &have_pre, float (*red_m)[16],
+                                                 float (*red_l)[16], float *red_o, uint8_t *vt_all)
+{
+    // the thread index through an opaque move, so that the lane-dependent
+    // addresses below are recomputed per item rather than held in registers
+    // across the item loop
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int l = tid & 63, n = l & 15, qg = l >> 4;
+    LaneOffsets lo;
+    {
+        const uint32_t tr = (uint32_t)a.tok_rows;
+        lo.k = 0;
+        lo.ks = 0;
+        lo.v = (l >> 2) * tr * (kD / 2) + 16 * (l & 3);
+        lo.vs = ((l & 31) >> 1) * tr * (kD / 16) + 4 * (l & 1);
+    }
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = it.x, split = it.y, h = it.z, len = it.w;
+    const int t_w = split * kSplitTokens + w * (kTile * kWaveTiles);
+    uint8_t *vt = vt_all + w * kVtBytes;
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    bool have_next = false;
+    auto issue_next = [&]() { have_next = has_next && issue_staged(a, bt, next, w, 0, lo, l, pre); };
+    auto stage_k = [&](const RawTile &r, TileLoads &cur) {
+        stage_tile(r, vt, l);
+#pragma unroll
+        for (int eta = 0; eta < 2; ++eta) {
+            cur.kc[eta] = *(const u32x4 *)(vt + kKOff + (16 * eta + n) * kVPitch + 16 * qg);
+            cur.ks[eta] = *(const uint16_t *)(vt + kKOff + 32 * kVPitch + (16 * eta + n) * (kD / 16) + 2 * qg);
+        }
+    };
+    auto fv = [&](uint32_t *vc, uint32_t *vs) { read_v(vt, n, qg, vc, vs); };
+
+    if (t_w < len) {
+        if (!have_pre)
+            issue_staged(a, bt, it, w, 0, lo, l, pre);
+        RawTile r1;
+        const bool two = issue_staged(a, bt, it, w, 1, lo, l, r1);
+        f16x8 qv[4];
+        const float c = load_query<BF16>(a, k_scale, b, h, n, qg, qv);
+        {
+            TileLoads cur;
+            stage_k(pre, cur);
+            if (!two)
+                issue_next();
+            attend_tile<true>(cur, fv, qv, t_w, len, qg, c, m_run, l_run, o);
+        }
+        if (two) {
+            TileLoads cur;
+            stage_k(r1, cur);
+            issue_next();
+            attend_tile<false>(cur, fv, qv, t_w + kTile, len, qg, c, m_run, l_run, o);
+        }
+    } else {
+        issue_next();
+    }
+    have_pre = have_next;
+
+    if (qg == 0) {
+        red_m[w][n] = m_run;
+        red_l[w][n] = l_run;
+    }
+    if (n < a.G) {
+        float *orow = red_o + (w * a.G + n) * kD + 32 * qg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *(f32x4 *)(orow + 8 * i) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+            *(f32x4 *)(orow + 8 * i + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+        }
+    }
+    __syncthreads();
+    const int pf = partial_floats(a.G);
+    float *ws = a.ws + (((int64_t)b * a.H + h) * a.splits + split) * pf;
+    for (int idx = tid; idx < a.G * (kD / 4); idx += 64 * kWaves) {
+        const int g = idx / (kD / 4), d0 = (idx - g * (kD / 4)) * 4;
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, red_m[v][g]);
+        float L = 0.0f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const float f = __builtin_amdgcn_exp2f(red_m[v][g] - M);
+            L += red_l[v][g] * f;
+            acc += *(const f32x4 *)(red_o + (v * a.G + g) * kD + d0) * f;
+        }
+        if (d0 == 0) {
+            ws[g] = M;
+            ws[a.G + g] = L;
+        }
+        *(f32x4 *)(ws + 2 * a.G + g * kD + d0) = acc;
+    }
+    __syncthreads();
+}
+
 // block-wide exclusive prefix sum of one int per thread (blockDim 64 * kWaves)
 __device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot, int &total)
 {
@@ -499,12 +757,20 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot, int &t
 // under the round-robin dispatch), and the H heads of a group go to H
 // workgroups of that XCD in the same round, so a page's lines shared by
 // several heads (NHD rows, scale rows) are fetched into one L2 once.
-template <bool BF16, bool FAST16>
+// Loaders: kAnyPage (per-token page ids from LDS), kDirect (page size a
+// multiple of 16, the lanes gather their operands straight from the page)
+// and kStaged (the same page sizes, NHD: whole row pieces through LDS, and
+// each item's first tile issued before the previous item's merge; measured
+// 3.5% faster than kDirect on NHD pools and 8% slower on HND pools, whose
+// head runs the direct gathers already read contiguously).
+constexpr int kAnyPage = 0, kDirect = 1, kStaged = 2;
+template <bool BF16, int LOADER>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void attention_split_kernel(AttnArgs a, const int32_t *__restrict__ bt,
                                                                       const int32_t *__restrict__ seq_lens,
                                                                       const float *__restrict__ k_scale)
 {
-    __shared__ int pages[FAST16 ? 1 : kMaxPagesPerSplit];
+    __shared__ int pages[LOADER == kAnyPage ? kMaxPagesPerSplit : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t vt[LOADER == kStaged ? kWaves * kVtBytes : 16];
     __shared__ float red_m[kWaves][16], red_l[kWaves][16];
     __shared__ int wave_tot[kWaves];
     __shared__ int4 items[64 * kWaves];              // (b, split, h, len)
@@ -556,9 +822,20 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
         }
         __syncthreads();
         const int count = (int)min((int64_t)nthr, (nix - base + per_xcd - 1) / per_xcd);
-        for (int t = 0; t < count; ++t) {
-            const int4 it = items[t];
-            attend_item<BF16, FAST16>(a, bt, k_scale, it.x, it.z, it.y, it.w, pages, red_m, red_l, red_o);
+        if constexpr (LOADER == kStaged) {
+            RawTile pre;                                 // this wave's first tile of the next item
+            bool have_pre = false;
+            for (int t = 0; t < count; ++t) {
+                const int4 nx = items[t + 1 < count ? t + 1 : t];
+                attend_item_fast<BF16>(a, bt, k_scale, items[t], nx, t + 1 < count, pre, have_pre, red_m, red_l,
+                                       red_o, vt);
+            }
+        } else {
+            for (int t = 0; t < count; ++t) {
+                const int4 it = items[t];
+                attend_item<BF16, LOADER == kDirect>(a, bt, k_scale, it.x, it.z, it.y, it.w, pages, red_m, red_l,
+                                                     red_o);
+            }
         }
     }
 }
@@ -659,9 +936,13 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
     if (bh == 0)
         return hipSuccess;
     typedef void (*split_fn)(AttnArgs, const int32_t *, const int32_t *, const float *);
-    const bool fast = c.page_size % 16 == 0;
-    const split_fn kernel = bf16 ? (fast ? attention_split_kernel<true, true> : attention_split_kernel<true, false>)
-                                 : (fast ? attention_split_kernel<false, true> : attention_split_kernel<false, false>);
+    const int loader = c.page_size % 16 != 0 ? kAnyPage : (c.layout == KVFP4_NHD ? kStaged : kDirect);
+    const split_fn kernels[2][3] = {
+        {attention_split_kernel<false, kAnyPage>, attention_split_kernel<false, kDirect>,
+         attention_split_kernel<false, kStaged>},
+        {attention_split_kernel<true, kAnyPage>, attention_split_kernel<true, kDirect>,
+         attention_split_kernel<true, kStaged>}};
+    const split_fn kernel = kernels[bf16 ? 1 : 0][loader];
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess)
