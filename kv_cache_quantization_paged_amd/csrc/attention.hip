@@ -555,7 +555,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
 // into r; false (nothing issued) when the wave has no tokens there. A half
 // past the end reads the wave's first half (masked later).
 __device__ __forceinline__ bool issue_staged(const AttnArgs &a, const int32_t *__restrict__ bt, int4 it, int w, int k,
-                                           const LaneOffsets &lo, int l, RawTile &r)
+                                             const LaneOffsets &lo, int l, RawTile &r)
 {
     const int t_w = it.y * kSplitTokens + w * (kTile * kWaveTiles);
     const int t0 = t_w + kTile * k;
@@ -621,10 +621,10 @@ __device__ __forceinline__ float load_query(const AttnArgs &a, const float *__re
 // issued into pre before the merge, so that its loads are in flight through
 // the merge and the next item's start.
 template <bool BF16>
-__device__ __forceinline__ void attend_item_fast(const AttnArgs &a, const int32_t *__restrict__ bt,
-                                                 const float *__restrict__ k_scale, int4 it, int4 next, bool has_next,
-                                                 RawTile &pre, bool &have_pre, float (*red_m)[16],
-                                                 float (*red_l)[16], float *red_o, uint8_t *vt_all)
+__device__ __forceinline__ void attend_item_staged(const AttnArgs &a, const int32_t *__restrict__ bt,
+                                                   const float *__restrict__ k_scale, int4 it, int4 next, bool has_next,
+                                                   RawTile &pre, bool &have_pre, float (*red_m)[16],
+                                                   float (*red_l)[16], float *red_o, uint8_t *vt_all)
 {
     // the thread index through an opaque move, so that the lane-dependent
     // addresses below are recomputed per item rather than held in registers
@@ -827,8 +827,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
             bool have_pre = false;
             for (int t = 0; t < count; ++t) {
                 const int4 nx = items[t + 1 < count ? t + 1 : t];
-                attend_item_fast<BF16>(a, bt, k_scale, items[t], nx, t + 1 < count, pre, have_pre, red_m, red_l,
-                                       red_o, vt);
+                attend_item_staged<BF16>(a, bt, k_scale, items[t], nx, t + 1 < count, pre, have_pre, red_m,
+                                         red_l, red_o, vt);
             }
         } else {
             for (int t = 0; t < count; ++t) {
