@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const 
             }
 #pragma unroll
             for (int kv = 0; kv < 2; ++kv) {
-                code[kv][u] = buf_load_u32(src[kv], oc);
+                code[kv][u] = buf_load_u32_nt(src[kv], oc);
                 sbyte[kv][u] = buf_load_u8(sfs[kv], os);
             }
         }

@@ -183,10 +183,15 @@ __device__ __forceinline__ void buf_store_u32x4_nt(u32x4 v, rsrc_t r, uint32_t o
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStreamStore);
 }
-// non-temporal loads of bytes read once. They help only the materialize
-// stream (0.6%); the dequant streams lose 2% (NHD) and 6% (LDS-staged HND)
-// with them, so those keep the default policy.
+// non-temporal loads of bytes read once. Measured on the materialize loads
+// (+0.6%) and on the gather dequant's code bytes (+1.8%); the same hint on the
+// dequant's scale bytes (whose lines several lanes and items share) cost
+// 2.5%, and on the LDS-staged HND dequant 6%, so those keep the default.
 constexpr int kStreamLoad = 2;           // cache-policy bits: nt
+__device__ __forceinline__ uint32_t buf_load_u32_nt(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kStreamLoad);
+}
 __device__ __forceinline__ uint32_t buf_load_u8_nt(rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, kStreamLoad);
