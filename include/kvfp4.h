@@ -262,6 +262,10 @@ kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const v
  * over t < seq_lens[b], K and V decoded from the cache (page
  * block_tables[b * bt_row_stride + t / page_size], slot t % page_size) times
  * *k_scale / *v_scale (device fp32). A request of length 0 gives zeros.
+ * Lengths are values and are not checked on the host; the kernels cut a
+ * length to the bt_cols * page_size tokens its table row addresses and treat
+ * a negative one as 0, so no access leaves the caller's buffers and a bad
+ * length changes only its own request's output.
  * q and out are [batch_size, num_qo_heads, 128] of q_dtype (bf16 or fp16),
  * contiguous, 16-byte aligned; block_tables and seq_lens int32. head_dim
  * must be 128 and num_qo_heads / num_kv_heads at most 16

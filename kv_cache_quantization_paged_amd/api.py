@@ -34,7 +34,7 @@ CacheArg = Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]
 class NVFP44Over6Config:
     """4over6 block-scale recipe: e4m3_max (256 by default), err_mode "MSE"
     or "MAE". ``err_use_fast_math=True`` evaluates the candidates' error in
-    fp16 (a distinct recipe on the page: near-ties can go the other way)."""
+    fp16 (a distinct recipe: fp16 scoring can reverse a close decision)."""
     e4m3_max: float = 256.0
     err_mode: str = "MSE"
     err_use_fast_math: bool = False
@@ -47,7 +47,7 @@ class NVFP44Over6Config:
 
 
 def nvfp4_e4m3_max(nvfp4_4over6_config: Optional[NVFP44Over6Config] = None) -> float:
-    """E4M3 block-scale clamp implied by a resolved recipe (448 when None)."""
+    """The clamp a recipe puts on its E4M3 block scales (448 for standard NVFP4)."""
     return 448.0 if nvfp4_4over6_config is None else float(nvfp4_4over6_config.e4m3_max)
 
 

@@ -79,9 +79,15 @@ struct AttnArgs {
     int32_t tok_rows;         // rows between consecutive tokens of a page (HND 1, NHD H)
     int32_t head_rows;        // rows between consecutive kv heads of a page (HND ps, NHD 1)
     int32_t splits;           // per (request, kv head)
+    int32_t max_len;          // bt_cols * page_size (capped at INT32_MAX): longer lengths are cut to it
     int32_t batch;            // requests of this launch (bt, seq_lens, q and ws start at its first)
     float sm_scale_log2;      // sm_scale * log2(e)
 };
+
+// a request's length as the kernels use it: negative lengths count as 0 and
+// lengths past the table row are cut to it, so every access stays inside the
+// caller's buffers whatever the lengths hold
+__device__ __forceinline__ int clamp_len(int len, int max_len) { return max(0, min(len, max_len)); }
 
 // floats per partial result of a split: max and sum per query head, then the
 // unnormalised output rows [G][128]
@@ -784,7 +790,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
     int mine = 0;
     for (int k = 0; k < per; ++k) {
         const int bb = tid * per + k;
-        mine += bb < a.batch ? (seq_lens[bb] + kSplitTokens - 1) / kSplitTokens : 0;
+        mine += bb < a.batch ? (clamp_len(seq_lens[bb], a.max_len) + kSplitTokens - 1) / kSplitTokens : 0;
     }
     int total;
     int run = block_exclusive_scan(mine, wave_tot, total);
@@ -792,7 +798,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
         const int bb = tid * per + k;
         if (bb < a.batch) {
             cum[bb] = run;
-            run += (seq_lens[bb] + kSplitTokens - 1) / kSplitTokens;
+            run += (clamp_len(seq_lens[bb], a.max_len) + kSplitTokens - 1) / kSplitTokens;
         }
     }
     if (tid == 0)
@@ -818,7 +824,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
                 else
                     hi = mid;
             }
-            items[tid] = int4{lo, g - cum[lo], h, seq_lens[lo]};
+            items[tid] = int4{lo, g - cum[lo], h, clamp_len(seq_lens[lo], a.max_len)};
         }
         __syncthreads();
         const int count = (int)min((int64_t)nthr, (nix - base + per_xcd - 1) / per_xcd);
@@ -851,8 +857,8 @@ __global__ __launch_bounds__(512) void attention_merge_kernel(AttnArgs a, const 
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int g = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
-    const int len = seq_lens[b];
-    const int live = min(a.splits, (len + kSplitTokens - 1) / kSplitTokens);
+    const int len = clamp_len(seq_lens[b], a.max_len);
+    const int live = (len + kSplitTokens - 1) / kSplitTokens;
     const int pf = partial_floats(a.G);
     const float *ws = a.ws + (int64_t)bh * a.splits * pf;
     float M = -INFINITY, L = 0.0f;
@@ -931,6 +937,10 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
     a.tok_rows = c.layout == KVFP4_HND ? 1 : c.num_kv_heads;
     a.head_rows = c.layout == KVFP4_HND ? c.page_size : 1;
     a.splits = (int32_t)decode_attention_splits(bt_cols, c.page_size);
+    // a length past the table row would read other rows' (or no) page ids:
+    // such requests are cut to the tokens their row can address
+    const int64_t row_tokens = (int64_t)bt_cols * c.page_size;
+    a.max_len = (int32_t)(row_tokens < INT32_MAX ? row_tokens : INT32_MAX);
     a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
     const int64_t bh = (int64_t)batch * c.num_kv_heads;
     if (bh == 0)

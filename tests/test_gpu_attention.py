@@ -160,3 +160,47 @@ def test_attention_sm_scale_edge_values(K, orc, sm):
 def test_attention_split_boundaries(K, orc):
     """lengths at and next to the 256-token split and 64-token wave edges"""
     run_case(K, orc, 670, W.NHD, 16, 2, 4, [256, 512, 768, 255, 511, 64, 65, 192, 193], True)
+
+
+def test_attention_lengths_outside_the_table(K, orc):
+    """seq_lens past what a table row addresses (bt_cols * page_size) or
+    negative are values the host does not check: the kernels cut them to the
+    row (and to 0), so every read stays in the caller's buffers and the other
+    requests' outputs are exactly those of a call with in-range lengths"""
+    rng = np.random.default_rng(680)
+    ps, H, G, D, maxp = 16, 2, 4, 128, 5
+    B = 6
+    P = B * maxp + 3
+    cache, gk, gv = quantized_cache(orc, rng, P, ps, H, D, W.NHD)
+    bt = rng.permutation(P)[:B * maxp].reshape(B, maxp).astype(np.int32)
+    good = np.array([70, 80, 33, 1, 80, 17], np.int32)
+    bad = good.copy()
+    bad[1] = 100_000                       # past the row's 80 tokens (and the workspace's splits)
+    bad[3] = -7
+    bad[4] = 81
+    q = W.f32_to_bits(W.normal_rows(rng, (B, H * G, D)), True)
+    dev = DeviceCache(cache)
+    ws_bytes = K.kv_decode_attention_workspace_size(B, H, H * G, maxp, ps)
+    outs = []
+    for lens in (good, bad):
+        say(f"attention lengths outside the table: {list(lens)}")
+        out = torch.full((B, H * G, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+        K.kv_decode_attention(dev.cache, bits_tensor(q, True), i32(bt), i32(lens), torch.tensor([gk], device="cuda"),
+                              torch.tensor([gv], device="cuda"), 1.0 / np.sqrt(D), out, ws)
+        outs.append(tensor_bits(out))
+    want_cut = good.copy()
+    want_cut[3] = 0                         # the negative length counts as 0
+    assert np.array_equal(outs[1][[0, 2, 5]], outs[0][[0, 2, 5]])
+    assert np.array_equal(outs[1][1], outs[0][1]) and np.array_equal(outs[1][4], outs[0][4])
+    assert np.all(outs[1][3] == 0)
+    sel = np.array([0, 1, 2, 4, 5])
+    want = orc.decode_attention(cache, q[sel], True, bt[sel], want_cut[sel], gk, gv,
+                                float(np.float32(1.0 / np.sqrt(D))), threads=oracle_threads())
+    got = outs[1].view(np.int16).view(np.uint16).astype(np.uint32) << 16
+    got = got.view(np.float32).astype(np.float64)[sel]
+    for k_, b in enumerate(sel):
+        for hq in range(H * G):
+            vmax = max_abs_v(cache, bt, want_cut, gv, b, hq // G)
+            err = np.abs(got[k_, hq] - want[k_, hq])
+            assert np.all(err <= 2 * 2.0 ** -9 * (vmax + np.abs(want[k_, hq]))), (b, hq)

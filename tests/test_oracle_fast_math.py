@@ -1,7 +1,7 @@
 """Pins for the oracle's fp16 error evaluation of the 4over6 search
 ("err_use_fast_math", flashinfer.quantization module page, "NVFP4 4over6
-Recipes": the error is evaluated in fp16 instead of exactly in fp32, and on
-near-ties it can select the other candidate).
+Recipes": the candidates' errors are scored in fp16 rather than in exact
+fp32, so a close decision between the two candidates can come out reversed).
 
 Reading pinned here: the input and the fp32 reconstruction are rounded to
 fp16, then the difference, the square (MSE) and every pairwise sum are each
