@@ -56,7 +56,8 @@ enum {
     KVFP4_EINVAL = 1,        /* null pointer, bad enum, bad extent or scale */
     KVFP4_EALIGN = 2,        /* a base pointer or stride is not 16-byte aligned */
     KVFP4_EUNSUPPORTED = 3,  /* a valid request the library does not implement */
-    KVFP4_ELAUNCH = 4        /* the HIP runtime refused a launch */
+    KVFP4_ELAUNCH = 4,       /* the HIP runtime refused a launch */
+    KVFP4_ESCRATCH = 5       /* a no-allocation call needs more than its fixed scratch */
 };
 
 enum { KVFP4_NHD = 0, KVFP4_HND = 1 };                /* cache layouts */
@@ -291,6 +292,27 @@ kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void 
  * invalid sizes). */
 int64_t kv_decode_attention_workspace_size(int32_t batch_size, int32_t num_kv_heads, int32_t num_qo_heads,
                                            int32_t bt_cols, int32_t page_size);
+
+/*
+ * kv_decode_attention_noalloc - kv_decode_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc): the same arguments, kernels and result,
+ * without the workspace. The split partials go to a fixed device array of
+ * KVFP4_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; the call allocates and frees nothing. Calls whose partials
+ * (kv_decode_attention_workspace_size of the same sizes) exceed that size
+ * return KVFP4_ESCRATCH before anything is queued. Every call on a GPU uses
+ * that GPU's one array: calls whose stream work overlaps on the same GPU
+ * (other streams, other host threads) race and must be serialized by the
+ * caller; calls in order on one stream are safe. The array needs no initial
+ * contents (each call writes every partial it reads).
+ */
+#define KVFP4_NOALLOC_SCRATCH_BYTES (32ll << 20)
+kvfp4_status_t kv_decode_attention_noalloc(const kvfp4_paged_cache_t *cache, const void *q, int32_t q_dtype,
+                                           int32_t num_qo_heads, const int32_t *block_tables,
+                                           int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
+                                           int32_t batch_size, const float *k_scale, const float *v_scale,
+                                           float sm_scale, void *out, void *stream);
 
 /* Static description of a status code. */
 const char *kvfp4_status_string(kvfp4_status_t status);

@@ -16,7 +16,8 @@ import torch  # loads the HIP runtime that the library then shares
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libkvfp4.so")
 
-KVFP4_OK, KVFP4_EINVAL, KVFP4_EALIGN, KVFP4_EUNSUPPORTED, KVFP4_ELAUNCH = 0, 1, 2, 3, 4
+KVFP4_OK, KVFP4_EINVAL, KVFP4_EALIGN, KVFP4_EUNSUPPORTED, KVFP4_ELAUNCH, KVFP4_ESCRATCH = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 32 << 20      # KVFP4_NOALLOC_SCRATCH_BYTES
 KVFP4_NHD, KVFP4_HND = 0, 1
 KVFP4_F16, KVFP4_BF16 = 0, 1
 KVFP4_I32, KVFP4_I64 = 0, 1
@@ -24,7 +25,7 @@ KVFP4_ERR_MSE, KVFP4_ERR_MAE = 0, 1
 
 EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
             "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
-            "kv_decode_attention_workspace_size", "kvfp4_status_string")
+            "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc", "kvfp4_status_string")
 
 
 class PagedCacheDesc(C.Structure):
@@ -84,6 +85,9 @@ def load_library():
     lib.kv_decode_attention.restype = i32
     lib.kv_decode_attention.argtypes = [C.POINTER(PagedCacheDesc), P, i32, i32, P, i64, i32, P, i32, P, P, f32, P, P,
                                         i64, P]
+    lib.kv_decode_attention_noalloc.restype = i32
+    lib.kv_decode_attention_noalloc.argtypes = [C.POINTER(PagedCacheDesc), P, i32, i32, P, i64, i32, P, i32, P, P,
+                                                f32, P, P]
     lib.kv_decode_attention_workspace_size.restype = i64
     lib.kv_decode_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.kvfp4_status_string.restype = C.c_char_p
@@ -356,12 +360,7 @@ def kv_decode_attention_workspace_size(batch: int, num_kv_heads: int, num_qo_hea
                                                                  page_size))
 
 
-def kv_decode_attention(cache: PagedCache, q, block_tables, seq_lens, k_scale, v_scale, sm_scale: float, out,
-                        workspace, stream=None):
-    """q, out [batch, num_qo_heads, head_dim] bf16/fp16; block_tables int32
-    [batch, max_pages]; k_scale / v_scale 1-element float32 CUDA tensors;
-    workspace a CUDA byte tensor of kv_decode_attention_workspace_size()."""
-    lib = load_library()
+def _attention_args(cache: PagedCache, q, block_tables, seq_lens, k_scale, v_scale, out):
     _need_i32(seq_lens, "seq_lens")
     _need_scale(k_scale, "k_scale")
     _need_scale(v_scale, "v_scale")
@@ -376,8 +375,28 @@ def kv_decode_attention(cache: PagedCache, q, block_tables, seq_lens, k_scale, v
     B = q.shape[0]
     if block_tables.shape[0] != B or seq_lens.numel() != B:
         raise ValueError("batch sizes disagree")
-    st = lib.kv_decode_attention(C.byref(cache.desc), _ptr(q), _half_enum(q.dtype), q.shape[1], _ptr(block_tables),
-                                 _stride(block_tables, 0), block_tables.shape[1], _ptr(seq_lens), B, _ptr(k_scale),
-                                 _ptr(v_scale), float(sm_scale), _ptr(out), _ptr(workspace),
+    return (C.byref(cache.desc), _ptr(q), _half_enum(q.dtype), q.shape[1], _ptr(block_tables), _stride(block_tables, 0),
+            block_tables.shape[1], _ptr(seq_lens), B, _ptr(k_scale), _ptr(v_scale))
+
+
+def kv_decode_attention(cache: PagedCache, q, block_tables, seq_lens, k_scale, v_scale, sm_scale: float, out,
+                        workspace, stream=None):
+    """q, out [batch, num_qo_heads, head_dim] bf16/fp16; block_tables int32
+    [batch, max_pages]; k_scale / v_scale 1-element float32 CUDA tensors;
+    workspace a CUDA byte tensor of kv_decode_attention_workspace_size()."""
+    lib = load_library()
+    args = _attention_args(cache, q, block_tables, seq_lens, k_scale, v_scale, out)
+    st = lib.kv_decode_attention(*args, float(sm_scale), _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "kv_decode_attention")
+
+
+def kv_decode_attention_noalloc(cache: PagedCache, q, block_tables, seq_lens, k_scale, v_scale, sm_scale: float, out,
+                                stream=None):
+    """kv_decode_attention without a workspace: the partials live in the
+    library's fixed per-GPU scratch (NOALLOC_SCRATCH_BYTES). Calls that
+    overlap on one GPU race; calls in order on one stream do not."""
+    lib = load_library()
+    args = _attention_args(cache, q, block_tables, seq_lens, k_scale, v_scale, out)
+    st = lib.kv_decode_attention_noalloc(*args, float(sm_scale), _ptr(out), _stream(stream))
+    _check(st, "kv_decode_attention_noalloc")

@@ -247,12 +247,18 @@ kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const v
                                                 recipe, v_sf_interleaved != 0, (hipStream_t)stream));
 }
 
-kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void *q, int32_t q_dtype,
-                                   int32_t num_qo_heads, const int32_t *block_tables, int64_t bt_row_stride,
-                                   int32_t bt_cols, const int32_t *seq_lens, int32_t batch_size,
-                                   const float *k_scale, const float *v_scale, float sm_scale, void *out,
-                                   void *workspace, int64_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// the checks kv_decode_attention and kv_decode_attention_noalloc share (all
+// but the workspace); KVFP4_OK with *nothing_to_do set for an empty batch
+kvfp4_status_t check_attention(const kvfp4_paged_cache_t *cache, const void *q, int32_t q_dtype,
+                               int32_t num_qo_heads, const int32_t *block_tables, int64_t bt_row_stride,
+                               int32_t bt_cols, const int32_t *seq_lens, int32_t batch_size, const float *k_scale,
+                               const float *v_scale, float sm_scale, const void *out, bool *nothing_to_do)
 {
+    *nothing_to_do = false;
     kvfp4_status_t s = check_cache(cache);
     if (s != KVFP4_OK)
         return s;
@@ -264,25 +270,70 @@ kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void 
         return KVFP4_EINVAL;
     if (cache->head_dim != 128 || num_qo_heads / cache->num_kv_heads > 16)
         return KVFP4_EUNSUPPORTED;
-    if (batch_size == 0)
+    if (batch_size == 0) {
+        *nothing_to_do = true;
         return KVFP4_OK;
-    if (!q || !block_tables || !seq_lens || !k_scale || !v_scale || !out || bt_cols < 1 || !workspace)
+    }
+    if (!q || !block_tables || !seq_lens || !k_scale || !v_scale || !out || bt_cols < 1)
         return KVFP4_EINVAL;
     if ((int64_t)batch_size * cache->num_kv_heads * decode_attention_splits(bt_cols, cache->page_size) > INT32_MAX)
         return KVFP4_EUNSUPPORTED;
-    if (workspace_bytes < decode_attention_workspace_bytes(batch_size, cache->num_kv_heads, num_qo_heads, bt_cols,
-                                                           cache->page_size))
-        return KVFP4_EINVAL;
-    if (!aligned16(workspace))
-        return KVFP4_EALIGN;
     if (!aligned16(q) || !aligned16(out))
         return KVFP4_EALIGN;
     if ((((uintptr_t)cache->k_sf | (uintptr_t)cache->v_sf) & 1u) ||
         ((cache->k_sf_page_stride | cache->v_sf_page_stride) & 1))
         return KVFP4_EALIGN;
+    return KVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void *q, int32_t q_dtype,
+                                   int32_t num_qo_heads, const int32_t *block_tables, int64_t bt_row_stride,
+                                   int32_t bt_cols, const int32_t *seq_lens, int32_t batch_size,
+                                   const float *k_scale, const float *v_scale, float sm_scale, void *out,
+                                   void *workspace, int64_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    kvfp4_status_t s = check_attention(cache, q, q_dtype, num_qo_heads, block_tables, bt_row_stride, bt_cols,
+                                       seq_lens, batch_size, k_scale, v_scale, sm_scale, out, &empty);
+    if (s != KVFP4_OK || empty)
+        return s;
+    if (!workspace)
+        return KVFP4_EINVAL;
+    if (workspace_bytes < decode_attention_workspace_bytes(batch_size, cache->num_kv_heads, num_qo_heads, bt_cols,
+                                                           cache->page_size))
+        return KVFP4_EINVAL;
+    if (!aligned16(workspace))
+        return KVFP4_EALIGN;
     return from_hip(launch_decode_attention(*cache, q, q_dtype == KVFP4_BF16, num_qo_heads, block_tables,
                                             bt_row_stride, bt_cols, seq_lens, batch_size, k_scale, v_scale,
                                             sm_scale, out, workspace, (hipStream_t)stream));
+}
+
+kvfp4_status_t kv_decode_attention_noalloc(const kvfp4_paged_cache_t *cache, const void *q, int32_t q_dtype,
+                                           int32_t num_qo_heads, const int32_t *block_tables,
+                                           int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
+                                           int32_t batch_size, const float *k_scale, const float *v_scale,
+                                           float sm_scale, void *out, void *stream)
+{
+    bool empty = false;
+    kvfp4_status_t s = check_attention(cache, q, q_dtype, num_qo_heads, block_tables, bt_row_stride, bt_cols,
+                                       seq_lens, batch_size, k_scale, v_scale, sm_scale, out, &empty);
+    if (s != KVFP4_OK || empty)
+        return s;
+    if (decode_attention_workspace_bytes(batch_size, cache->num_kv_heads, num_qo_heads, bt_cols,
+                                         cache->page_size) > kNoAllocScratchBytes)
+        return KVFP4_ESCRATCH;
+    void *ws = nullptr;
+    hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess)
+        return KVFP4_ELAUNCH;
+    return from_hip(launch_decode_attention(*cache, q, q_dtype == KVFP4_BF16, num_qo_heads, block_tables,
+                                            bt_row_stride, bt_cols, seq_lens, batch_size, k_scale, v_scale,
+                                            sm_scale, out, ws, (hipStream_t)stream));
 }
 
 int64_t kv_decode_attention_workspace_size(int32_t batch_size, int32_t num_kv_heads, int32_t num_qo_heads,
@@ -302,6 +353,8 @@ const char *kvfp4_status_string(kvfp4_status_t status)
     case KVFP4_EALIGN: return "misaligned pointer or stride (16-byte alignment required)";
     case KVFP4_EUNSUPPORTED: return "unsupported request (sizes beyond the library's 32-bit index limits)";
     case KVFP4_ELAUNCH: return "HIP kernel launch failed (is the device gfx950?)";
+    case KVFP4_ESCRATCH: return "the call needs more than the no-allocation entry point's fixed scratch "
+                                "(KVFP4_NOALLOC_SCRATCH_BYTES); use the variant with a caller workspace";
     default: return "unknown status";
     }
 }

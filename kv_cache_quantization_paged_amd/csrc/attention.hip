@@ -47,6 +47,8 @@
 // score factor carries 2^-k. The global scales are applied to the scores
 // (K) and to the output (V) in fp32; the probabilities are rounded to fp16
 // (11 significant bits) for the second MFMA.
+#include <mutex>
+
 #include "kvfp4_internal.h"
 #include "nvfp4_device.h"
 
@@ -897,6 +899,39 @@ __global__ __launch_bounds__(512) void attention_merge_kernel(AttnArgs a, const 
 }
 
 }  // namespace
+
+// The partial results of kv_decode_attention_noalloc, for callers that cannot
+// allocate: a file-scope device array that every GPU the library runs on
+// holds until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mutex;
+void *g_scratch_addr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void **addr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));    // with `dev` current: its own copy
+        if (e != hipSuccess)
+            return e;
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return hipSuccess;
+}
 
 int64_t decode_attention_splits(int32_t bt_cols, int32_t page_size)
 {

@@ -48,6 +48,10 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
                                    const float *v_scale, float sm_scale, void *out, void *workspace,
                                    hipStream_t st);
 int64_t decode_attention_splits(int32_t bt_cols, int32_t page_size);
+// the current device's address of the no-allocation entry point's scratch
+// array (kNoAllocScratchBytes), looked up on the first call on each device
+constexpr int64_t kNoAllocScratchBytes = KVFP4_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void **addr);
 int64_t decode_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_qo_heads, int32_t bt_cols,
                                          int32_t page_size);
 

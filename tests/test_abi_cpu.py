@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
                             "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
-                            "kv_decode_attention_workspace_size", "kvfp4_status_string"])
+                            "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc",
+                            "kvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -39,8 +40,8 @@ def test_library_exports_every_declared_symbol(B):
 
 
 def test_status_strings(B):
-    for s in range(5):
-        assert B.status_string(s)
+    for s in range(6):
+        assert B.status_string(s) and B.status_string(s) != "unknown status"
     assert B.status_string(99) == "unknown status"
 
 
@@ -203,6 +204,26 @@ def test_decode_attention_rejects_bad_arguments(B):
     assert call(_cache(B), wsb=need - 1) == B.KVFP4_EINVAL                     # workspace too small
     assert call(_cache(B), ws=None) == B.KVFP4_EINVAL
     assert call(_cache(B), ws=P((1 << 20) + 8)) == B.KVFP4_EALIGN
+
+
+def test_noalloc_attention_rejects_bad_arguments_and_oversized_calls(B):
+    """the no-allocation variant shares the argument checks and refuses, before
+    anything is launched, calls whose partials exceed its fixed scratch"""
+    lib = B.load_library()
+    P = C.c_void_p
+
+    def call(cache, dt=1, hq=16, cols=8, batch=2, sm=0.1, out=P(8192)):
+        return lib.kv_decode_attention_noalloc(C.byref(cache), P(4096), dt, hq, P(64), cols, cols, P(64), batch,
+                                               P(64), P(64), sm, out, None)
+    assert call(_cache(B), dt=4) == B.KVFP4_EINVAL
+    assert call(_cache(B), hq=8 * 17) == B.KVFP4_EUNSUPPORTED
+    assert call(_cache(B), sm=float("inf")) == B.KVFP4_EINVAL
+    assert call(_cache(B), out=P(8200)) == B.KVFP4_EALIGN
+    assert call(_cache(B), batch=0) == B.KVFP4_OK
+    # 4096 requests x 8 kv heads x 16 splits of 16 query heads: ~2 GiB of partials
+    big = lib.kv_decode_attention_workspace_size(4096, 8, 128, 256, 16)
+    assert big > B.NOALLOC_SCRATCH_BYTES
+    assert call(_cache(B), hq=128, cols=256, batch=4096) == B.KVFP4_ESCRATCH
 
 
 def test_package_refuses_to_run_without_library(tmp_path, monkeypatch):
