@@ -13,6 +13,8 @@
  *                        scales optionally 4-token interleaved
  *   kv_decode_attention  one-token-per-request attention read straight
  *                        from the NVFP4 pages
+ *   *_prepare + kvfp4_launch  the first three calls checked once, then
+ *                        launched many times without re-checking
  *
  * Sources (FlashInfer 0.7.4 documentation): the API pages
  * flashinfer.page.nvfp4_quantize_append_paged_kv_cache,
@@ -192,6 +194,50 @@ kvfp4_status_t kv_materialize_fp8(const kvfp4_paged_cache_t *cache, int32_t v_sf
                                   int32_t batch_size, void *out_fp8, int64_t num_out_pages,
                                   int32_t *fp8_block_tables, int32_t max_pages_per_seq,
                                   void *stream);
+
+/*
+ * Validate once, launch many (the NVFP4KVMaterializer pattern of the module
+ * page's "NVFP4 KV Cache Materialization" section: its functional form checks
+ * every tensor on every call, which costs more host time than the launch,
+ * so the class checks at construction and run() only launches). A
+ * kvfp4_call_t is caller-owned memory. A *_prepare call runs every check of
+ * the entry point of the same name, exactly as that entry point does, and
+ * on success stores the checked arguments in *call; on failure it returns the
+ * same status and leaves a record that kvfp4_launch refuses. kvfp4_launch
+ * then queues that call's kernels on `stream` without checking anything
+ * again, as often as wanted (each launch reads the buffers' contents at the
+ * time it runs: caches, tables and lengths may change between launches, the
+ * pointers and sizes may not - prepare again for those). A record that no
+ * prepare call wrote, or that was modified since, gives KVFP4_EINVAL (the
+ * record carries a seal over its contents). Launches are graph-capturable
+ * and, like the entry points, allocate and synchronize nothing.
+ */
+typedef struct {
+    uint64_t opaque[40];
+} kvfp4_call_t;
+
+kvfp4_status_t kv_quantize_append_prepare(kvfp4_call_t *call, const kvfp4_paged_cache_t *cache,
+                                          const void *append_key, const void *append_value, int32_t in_dtype,
+                                          int64_t nnz, const int32_t *batch_indices, const int32_t *positions,
+                                          const int32_t *kv_indices, const int32_t *kv_indptr,
+                                          const int32_t *kv_last_page_len, int32_t batch_size, float k_scale,
+                                          float v_scale, const kvfp4_recipe_t *recipe);
+
+kvfp4_status_t kv_dequantize_paged_prepare(kvfp4_call_t *call, const kvfp4_paged_cache_t *cache,
+                                           const void *block_tables, int32_t bt_dtype, int64_t bt_row_stride,
+                                           int32_t bt_cols, const int32_t *seq_lens, int32_t batch_size,
+                                           const float *k_scale, const float *v_scale, void *output_k,
+                                           void *output_v, int32_t out_dtype, int32_t max_seq_len);
+
+kvfp4_status_t kv_materialize_fp8_prepare(kvfp4_call_t *call, const kvfp4_paged_cache_t *cache,
+                                          int32_t v_sf_interleaved, const int32_t *block_tables,
+                                          int32_t uses_shared_paged_kv_idx, int64_t bt_row_stride,
+                                          int64_t bt_kv_stride, int32_t bt_cols, const int32_t *seq_lens,
+                                          const int32_t *kv_page_indptr, int32_t batch_size, void *out_fp8,
+                                          int64_t num_out_pages, int32_t *fp8_block_tables,
+                                          int32_t max_pages_per_seq);
+
+kvfp4_status_t kvfp4_launch(const kvfp4_call_t *call, void *stream);
 
 /*
  * kv_global_scale - make_nvfp4_global_scale(x, per_token_activation=False,

@@ -25,7 +25,8 @@ KVFP4_ERR_MSE, KVFP4_ERR_MAE = 0, 1
 
 EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
             "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
-            "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc", "kvfp4_status_string")
+            "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc", "kv_quantize_append_prepare",
+            "kv_dequantize_paged_prepare", "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_status_string")
 
 
 class PagedCacheDesc(C.Structure):
@@ -90,6 +91,14 @@ def load_library():
                                                 f32, P, P]
     lib.kv_decode_attention_workspace_size.restype = i64
     lib.kv_decode_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.kv_quantize_append_prepare.restype = i32
+    lib.kv_quantize_append_prepare.argtypes = [P] + lib.kv_quantize_append.argtypes[:-1]
+    lib.kv_dequantize_paged_prepare.restype = i32
+    lib.kv_dequantize_paged_prepare.argtypes = [P] + lib.kv_dequantize_paged.argtypes[:-1]
+    lib.kv_materialize_fp8_prepare.restype = i32
+    lib.kv_materialize_fp8_prepare.argtypes = [P] + lib.kv_materialize_fp8.argtypes[:-1]
+    lib.kvfp4_launch.restype = i32
+    lib.kvfp4_launch.argtypes = [P, P]
     lib.kvfp4_status_string.restype = C.c_char_p
     lib.kvfp4_status_string.argtypes = [i32]
     _lib = lib
@@ -121,9 +130,22 @@ def _stride(t, dim):
     return t.stride(dim)
 
 
+# torch's current stream as a raw pointer: the private accessor costs ~0.1 us
+# where torch.cuda.current_stream() builds a Stream object (~3 us per call)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _current_stream_ptr(device_index=None) -> int:
+    if device_index is None:
+        device_index = torch.cuda.current_device()
+    if _raw_stream is not None:
+        return _raw_stream(device_index)
+    return torch.cuda.current_stream(device_index).cuda_stream
+
+
 def _stream(stream=None):
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return C.c_void_p(_current_stream_ptr())
     return C.c_void_p(stream.cuda_stream)
 
 
@@ -192,10 +214,41 @@ class Recipe:
 # ---------------------------------------------------------------------------
 # the C entry points, one Python function each
 # ---------------------------------------------------------------------------
-def kv_quantize_append(cache: PagedCache, append_key, append_value, batch_indices, positions,
-                       kv_indices, kv_indptr, kv_last_page_len, k_scale: float, v_scale: float,
-                       recipe: Recipe | None = None, stream=None):
-    lib = load_library()
+class PreparedCall:
+    """A call checked once (``kv_*_prepare``) and launched many times
+    (``kvfp4_launch``): ``launch()`` queues the kernels on the current stream
+    of the tensors' device (or on ``stream``) without checking anything
+    again. Holds the tensors it was prepared with, so their memory stays
+    valid; their contents may change between launches (that is the point:
+    new lengths, new tables), their shapes and storage may not."""
+    __slots__ = ("_rec", "_addr", "_dev", "_tensors", "_launch", "name")
+
+    def __init__(self, name: str, device_index: int, tensors):
+        self._rec = (C.c_uint64 * 40)()
+        self._addr = C.addressof(self._rec)
+        self._dev = device_index
+        self._tensors = tensors
+        self._launch = load_library().kvfp4_launch
+        self.name = name
+
+    def launch(self, stream=None):
+        if stream is None:
+            st = _raw_stream(self._dev) if _raw_stream is not None else _current_stream_ptr(self._dev)
+        else:
+            st = stream.cuda_stream
+        status = self._launch(self._addr, st)
+        if status:
+            raise KVFP4Error(status, self.name)
+
+
+def _prepared(name, prepare_fn, args, tensors, device_index):
+    call = PreparedCall(name, device_index, tensors)
+    _check(prepare_fn(call._addr, *args), name)
+    return call
+
+
+def _append_args(cache: PagedCache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                 kv_last_page_len, k_scale, v_scale, recipe):
     if append_key.shape != append_value.shape or append_key.dtype != append_value.dtype:
         raise ValueError("append_key and append_value must match")
     if append_key.dim() != 3 or tuple(append_key.shape[1:]) != (cache.num_kv_heads, cache.head_dim):
@@ -212,17 +265,34 @@ def kv_quantize_append(cache: PagedCache, append_key, append_value, batch_indice
     if kv_last_page_len.numel() != batch:
         raise ValueError("kv_last_page_len must have batch_size entries")
     rd = recipe.desc() if recipe is not None else None
-    st = lib.kv_quantize_append(C.byref(cache.desc), _ptr(append_key), _ptr(append_value),
-                                _half_enum(append_key.dtype), nnz, _ptr(batch_indices), _ptr(positions),
-                                _ptr(kv_indices), _ptr(kv_indptr), _ptr(kv_last_page_len), batch,
-                                float(k_scale), float(v_scale), C.byref(rd) if rd is not None else None,
-                                _stream(stream))
-    _check(st, "kv_quantize_append")
+    return (C.byref(cache.desc), _ptr(append_key), _ptr(append_value), _half_enum(append_key.dtype), nnz,
+            _ptr(batch_indices), _ptr(positions), _ptr(kv_indices), _ptr(kv_indptr), _ptr(kv_last_page_len), batch,
+            float(k_scale), float(v_scale), C.byref(rd) if rd is not None else None)
 
 
-def kv_dequantize_paged(cache: PagedCache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v,
-                        stream=None):
+def kv_quantize_append(cache: PagedCache, append_key, append_value, batch_indices, positions,
+                       kv_indices, kv_indptr, kv_last_page_len, k_scale: float, v_scale: float,
+                       recipe: Recipe | None = None, stream=None):
     lib = load_library()
+    args = _append_args(cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                        kv_last_page_len, k_scale, v_scale, recipe)
+    _check(lib.kv_quantize_append(*args, _stream(stream)), "kv_quantize_append")
+
+
+def prepare_quantize_append(cache: PagedCache, append_key, append_value, batch_indices, positions, kv_indices,
+                            kv_indptr, kv_last_page_len, k_scale: float, v_scale: float,
+                            recipe: Recipe | None = None) -> PreparedCall:
+    """kv_quantize_append checked once; ``.launch()`` appends again (e.g. the
+    next decode step's rows written into the same tensors)."""
+    lib = load_library()
+    args = _append_args(cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                        kv_last_page_len, k_scale, v_scale, recipe)
+    return _prepared("kv_quantize_append", lib.kv_quantize_append_prepare, args,
+                     (cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                      kv_last_page_len), append_key.device.index)
+
+
+def _dequant_args(cache: PagedCache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v):
     if block_tables.dtype not in (torch.int32, torch.int64) or block_tables.dim() != 2 or not block_tables.is_cuda:
         raise TypeError("block_tables must be a 2-D int32/int64 CUDA tensor")
     if _stride(block_tables, 1) != 1:
@@ -240,17 +310,30 @@ def kv_dequantize_paged(cache: PagedCache, block_tables, seq_lens, k_scale, v_sc
     B, T = output_k.shape[0], output_k.shape[1]
     if block_tables.shape[0] != B or seq_lens.numel() != B:
         raise ValueError("block_tables / seq_lens batch size disagrees with the outputs")
-    st = lib.kv_dequantize_paged(C.byref(cache.desc), _ptr(block_tables),
-                                 KVFP4_I64 if block_tables.dtype == torch.int64 else KVFP4_I32,
-                                 _stride(block_tables, 0), block_tables.shape[1], _ptr(seq_lens), B,
-                                 _ptr(k_scale), _ptr(v_scale), _ptr(output_k), _ptr(output_v),
-                                 _half_enum(output_k.dtype), T, _stream(stream))
-    _check(st, "kv_dequantize_paged")
+    return (C.byref(cache.desc), _ptr(block_tables), KVFP4_I64 if block_tables.dtype == torch.int64 else KVFP4_I32,
+            _stride(block_tables, 0), block_tables.shape[1], _ptr(seq_lens), B, _ptr(k_scale), _ptr(v_scale),
+            _ptr(output_k), _ptr(output_v), _half_enum(output_k.dtype), T)
 
 
-def kv_materialize_fp8(cache: PagedCache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
-                       uses_shared_paged_kv_idx: bool = True, v_sf_interleaved: bool = True, stream=None):
+def kv_dequantize_paged(cache: PagedCache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v,
+                        stream=None):
     lib = load_library()
+    args = _dequant_args(cache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v)
+    _check(lib.kv_dequantize_paged(*args, _stream(stream)), "kv_dequantize_paged")
+
+
+def prepare_dequantize_paged(cache: PagedCache, block_tables, seq_lens, k_scale, v_scale, output_k,
+                             output_v) -> PreparedCall:
+    """kv_dequantize_paged checked once; ``.launch()`` dequantizes again with
+    whatever the table, lengths and cache hold at that time."""
+    lib = load_library()
+    args = _dequant_args(cache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v)
+    return _prepared("kv_dequantize_paged", lib.kv_dequantize_paged_prepare, args,
+                     (cache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v), output_k.device.index)
+
+
+def _materialize_args(cache: PagedCache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
+                      uses_shared_paged_kv_idx, v_sf_interleaved):
     _need_i32(seq_lens, "seq_lens")
     _need_i32(kv_page_indptr, "kv_page_indptr")
     _need_i32(fp8_block_tables, "fp8_block_tables")
@@ -271,11 +354,27 @@ def kv_materialize_fp8(cache: PagedCache, block_tables, seq_lens, kv_page_indptr
         raise ValueError("out must be [num_out_pages, 2, num_kv_heads, page_size, head_dim]")
     if out.element_size() != 1 or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("out must be a contiguous one-byte (float8_e4m3fn) CUDA tensor")
-    st = lib.kv_materialize_fp8(C.byref(cache.desc), int(bool(v_sf_interleaved)), _ptr(block_tables),
-                                int(bool(uses_shared_paged_kv_idx)), row, kvs, cols, _ptr(seq_lens),
-                                _ptr(kv_page_indptr), B, _ptr(out), out.shape[0], _ptr(fp8_block_tables),
-                                fp8_block_tables.shape[1], _stream(stream))
-    _check(st, "kv_materialize_fp8")
+    return (C.byref(cache.desc), int(bool(v_sf_interleaved)), _ptr(block_tables), int(bool(uses_shared_paged_kv_idx)),
+            row, kvs, cols, _ptr(seq_lens), _ptr(kv_page_indptr), B, _ptr(out), out.shape[0],
+            _ptr(fp8_block_tables), fp8_block_tables.shape[1])
+
+
+def kv_materialize_fp8(cache: PagedCache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
+                       uses_shared_paged_kv_idx: bool = True, v_sf_interleaved: bool = True, stream=None):
+    lib = load_library()
+    args = _materialize_args(cache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
+                             uses_shared_paged_kv_idx, v_sf_interleaved)
+    _check(lib.kv_materialize_fp8(*args, _stream(stream)), "kv_materialize_fp8")
+
+
+def prepare_materialize_fp8(cache: PagedCache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
+                            uses_shared_paged_kv_idx: bool = True, v_sf_interleaved: bool = True) -> PreparedCall:
+    """kv_materialize_fp8 checked once; ``.launch()`` materializes again."""
+    lib = load_library()
+    args = _materialize_args(cache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
+                             uses_shared_paged_kv_idx, v_sf_interleaved)
+    return _prepared("kv_materialize_fp8", lib.kv_materialize_fp8_prepare, args,
+                     (cache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables), out.device.index)
 
 
 def kv_global_scale(x, e4m3_max: float, g_out, stream=None):

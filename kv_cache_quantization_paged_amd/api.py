@@ -17,6 +17,7 @@ the library's kernels on torch's current stream.
 """
 from __future__ import annotations
 
+import weakref
 from dataclasses import dataclass
 from typing import Optional, Tuple, Union
 
@@ -146,8 +147,20 @@ def nvfp4_kv_materialize_fp8(k_cache, v_cache, k_block_scales, v_block_scales, b
 
 
 class NVFP4KVMaterializer:
-    """Validate once, launch many times. ``run()`` allocates nothing, does
-    not synchronize, and launches on the current stream."""
+    """Validate once, launch many times. The geometry is checked at
+    construction; ``run()`` checks a set of tensors the first time it sees
+    it (the C launcher's checks, through ``kv_materialize_fp8_prepare``) and
+    afterwards only launches the prepared call (``kvfp4_launch``). ``run()``
+    allocates nothing, does not synchronize, and launches on the current
+    stream of the materializer's device.
+
+    Prepared calls are kept per tensor set (by object identity, through weak
+    references: a tensor freed by the caller drops its entries, and a new
+    tensor is checked again). Changing a known tensor's storage in place
+    (``set_``, ``resize_``) is not noticed; new contents (lengths, tables,
+    cache bytes) are the normal case and need nothing."""
+
+    _MAX_PREPARED = 128
 
     def __init__(self, num_kv_heads: int, page_size: int, head_dim: int, device="cuda",
                  uses_shared_paged_kv_idx: bool = True, v_sf_interleaved: bool = True):
@@ -157,18 +170,50 @@ class NVFP4KVMaterializer:
             raise ValueError("head_dim must be divisible by 64")
         self.num_kv_heads, self.page_size, self.head_dim = num_kv_heads, page_size, head_dim
         self.device = torch.device(device)
+        if self.device.type != "cuda":
+            raise ValueError("the materializer runs on a CUDA (HIP) device")
         self.shared = bool(uses_shared_paged_kv_idx)
         self.v_sf_interleaved = bool(v_sf_interleaved)
+        self._prepared = {}
         B.load_library()
 
-    def run(self, k_cache, v_cache, k_block_scales, v_block_scales, block_tables, seq_lens, kv_page_indptr,
-            *, out: torch.Tensor, fp8_block_tables: torch.Tensor):
+    def prepare(self, k_cache, v_cache, k_block_scales, v_block_scales, block_tables, seq_lens, kv_page_indptr,
+                *, out: torch.Tensor, fp8_block_tables: torch.Tensor) -> B.PreparedCall:
+        """Check one tensor set and return its prepared call (run() does this
+        on first sight)."""
         cache = _hnd_cache(k_cache, v_cache, k_block_scales, v_block_scales)
         if (cache.num_kv_heads, cache.page_size, cache.head_dim) != (self.num_kv_heads, self.page_size,
                                                                      self.head_dim):
             raise ValueError("cache geometry differs from the materializer's")
-        B.kv_materialize_fp8(cache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
-                             self.shared, self.v_sf_interleaved)
+        for t in (k_cache, v_cache, k_block_scales, v_block_scales, block_tables, seq_lens, kv_page_indptr, out,
+                  fp8_block_tables):
+            if t.device != self.device and not (self.device.index is None and t.device.type == "cuda"):
+                raise ValueError(f"tensors must be on the materializer's device {self.device}")
+        return B.prepare_materialize_fp8(cache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,
+                                         self.shared, self.v_sf_interleaved)
+
+    def run(self, k_cache, v_cache, k_block_scales, v_block_scales, block_tables, seq_lens, kv_page_indptr,
+            *, out: torch.Tensor, fp8_block_tables: torch.Tensor):
+        ts = (k_cache, v_cache, k_block_scales, v_block_scales, block_tables, seq_lens, kv_page_indptr, out,
+              fp8_block_tables)
+        hit = self._prepared.get(tuple(map(id, ts)))
+        if hit is not None:
+            refs, call = hit
+            for r, t in zip(refs, ts):
+                if r() is not t:
+                    break
+            else:
+                call.launch()
+                return out, fp8_block_tables
+        key = tuple(map(id, ts))
+        call = self.prepare(*ts[:7], out=out, fp8_block_tables=fp8_block_tables)
+        # the prepared call keeps the descriptor only; the weak references let
+        # freed tensors go (their entries then never match again)
+        call._tensors = None
+        if len(self._prepared) >= self._MAX_PREPARED:
+            self._prepared.clear()
+        self._prepared[key] = (tuple(weakref.ref(t) for t in ts), call)
+        call.launch()
         return out, fp8_block_tables
 
 

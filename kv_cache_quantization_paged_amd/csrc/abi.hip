@@ -73,12 +73,97 @@ constexpr int64_t kMaxBlocks = ((int64_t)1 << 31) - 1;   // blocks of 16 per qua
 
 extern "C" {
 
-kvfp4_status_t kv_quantize_append(const kvfp4_paged_cache_t *cache, const void *append_key,
-                                  const void *append_value, int32_t in_dtype, int64_t nnz,
-                                  const int32_t *batch_indices, const int32_t *positions,
-                                  const int32_t *kv_indices, const int32_t *kv_indptr,
-                                  const int32_t *kv_last_page_len, int32_t batch_size, float k_scale,
-                                  float v_scale, const kvfp4_recipe_t *recipe, void *stream)
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// prepared calls: a *_prepare function runs every check of its entry point and
+// stores the checked arguments in the caller's kvfp4_call_t; kvfp4_launch then
+// only launches. The seal (a hash over the stored record) lets kvfp4_launch
+// refuse a record that no prepare call wrote or that was changed since.
+// ---------------------------------------------------------------------------
+namespace {
+
+enum : uint32_t { kOpAppend = 1, kOpDequant = 2, kOpMaterialize = 3 };
+
+struct AppendRec {
+    kvfp4_paged_cache_t cache;
+    const void *key, *value;
+    int64_t nnz;
+    const int32_t *batch_indices, *positions, *kv_indices, *kv_indptr;
+    float k_scale, v_scale;
+    int32_t bf16, has_recipe;
+    kvfp4_recipe_t recipe;
+};
+
+struct DequantRec {
+    kvfp4_paged_cache_t cache;
+    const void *block_tables;
+    int64_t bt_row_stride;
+    const int32_t *seq_lens;
+    const float *k_scale, *v_scale;
+    void *out_k, *out_v;
+    int32_t bt64, batch, out_bf16, max_seq_len;
+};
+
+struct MaterializeRec {
+    kvfp4_paged_cache_t cache;
+    const int32_t *block_tables;
+    int64_t bt_row_stride, bt_kv_stride;
+    const int32_t *seq_lens, *kv_page_indptr;
+    void *out;
+    int64_t num_out_pages;
+    int32_t *fp8_block_tables;
+    int32_t interleaved, shared, batch, max_pages_per_seq;
+};
+
+struct CallRec {
+    uint64_t seal;
+    uint32_t op;
+    uint32_t nothing_to_do;      // checks passed, but the call queues no work
+    union {
+        AppendRec append;
+        DequantRec dequant;
+        MaterializeRec materialize;
+    } u;
+};
+static_assert(sizeof(CallRec) <= sizeof(kvfp4_call_t), "kvfp4_call_t is too small for the call records");
+static_assert(alignof(kvfp4_call_t) >= alignof(CallRec), "kvfp4_call_t alignment");
+
+// FNV-1a over the whole kvfp4_call_t after the seal (unused tail bytes
+// included, so that no byte can change unnoticed), mixed with a library constant
+uint64_t seal_of(const CallRec *r)
+{
+    const unsigned char *p = (const unsigned char *)r + sizeof(uint64_t);
+    uint64_t h = 0xcbf29ce484222325ull;
+    for (size_t i = 0; i < sizeof(kvfp4_call_t) - sizeof(uint64_t); ++i) {
+        h ^= p[i];
+        h *= 0x100000001b3ull;
+    }
+    return h ^ 0x6b76667034ull;
+}
+
+CallRec *begin(kvfp4_call_t *call, uint32_t op)
+{
+    memset(call, 0, sizeof(*call));        // padding bytes too: the seal covers them
+    CallRec *r = (CallRec *)call;
+    r->op = op;
+    return r;
+}
+
+kvfp4_status_t finish(CallRec *r, kvfp4_status_t s)
+{
+    if (s == KVFP4_OK)
+        r->seal = seal_of(r);
+    else
+        memset(r, 0, sizeof(kvfp4_call_t));  // a failed prepare leaves a record no launch accepts
+    return s;
+}
+
+kvfp4_status_t prepare_append(CallRec *r, const kvfp4_paged_cache_t *cache, const void *append_key,
+                              const void *append_value, int32_t in_dtype, int64_t nnz, const int32_t *batch_indices,
+                              const int32_t *positions, const int32_t *kv_indices, const int32_t *kv_indptr,
+                              const int32_t *kv_last_page_len, int32_t batch_size, float k_scale, float v_scale,
+                              const kvfp4_recipe_t *recipe)
 {
     kvfp4_status_t s = check_cache(cache);
     if (s != KVFP4_OK)
@@ -92,23 +177,37 @@ kvfp4_status_t kv_quantize_append(const kvfp4_paged_cache_t *cache, const void *
     s = check_recipe(recipe);
     if (s != KVFP4_OK)
         return s;
-    if (nnz == 0)
+    if (nnz == 0) {
+        r->nothing_to_do = 1;
         return KVFP4_OK;
+    }
     if (batch_size == 0 || !append_key || !append_value || !batch_indices || !positions || !kv_indices ||
         !kv_indptr || !kv_last_page_len)
         return KVFP4_EINVAL;
     if (!aligned16(append_key) || !aligned16(append_value))
         return KVFP4_EALIGN;
-    return from_hip(launch_quantize_append(*cache, append_key, append_value, in_dtype == KVFP4_BF16, nnz,
-                                           batch_indices, positions, kv_indices, kv_indptr, k_scale, v_scale,
-                                           recipe, (hipStream_t)stream));
+    AppendRec &a = r->u.append;
+    a.cache = *cache;
+    a.key = append_key;
+    a.value = append_value;
+    a.nnz = nnz;
+    a.batch_indices = batch_indices;
+    a.positions = positions;
+    a.kv_indices = kv_indices;
+    a.kv_indptr = kv_indptr;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.bf16 = in_dtype == KVFP4_BF16;
+    a.has_recipe = recipe != nullptr;
+    if (recipe)
+        a.recipe = *recipe;
+    return KVFP4_OK;
 }
 
-kvfp4_status_t kv_dequantize_paged(const kvfp4_paged_cache_t *cache, const void *block_tables, int32_t bt_dtype,
-                                   int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
-                                   int32_t batch_size, const float *k_scale, const float *v_scale,
-                                   void *output_k, void *output_v, int32_t out_dtype, int32_t max_seq_len,
-                                   void *stream)
+kvfp4_status_t prepare_dequant(CallRec *r, const kvfp4_paged_cache_t *cache, const void *block_tables,
+                               int32_t bt_dtype, int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
+                               int32_t batch_size, const float *k_scale, const float *v_scale, void *output_k,
+                               void *output_v, int32_t out_dtype, int32_t max_seq_len)
 {
     kvfp4_status_t s = check_cache(cache);
     if (s != KVFP4_OK)
@@ -119,24 +218,37 @@ kvfp4_status_t kv_dequantize_paged(const kvfp4_paged_cache_t *cache, const void 
         return KVFP4_EINVAL;
     if (batch_size < 0 || max_seq_len < 0 || bt_cols < 0 || bt_row_stride < bt_cols)
         return KVFP4_EINVAL;
-    if (batch_size == 0 || max_seq_len == 0)
+    if (batch_size == 0 || max_seq_len == 0) {
+        r->nothing_to_do = 1;
         return KVFP4_OK;
+    }
     // each row needs ceil(min(seq_len, max_seq_len) / page_size) columns: a value, not checked
     if (bt_cols < 1 || !block_tables || !seq_lens || !k_scale || !v_scale || !output_k || !output_v)
         return KVFP4_EINVAL;
     if (!aligned16(output_k) || !aligned16(output_v))
         return KVFP4_EALIGN;
-    return from_hip(launch_dequantize_paged(*cache, block_tables, bt_dtype == KVFP4_I64, bt_row_stride, seq_lens,
-                                            batch_size, k_scale, v_scale, output_k, output_v,
-                                            out_dtype == KVFP4_BF16, max_seq_len, (hipStream_t)stream));
+    DequantRec &d = r->u.dequant;
+    d.cache = *cache;
+    d.block_tables = block_tables;
+    d.bt_row_stride = bt_row_stride;
+    d.seq_lens = seq_lens;
+    d.k_scale = k_scale;
+    d.v_scale = v_scale;
+    d.out_k = output_k;
+    d.out_v = output_v;
+    d.bt64 = bt_dtype == KVFP4_I64;
+    d.batch = batch_size;
+    d.out_bf16 = out_dtype == KVFP4_BF16;
+    d.max_seq_len = max_seq_len;
+    return KVFP4_OK;
 }
 
-kvfp4_status_t kv_materialize_fp8(const kvfp4_paged_cache_t *cache, int32_t v_sf_interleaved,
-                                  const int32_t *block_tables, int32_t uses_shared_paged_kv_idx,
-                                  int64_t bt_row_stride, int64_t bt_kv_stride, int32_t bt_cols,
-                                  const int32_t *seq_lens, const int32_t *kv_page_indptr, int32_t batch_size,
-                                  void *out_fp8, int64_t num_out_pages, int32_t *fp8_block_tables,
-                                  int32_t max_pages_per_seq, void *stream)
+kvfp4_status_t prepare_materialize(CallRec *r, const kvfp4_paged_cache_t *cache, int32_t v_sf_interleaved,
+                                   const int32_t *block_tables, int32_t uses_shared_paged_kv_idx,
+                                   int64_t bt_row_stride, int64_t bt_kv_stride, int32_t bt_cols,
+                                   const int32_t *seq_lens, const int32_t *kv_page_indptr, int32_t batch_size,
+                                   void *out_fp8, int64_t num_out_pages, int32_t *fp8_block_tables,
+                                   int32_t max_pages_per_seq)
 {
     kvfp4_status_t s = check_cache(cache);
     if (s != KVFP4_OK)
@@ -159,10 +271,152 @@ kvfp4_status_t kv_materialize_fp8(const kvfp4_paged_cache_t *cache, int32_t v_sf
             return KVFP4_EINVAL;
         }
     }
-    return from_hip(launch_materialize_fp8(*cache, v_sf_interleaved != 0, block_tables, uses_shared_paged_kv_idx != 0,
-                                           bt_row_stride, bt_kv_stride, seq_lens, kv_page_indptr, batch_size,
-                                           out_fp8, num_out_pages, fp8_block_tables, max_pages_per_seq,
-                                           (hipStream_t)stream));
+    MaterializeRec &m = r->u.materialize;
+    m.cache = *cache;
+    m.block_tables = block_tables;
+    m.bt_row_stride = bt_row_stride;
+    m.bt_kv_stride = bt_kv_stride;
+    m.seq_lens = seq_lens;
+    m.kv_page_indptr = kv_page_indptr;
+    m.out = out_fp8;
+    m.num_out_pages = num_out_pages;
+    m.fp8_block_tables = fp8_block_tables;
+    m.interleaved = v_sf_interleaved != 0;
+    m.shared = uses_shared_paged_kv_idx != 0;
+    m.batch = batch_size;
+    m.max_pages_per_seq = max_pages_per_seq;
+    return KVFP4_OK;
+}
+
+kvfp4_status_t launch_rec(const CallRec *r, hipStream_t st)
+{
+    if (r->nothing_to_do)
+        return KVFP4_OK;
+    switch (r->op) {
+    case kOpAppend: {
+        const AppendRec &a = r->u.append;
+        return from_hip(launch_quantize_append(a.cache, a.key, a.value, a.bf16 != 0, a.nnz, a.batch_indices,
+                                               a.positions, a.kv_indices, a.kv_indptr, a.k_scale, a.v_scale,
+                                               a.has_recipe ? &a.recipe : nullptr, st));
+    }
+    case kOpDequant: {
+        const DequantRec &d = r->u.dequant;
+        return from_hip(launch_dequantize_paged(d.cache, d.block_tables, d.bt64 != 0, d.bt_row_stride, d.seq_lens,
+                                                d.batch, d.k_scale, d.v_scale, d.out_k, d.out_v, d.out_bf16 != 0,
+                                                d.max_seq_len, st));
+    }
+    case kOpMaterialize: {
+        const MaterializeRec &m = r->u.materialize;
+        return from_hip(launch_materialize_fp8(m.cache, m.interleaved != 0, m.block_tables, m.shared != 0,
+                                               m.bt_row_stride, m.bt_kv_stride, m.seq_lens, m.kv_page_indptr,
+                                               m.batch, m.out, m.num_out_pages, m.fp8_block_tables,
+                                               m.max_pages_per_seq, st));
+    }
+    default:
+        return KVFP4_EINVAL;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+kvfp4_status_t kv_quantize_append_prepare(kvfp4_call_t *call, const kvfp4_paged_cache_t *cache,
+                                          const void *append_key, const void *append_value, int32_t in_dtype,
+                                          int64_t nnz, const int32_t *batch_indices, const int32_t *positions,
+                                          const int32_t *kv_indices, const int32_t *kv_indptr,
+                                          const int32_t *kv_last_page_len, int32_t batch_size, float k_scale,
+                                          float v_scale, const kvfp4_recipe_t *recipe)
+{
+    if (!call)
+        return KVFP4_EINVAL;
+    CallRec *r = begin(call, kOpAppend);
+    return finish(r, prepare_append(r, cache, append_key, append_value, in_dtype, nnz, batch_indices, positions,
+                                    kv_indices, kv_indptr, kv_last_page_len, batch_size, k_scale, v_scale, recipe));
+}
+
+kvfp4_status_t kv_dequantize_paged_prepare(kvfp4_call_t *call, const kvfp4_paged_cache_t *cache,
+                                           const void *block_tables, int32_t bt_dtype, int64_t bt_row_stride,
+                                           int32_t bt_cols, const int32_t *seq_lens, int32_t batch_size,
+                                           const float *k_scale, const float *v_scale, void *output_k,
+                                           void *output_v, int32_t out_dtype, int32_t max_seq_len)
+{
+    if (!call)
+        return KVFP4_EINVAL;
+    CallRec *r = begin(call, kOpDequant);
+    return finish(r, prepare_dequant(r, cache, block_tables, bt_dtype, bt_row_stride, bt_cols, seq_lens, batch_size,
+                                     k_scale, v_scale, output_k, output_v, out_dtype, max_seq_len));
+}
+
+kvfp4_status_t kv_materialize_fp8_prepare(kvfp4_call_t *call, const kvfp4_paged_cache_t *cache,
+                                          int32_t v_sf_interleaved, const int32_t *block_tables,
+                                          int32_t uses_shared_paged_kv_idx, int64_t bt_row_stride,
+                                          int64_t bt_kv_stride, int32_t bt_cols, const int32_t *seq_lens,
+                                          const int32_t *kv_page_indptr, int32_t batch_size, void *out_fp8,
+                                          int64_t num_out_pages, int32_t *fp8_block_tables,
+                                          int32_t max_pages_per_seq)
+{
+    if (!call)
+        return KVFP4_EINVAL;
+    CallRec *r = begin(call, kOpMaterialize);
+    return finish(r, prepare_materialize(r, cache, v_sf_interleaved, block_tables, uses_shared_paged_kv_idx,
+                                         bt_row_stride, bt_kv_stride, bt_cols, seq_lens, kv_page_indptr, batch_size,
+                                         out_fp8, num_out_pages, fp8_block_tables, max_pages_per_seq));
+}
+
+kvfp4_status_t kvfp4_launch(const kvfp4_call_t *call, void *stream)
+{
+    if (!call)
+        return KVFP4_EINVAL;
+    const CallRec *r = (const CallRec *)call;
+    if (r->op == 0 || r->seal != seal_of(r))
+        return KVFP4_EINVAL;
+    return launch_rec(r, (hipStream_t)stream);
+}
+
+kvfp4_status_t kv_quantize_append(const kvfp4_paged_cache_t *cache, const void *append_key,
+                                  const void *append_value, int32_t in_dtype, int64_t nnz,
+                                  const int32_t *batch_indices, const int32_t *positions,
+                                  const int32_t *kv_indices, const int32_t *kv_indptr,
+                                  const int32_t *kv_last_page_len, int32_t batch_size, float k_scale,
+                                  float v_scale, const kvfp4_recipe_t *recipe, void *stream)
+{
+    kvfp4_call_t call;
+    CallRec *r = begin(&call, kOpAppend);
+    const kvfp4_status_t s = prepare_append(r, cache, append_key, append_value, in_dtype, nnz, batch_indices,
+                                            positions, kv_indices, kv_indptr, kv_last_page_len, batch_size, k_scale,
+                                            v_scale, recipe);
+    return s != KVFP4_OK ? s : launch_rec(r, (hipStream_t)stream);
+}
+
+kvfp4_status_t kv_dequantize_paged(const kvfp4_paged_cache_t *cache, const void *block_tables, int32_t bt_dtype,
+                                   int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
+                                   int32_t batch_size, const float *k_scale, const float *v_scale,
+                                   void *output_k, void *output_v, int32_t out_dtype, int32_t max_seq_len,
+                                   void *stream)
+{
+    kvfp4_call_t call;
+    CallRec *r = begin(&call, kOpDequant);
+    const kvfp4_status_t s = prepare_dequant(r, cache, block_tables, bt_dtype, bt_row_stride, bt_cols, seq_lens,
+                                             batch_size, k_scale, v_scale, output_k, output_v, out_dtype,
+                                             max_seq_len);
+    return s != KVFP4_OK ? s : launch_rec(r, (hipStream_t)stream);
+}
+
+kvfp4_status_t kv_materialize_fp8(const kvfp4_paged_cache_t *cache, int32_t v_sf_interleaved,
+                                  const int32_t *block_tables, int32_t uses_shared_paged_kv_idx,
+                                  int64_t bt_row_stride, int64_t bt_kv_stride, int32_t bt_cols,
+                                  const int32_t *seq_lens, const int32_t *kv_page_indptr, int32_t batch_size,
+                                  void *out_fp8, int64_t num_out_pages, int32_t *fp8_block_tables,
+                                  int32_t max_pages_per_seq, void *stream)
+{
+    kvfp4_call_t call;
+    CallRec *r = begin(&call, kOpMaterialize);
+    const kvfp4_status_t s = prepare_materialize(r, cache, v_sf_interleaved, block_tables, uses_shared_paged_kv_idx,
+                                                 bt_row_stride, bt_kv_stride, bt_cols, seq_lens, kv_page_indptr,
+                                                 batch_size, out_fp8, num_out_pages, fp8_block_tables,
+                                                 max_pages_per_seq);
+    return s != KVFP4_OK ? s : launch_rec(r, (hipStream_t)stream);
 }
 
 kvfp4_status_t kv_global_scale(const void *x, int32_t dtype, int64_t n, float e4m3_max, float *g_out, void *stream)

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     assert names == sorted(["kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
                             "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
                             "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc",
-                            "kvfp4_status_string"])
+                            "kv_quantize_append_prepare", "kv_dequantize_paged_prepare",
+                            "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -224,6 +225,57 @@ def test_noalloc_attention_rejects_bad_arguments_and_oversized_calls(B):
     big = lib.kv_decode_attention_workspace_size(4096, 8, 128, 256, 16)
     assert big > B.NOALLOC_SCRATCH_BYTES
     assert call(_cache(B), hq=128, cols=256, batch=4096) == B.KVFP4_ESCRATCH
+
+
+def test_prepare_runs_the_entry_point_checks_and_launch_refuses_bad_records(B):
+    """*_prepare returns the entry point's status for the same arguments; a
+    record that no prepare wrote, that a failed prepare left, or that was
+    changed afterwards is refused by kvfp4_launch before any launch (none of
+    these calls reaches the GPU)."""
+    lib = B.load_library()
+    P = C.c_void_p
+    rec = (C.c_uint64 * 40)()
+    addr = C.addressof(rec)
+
+    def prep_append(cache, **kw):
+        a = dict(key=P(4096), value=P(8192), dtype=1, nnz=1, bi=P(64), pos=P(64), ind=P(64), ptr=P(64), last=P(64),
+                 batch=1, ks=1.0, vs=1.0, recipe=None)
+        a.update(kw)
+        return lib.kv_quantize_append_prepare(addr, C.byref(cache), a["key"], a["value"], a["dtype"], a["nnz"],
+                                              a["bi"], a["pos"], a["ind"], a["ptr"], a["last"], a["batch"], a["ks"],
+                                              a["vs"], a["recipe"])
+    # the same statuses as the entry point
+    for kw, cache_kw in (({}, dict(k_data=None)), ({}, dict(head_dim=40)), ({"dtype": 7}, {}), ({"ks": 0.0}, {}),
+                         ({"key": P(4100)}, {}), ({"nnz": -1}, {})):
+        want = _append(B, _cache(B, **cache_kw), **kw)
+        assert want != B.KVFP4_OK
+        assert prep_append(_cache(B, **cache_kw), **kw) == want
+        assert lib.kvfp4_launch(addr, None) == B.KVFP4_EINVAL          # a failed prepare leaves no valid record
+    # never prepared
+    zero = (C.c_uint64 * 40)()
+    assert lib.kvfp4_launch(C.addressof(zero), None) == B.KVFP4_EINVAL
+    assert lib.kvfp4_launch(None, None) == B.KVFP4_EINVAL
+    # prepared, then one byte changed: refused
+    assert prep_append(_cache(B)) == B.KVFP4_OK
+    raw = (C.c_ubyte * 320).from_address(addr)
+    for i in (9, 40, 150, 300):
+        raw[i] ^= 0x10
+        assert lib.kvfp4_launch(addr, None) == B.KVFP4_EINVAL, i
+        raw[i] ^= 0x10
+    # nnz == 0 prepares an empty call: launching it queues nothing (no GPU needed)
+    assert prep_append(_cache(B), nnz=0, bi=None) == B.KVFP4_OK
+    assert lib.kvfp4_launch(addr, None) == B.KVFP4_OK
+    # dequant and materialize prepares mirror their entry points too
+    hnd = dict(layout=1)
+    assert lib.kv_dequantize_paged_prepare(addr, C.byref(_cache(B)), P(64), 3, 8, 8, P(64), 2, P(64), P(64),
+                                           P(4096), P(8192), 1, 16) == B.KVFP4_EINVAL     # bad table dtype
+    assert lib.kv_dequantize_paged_prepare(addr, C.byref(_cache(B)), P(64), 0, 8, 8, P(64), 0, P(64), P(64),
+                                           P(4096), P(8192), 1, 16) == B.KVFP4_OK         # empty batch
+    assert lib.kvfp4_launch(addr, None) == B.KVFP4_OK
+    assert lib.kv_materialize_fp8_prepare(addr, C.byref(_cache(B)), 1, P(64), 1, 8, 0, 8, P(64), P(64), 2,
+                                          P(4096), 10, P(64), 8) == B.KVFP4_EINVAL        # NHD is refused
+    assert lib.kv_materialize_fp8_prepare(addr, C.byref(_cache(B, **hnd)), 1, P(64), 1, 8, 0, 8, P(64), P(64), 2,
+                                          P(4100), 10, P(64), 8) == B.KVFP4_EALIGN
 
 
 def test_package_refuses_to_run_without_library(tmp_path, monkeypatch):
