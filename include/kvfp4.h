@@ -59,7 +59,8 @@ enum {
     KVFP4_EALIGN = 2,        /* a base pointer or stride is not 16-byte aligned */
     KVFP4_EUNSUPPORTED = 3,  /* a valid request the library does not implement */
     KVFP4_ELAUNCH = 4,       /* the HIP runtime refused a launch */
-    KVFP4_ESCRATCH = 5       /* a no-allocation call needs more than its fixed scratch */
+    KVFP4_ESCRATCH = 5,      /* a no-allocation call needs more than its fixed scratch */
+    KVFP4_EVALUE = 6         /* a table check found a value out of range (see the report) */
 };
 
 enum { KVFP4_NHD = 0, KVFP4_HND = 1 };                /* cache layouts */
@@ -359,6 +360,75 @@ kvfp4_status_t kv_decode_attention_noalloc(const kvfp4_paged_cache_t *cache, con
                                            int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
                                            int32_t batch_size, const float *k_scale, const float *v_scale,
                                            float sm_scale, void *out, void *stream);
+
+/*
+ * Host-side table checks: a debugging aid for the values the calls above
+ * never check (the module page's materializer note: lengths, page indices
+ * and indptr are not checked by the launchers). Each function reads HOST
+ * copies of the index arrays (plain host pointers, not device memory), with
+ * the same meaning as the corresponding call's arguments, and returns
+ * KVFP4_OK when every value the call would use is in range, KVFP4_EVALUE with
+ * *report set to the first problem found, or KVFP4_EINVAL for bad arguments.
+ * Nothing is launched and no device memory is touched.
+ *   problem  one of KVFP4_TABLE_* below
+ *   index    the offending element: the row (append rows), the request, or
+ *            the flat index into kv_indices / block_tables / indptr
+ *   value    that element's value
+ */
+enum {
+    KVFP4_TABLE_OK = 0,
+    KVFP4_TABLE_INDPTR_START = 1,    /* kv_indptr / kv_page_indptr[0] != 0 */
+    KVFP4_TABLE_INDPTR_ORDER = 2,    /* the indptr array decreases */
+    KVFP4_TABLE_PAGE_RANGE = 3,      /* a page id the call reads is outside [0, num_pages) */
+    KVFP4_TABLE_BATCH_RANGE = 4,     /* batch_indices[r] outside [0, batch_size) */
+    KVFP4_TABLE_POSITION_RANGE = 5,  /* positions[r] outside the request's reserved space */
+    KVFP4_TABLE_LAST_PAGE_LEN = 6,   /* kv_last_page_len[b] outside [1, page_size] (0 without pages) */
+    KVFP4_TABLE_DUPLICATE_ROW = 7,   /* two rows write the same (request, position): they race */
+    KVFP4_TABLE_LENGTH_RANGE = 8,    /* a length below 0 or longer than the table row addresses */
+    KVFP4_TABLE_RESERVATION = 9,     /* kv_page_indptr reserves fewer pages than a request needs */
+    KVFP4_TABLE_OUT_PAGES = 10       /* out has fewer than kv_page_indptr[batch_size] + 1 pages */
+};
+typedef struct {
+    int32_t problem;
+    int64_t index;
+    int64_t value;
+} kvfp4_table_report_t;
+
+/* kv_quantize_append's tables: kv_indptr starts at 0 and never decreases,
+ * every kv_indices entry is a page id, kv_last_page_len[b] is in
+ * [1, page_size] for a request with pages (0 otherwise), every row's request
+ * is in range and its position inside (pages - 1) * page_size +
+ * kv_last_page_len[b]. With `scratch` (host memory for nnz int64 values,
+ * overwritten) rows that write the same (request, position) are reported
+ * too; NULL skips that check. */
+kvfp4_status_t kvfp4_check_append_tables(const int32_t *batch_indices, const int32_t *positions, int64_t nnz,
+                                         const int32_t *kv_indices, const int32_t *kv_indptr,
+                                         const int32_t *kv_last_page_len, int32_t batch_size, int32_t page_size,
+                                         int32_t num_pages, int64_t *scratch, kvfp4_table_report_t *report);
+
+/* kv_dequantize_paged's (max_seq_len as given) and kv_decode_attention's
+ * (max_seq_len = INT32_MAX, bt_dtype KVFP4_I32) tables: every length is
+ * >= 0 and needs at most bt_cols pages, and the page ids of the pages a
+ * request uses are in range. */
+kvfp4_status_t kvfp4_check_paged_tables(const void *block_tables, int32_t bt_dtype, int64_t bt_row_stride,
+                                        int32_t bt_cols, const int32_t *seq_lens, int32_t batch_size,
+                                        int32_t page_size, int32_t num_pages, int32_t max_seq_len,
+                                        kvfp4_table_report_t *report);
+
+/* kv_materialize_fp8's tables: kv_page_indptr starts at 0 and never
+ * decreases, reserves at least ceil(seq_lens[b] / page_size) pages per
+ * request and fits num_out_pages - 1 pages; 0 <= seq_lens[b] <=
+ * max_pages_per_seq * page_size; the K (and V) page ids of every page used
+ * are in range. */
+kvfp4_status_t kvfp4_check_materialize_tables(const int32_t *block_tables, int32_t uses_shared_paged_kv_idx,
+                                              int64_t bt_row_stride, int64_t bt_kv_stride, int32_t bt_cols,
+                                              const int32_t *seq_lens, const int32_t *kv_page_indptr,
+                                              int32_t batch_size, int32_t page_size, int32_t num_pages,
+                                              int32_t max_pages_per_seq, int64_t num_out_pages,
+                                              kvfp4_table_report_t *report);
+
+/* Static description of a KVFP4_TABLE_* problem. */
+const char *kvfp4_table_problem_string(int32_t problem);
 
 /* Static description of a status code. */
 const char *kvfp4_status_string(kvfp4_status_t status);

@@ -15,7 +15,8 @@ from ._binding import (KVFP4Error, PagedCache, Recipe, kv_dequantize, kv_dequant
                        kv_quantize_paged_cache, kv_decode_attention,
                        kv_decode_attention_workspace_size, kv_decode_attention_noalloc, load_library,
                        status_string, PreparedCall, prepare_quantize_append, prepare_dequantize_paged,
-                       prepare_materialize_fp8)
+                       prepare_materialize_fp8, TableError, check_append_tables, check_paged_tables,
+                       check_materialize_tables)
 from ._binding import (KVFP4_BF16, KVFP4_ERR_MAE, KVFP4_ERR_MSE, KVFP4_F16, KVFP4_HND,  # noqa: F401
                        KVFP4_I32, KVFP4_I64, KVFP4_NHD)
 from .api import (NVFP44Over6Config, NVFP4KVMaterializer, make_nvfp4_global_scale,  # noqa: F401

@@ -16,7 +16,7 @@ import torch  # loads the HIP runtime that the library then shares
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libkvfp4.so")
 
-KVFP4_OK, KVFP4_EINVAL, KVFP4_EALIGN, KVFP4_EUNSUPPORTED, KVFP4_ELAUNCH, KVFP4_ESCRATCH = 0, 1, 2, 3, 4, 5
+KVFP4_OK, KVFP4_EINVAL, KVFP4_EALIGN, KVFP4_EUNSUPPORTED, KVFP4_ELAUNCH, KVFP4_ESCRATCH, KVFP4_EVALUE = range(7)
 NOALLOC_SCRATCH_BYTES = 32 << 20      # KVFP4_NOALLOC_SCRATCH_BYTES
 KVFP4_NHD, KVFP4_HND = 0, 1
 KVFP4_F16, KVFP4_BF16 = 0, 1
@@ -26,7 +26,9 @@ KVFP4_ERR_MSE, KVFP4_ERR_MAE = 0, 1
 EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
             "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
             "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc", "kv_quantize_append_prepare",
-            "kv_dequantize_paged_prepare", "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_status_string")
+            "kv_dequantize_paged_prepare", "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_check_append_tables",
+            "kvfp4_check_paged_tables", "kvfp4_check_materialize_tables", "kvfp4_table_problem_string",
+            "kvfp4_status_string")
 
 
 class PagedCacheDesc(C.Structure):
@@ -39,6 +41,11 @@ class PagedCacheDesc(C.Structure):
         ("num_pages", C.c_int32), ("page_size", C.c_int32),
         ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("layout", C.c_int32),
     ]
+
+
+class TableReport(C.Structure):
+    """``kvfp4_table_report_t``"""
+    _fields_ = [("problem", C.c_int32), ("index", C.c_int64), ("value", C.c_int64)]
 
 
 class RecipeDesc(C.Structure):
@@ -99,6 +106,15 @@ def load_library():
     lib.kv_materialize_fp8_prepare.argtypes = [P] + lib.kv_materialize_fp8.argtypes[:-1]
     lib.kvfp4_launch.restype = i32
     lib.kvfp4_launch.argtypes = [P, P]
+    lib.kvfp4_check_append_tables.restype = i32
+    lib.kvfp4_check_append_tables.argtypes = [P, P, i64, P, P, P, i32, i32, i32, P, C.POINTER(TableReport)]
+    lib.kvfp4_check_paged_tables.restype = i32
+    lib.kvfp4_check_paged_tables.argtypes = [P, i32, i64, i32, P, i32, i32, i32, i32, C.POINTER(TableReport)]
+    lib.kvfp4_check_materialize_tables.restype = i32
+    lib.kvfp4_check_materialize_tables.argtypes = [P, i32, i64, i64, i32, P, P, i32, i32, i32, i32, i64,
+                                                   C.POINTER(TableReport)]
+    lib.kvfp4_table_problem_string.restype = C.c_char_p
+    lib.kvfp4_table_problem_string.argtypes = [i32]
     lib.kvfp4_status_string.restype = C.c_char_p
     lib.kvfp4_status_string.argtypes = [i32]
     _lib = lib
@@ -499,3 +515,96 @@ def kv_decode_attention_noalloc(cache: PagedCache, q, block_tables, seq_lens, k_
     args = _attention_args(cache, q, block_tables, seq_lens, k_scale, v_scale, out)
     st = lib.kv_decode_attention_noalloc(*args, float(sm_scale), _ptr(out), _stream(stream))
     _check(st, "kv_decode_attention_noalloc")
+
+
+# ---------------------------------------------------------------------------
+# host-side table checks (debugging aid: the device calls never check values)
+# ---------------------------------------------------------------------------
+class TableError(ValueError):
+    """A table value a call would use out of range: ``problem`` (a
+    KVFP4_TABLE_* code), ``index`` and ``value`` locate it."""
+
+    def __init__(self, where: str, report: TableReport):
+        self.problem, self.index, self.value = report.problem, report.index, report.value
+        text = load_library().kvfp4_table_problem_string(report.problem).decode()
+        super().__init__(f"{where}: {text} (element {report.index}, value {report.value})")
+
+
+def _host_ints(a, dtype=None):
+    """a host numpy copy of a tensor or array (int32 unless dtype says)"""
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    a = np.asarray(a)
+    if dtype is not None:
+        a = a.astype(dtype, copy=False)
+    return np.ascontiguousarray(a)
+
+
+def _np_ptr(a):
+    return C.c_void_p(a.ctypes.data) if a.size else None
+
+
+def _table_result(st, rep, where):
+    if st == KVFP4_EVALUE:
+        raise TableError(where, rep)
+    _check(st, where)
+
+
+def check_append_tables(batch_indices, positions, kv_indices, kv_indptr, kv_last_page_len, page_size: int,
+                        num_pages: int, check_duplicates: bool = True):
+    """Raise TableError unless every table value kv_quantize_append would use
+    is in range (host copies; works on CPU or GPU tensors and arrays)."""
+    import numpy as np
+    bi, pos = _host_ints(batch_indices, np.int32), _host_ints(positions, np.int32)
+    ind, ptr, last = _host_ints(kv_indices, np.int32), _host_ints(kv_indptr, np.int32), _host_ints(kv_last_page_len, np.int32)
+    if bi.shape != pos.shape or ptr.size < 1 or last.size != ptr.size - 1 or ind.size < (ptr[-1] if ptr.size else 0):
+        raise ValueError("table sizes disagree")
+    scratch = np.empty(bi.size, np.int64) if check_duplicates else None
+    rep = TableReport()
+    st = load_library().kvfp4_check_append_tables(_np_ptr(bi), _np_ptr(pos), bi.size, _np_ptr(ind), _np_ptr(ptr),
+                                                  _np_ptr(last), ptr.size - 1, page_size, num_pages,
+                                                  None if scratch is None else _np_ptr(scratch), C.byref(rep))
+    _table_result(st, rep, "append tables")
+
+
+def check_paged_tables(block_tables, seq_lens, page_size: int, num_pages: int, max_seq_len: int = 2 ** 31 - 1):
+    """Raise TableError unless every table value kv_dequantize_paged (with
+    this max_seq_len) or kv_decode_attention (the default) would use is in
+    range."""
+    import numpy as np
+    bt = _host_ints(block_tables)
+    if bt.dtype not in (np.int32, np.int64) or bt.ndim != 2:
+        raise ValueError("block_tables must be 2-D int32 or int64")
+    sl = _host_ints(seq_lens, np.int32)
+    if sl.size != bt.shape[0]:
+        raise ValueError("table sizes disagree")
+    rep = TableReport()
+    st = load_library().kvfp4_check_paged_tables(_np_ptr(bt), KVFP4_I64 if bt.dtype == np.int64 else KVFP4_I32,
+                                                 bt.shape[1], bt.shape[1], _np_ptr(sl), sl.size, page_size, num_pages,
+                                                 max_seq_len, C.byref(rep))
+    _table_result(st, rep, "paged tables")
+
+
+def check_materialize_tables(block_tables, seq_lens, kv_page_indptr, page_size: int, num_pages: int,
+                             max_pages_per_seq: int, num_out_pages: int, uses_shared_paged_kv_idx: bool = True):
+    """Raise TableError unless every table value kv_materialize_fp8 would
+    use is in range."""
+    import numpy as np
+    bt = _host_ints(block_tables, np.int32)
+    sl, ip = _host_ints(seq_lens, np.int32), _host_ints(kv_page_indptr, np.int32)
+    if uses_shared_paged_kv_idx:
+        if bt.ndim != 2:
+            raise ValueError("shared block_tables are [batch, max_num_pages]")
+        cols, row, kvs = bt.shape[1], bt.shape[1], 0
+    else:
+        if bt.ndim != 3 or bt.shape[1] != 2:
+            raise ValueError("separate block_tables are [batch, 2, max_num_pages]")
+        cols, row, kvs = bt.shape[2], 2 * bt.shape[2], bt.shape[2]
+    if bt.shape[0] != sl.size or ip.size != sl.size + 1:
+        raise ValueError("table sizes disagree")
+    rep = TableReport()
+    st = load_library().kvfp4_check_materialize_tables(_np_ptr(bt), int(bool(uses_shared_paged_kv_idx)), row, kvs,
+                                                       cols, _np_ptr(sl), _np_ptr(ip), sl.size, page_size, num_pages,
+                                                       max_pages_per_seq, num_out_pages, C.byref(rep))
+    _table_result(st, rep, "materialize tables")

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libkvfp4.so")
 SOURCES = ["abi.hip", "append.hip", "dequant.hip", "materialize.hip", "global_scale.hip", "codec.hip",
-           "attention.hip"]
+           "attention.hip", "table_checks.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -607,6 +607,7 @@ const char *kvfp4_status_string(kvfp4_status_t status)
     case KVFP4_EALIGN: return "misaligned pointer or stride (16-byte alignment required)";
     case KVFP4_EUNSUPPORTED: return "unsupported request (sizes beyond the library's 32-bit index limits)";
     case KVFP4_ELAUNCH: return "HIP kernel launch failed (is the device gfx950?)";
+    case KVFP4_EVALUE: return "a table value is out of range (see the check's report)";
     case KVFP4_ESCRATCH: return "the call needs more than the no-allocation entry point's fixed scratch "
                                 "(KVFP4_NOALLOC_SCRATCH_BYTES); use the variant with a caller workspace";
     default: return "unknown status";
