@@ -30,7 +30,9 @@ def test_header_declares_the_boundary():
                             "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
                             "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc",
                             "kv_quantize_append_prepare", "kv_dequantize_paged_prepare",
-                            "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_status_string"])
+                            "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_check_append_tables",
+                            "kvfp4_check_paged_tables", "kvfp4_check_materialize_tables",
+                            "kvfp4_table_problem_string", "kvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -41,7 +43,7 @@ def test_library_exports_every_declared_symbol(B):
 
 
 def test_status_strings(B):
-    for s in range(6):
+    for s in range(7):
         assert B.status_string(s) and B.status_string(s) != "unknown status"
     assert B.status_string(99) == "unknown status"
 
