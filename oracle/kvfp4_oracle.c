@@ -676,17 +676,30 @@ struct materialize_ctx {
     uint8_t *out;
     int32_t *table;
     int64_t maxp;
+    int64_t batch;
 };
 
-static void materialize_requests(void *vctx, int64_t lo, int64_t hi)
+/* the threads split the reserved output pages p < indptr[batch]: page p
+ * belongs to the request b with indptr[b] <= p < indptr[b + 1] and is its
+ * page j = p - indptr[b], converted when j < ceil(seq_lens[b] / ps) */
+static void materialize_pages(void *vctx, int64_t lo, int64_t hi)
 {
     const struct materialize_ctx *a = (const struct materialize_ctx *)vctx;
     const orc_cache_t *c = a->c;
     const int64_t H = c->num_heads, D = c->head_dim, ps = c->page_size, nb = D / 16;
     const int64_t half_page = H * ps * D;        /* bytes of the K (or V) half of an FP8 page */
-    for (int64_t b = lo; b < hi; b++) {
+    for (int64_t p = lo; p < hi; p++) {
+        int64_t b = 0, top = a->batch;           /* the last b with indptr[b] <= p */
+        while (top - b > 1) {
+            int64_t mid = (b + top) / 2;
+            if (a->indptr[mid] <= p)
+                b = mid;
+            else
+                top = mid;
+        }
         int64_t n = (a->seq_lens[b] + ps - 1) / ps;
-        for (int64_t j = 0; j < n; j++) {
+        int64_t j = p - a->indptr[b];
+        if (j < n) {
             int64_t dst = (int64_t)a->indptr[b] + j + 1;
             int64_t kpage = a->bt[b * a->bt_row_stride + j];
             int64_t vpage = a->shared ? kpage : a->bt[b * a->bt_row_stride + a->bt_kv_stride + j];
@@ -755,8 +768,8 @@ int orc_materialize_fp8(const orc_cache_t *cache, int v_sf_interleaved,
         return -4;
     struct materialize_ctx ctx = {cache, v_sf_interleaved, block_tables, shared, bt_row_stride,
                                   bt_kv_stride, seq_lens, kv_page_indptr, out, fp8_block_tables,
-                                  max_pages_per_seq};
-    parallel_for(batch_size, threads, materialize_requests, &ctx);
+                                  max_pages_per_seq, batch_size};
+    parallel_for(kv_page_indptr[batch_size], threads, materialize_pages, &ctx);
     return 0;
 }
 
