@@ -1,9 +1,10 @@
 """GPU parity at the benchmark's full sizes and launch configurations.
 
-The device processes the whole workload. The oracle recomputes sampled
-requests (those it can finish in seconds), which must match bit for bit.
-Properties that hold at any size are checked on everything else: untouched
-tails, untouched pages, page 0 and the FP8 table.
+The device processes the whole workload and the oracle recomputes all of it
+(every request of the decode, prefill, materialize and 4over6 workloads), bit
+for bit: codes, scales, untouched cache bytes, dequantized values, untouched
+output tails, FP8 pages, page 0, pages past kv_page_indptr[-1] and the FP8
+table.
 """
 import numpy as np
 import pytest
@@ -27,37 +28,28 @@ def say(*a):
     print(*a, flush=True)
 
 
-def sample_requests(lens, k, rng):
-    """the shortest, the longest and k - 2 random others"""
-    order = np.argsort(lens)
-    pick = {int(order[0]), int(order[-1])}
-    while len(pick) < min(k, len(lens)):
-        pick.add(int(rng.integers(0, len(lens))))
-    return sorted(pick)
-
-
 def test_decode_workload_full_size(K, orc):
-    """64 requests (124,503 tokens): the sampled requests' history is
-    quantized by the oracle, the others' pages hold random bytes. The GPU
-    appends the 64 new tokens and dequantizes the whole context."""
+    """64 requests (124,503 tokens): the whole history is quantized by the
+    oracle; the GPU appends the 64 new tokens and dequantizes the whole
+    context, and every request is compared."""
     rng = np.random.default_rng(1002)
     ps, H, D, pool = 16, 8, 128, 20000
     old, new_len, indices, indptr, last, bt = W.decode_append_tables(rng, 64, 4096, pool, ps)
     a_k, a_v = W.head_scales(rng, H), W.head_scales(rng, H)
     cache = W.make_cache(rng, pool, ps, H, D, W.NHD)
-    srng = np.random.default_rng(7)
-    sample = sample_requests(new_len, 4, srng)
-    hist_rows = int(old[sample].sum())
+    for a in (cache.k_sf, cache.v_sf):              # unused pages: random bytes without NaN scales
+        a[(a & 0x7F) == 0x7F] = 0x7E
+    hist_rows = int(old.sum())
     hk = W.f32_to_bits(W.head_scaled_normal(rng, hist_rows, a_k, D), True)
     hv = W.f32_to_bits(W.head_scaled_normal(rng, hist_rows, a_v, D), True)
     nk = W.f32_to_bits(W.head_scaled_normal(rng, 64, a_k, D), True)
     nv = W.f32_to_bits(W.head_scaled_normal(rng, 64, a_v, D), True)
     gk = orc.global_scale(np.concatenate([hk.ravel(), nk.ravel()]), True)
     gv = orc.global_scale(np.concatenate([hv.ravel(), nv.ravel()]), True)
-    hb = np.concatenate([np.full(old[b], b, np.int32) for b in sample])
-    hp = np.concatenate([np.arange(old[b], dtype=np.int32) for b in sample])
-    say(f"decode full size: oracle history of requests {sample} ({hist_rows} rows)")
+    hb, hp = W.rows_for_positions(np.zeros(64, np.int64), old)
+    say(f"decode full size: oracle quantization of the whole history ({hist_rows} rows)")
     orc.quantize_append(cache, hk, hv, True, hb, hp, indices, indptr, last, gk, gv, threads=oracle_threads())
+    del hk, hv
 
     dev = DeviceCache(cache)
     bi, pos = np.arange(64, dtype=np.int32), old.astype(np.int32)
@@ -77,40 +69,37 @@ def test_decode_workload_full_size(K, orc):
     got = dev.to_host()
     for a, b in zip(got.bases, host.bases):          # the 64 new rows and every other byte
         assert np.array_equal(a, b)
-    kb, vb = tensor_bits(ok), tensor_bits(ov)
-    for b in range(64):                               # tails untouched everywhere
-        assert np.all(kb[b, new_len[b]:] == W.SENTINEL_16) and np.all(vb[b, new_len[b]:] == W.SENTINEL_16)
-    sl = np.zeros(64, np.int32)
-    sl[sample] = new_len[sample]
+    del got, dev
+    say("decode full size: oracle dequant of all 64 requests")
     wk = np.full((64, T, H, D), W.SENTINEL_16, np.uint16)
     wv = wk.copy()
-    orc.dequantize_paged(host, bt, sl, gk, gv, wk, wv, True, threads=oracle_threads())
-    for b in sample:
-        assert np.array_equal(kb[b], wk[b]), (b, first_mismatch(kb[b], wk[b]))
-        assert np.array_equal(vb[b], wv[b]), (b, first_mismatch(vb[b], wv[b]))
+    orc.dequantize_paged(host, bt, new_len.astype(np.int32), gk, gv, wk, wv, True, threads=oracle_threads())
+    kb = tensor_bits(ok)
+    del ok
+    assert np.array_equal(kb, wk), first_mismatch(kb, wk)           # tails keep the sentinel on both sides
+    del kb, wk
+    vb = tensor_bits(ov)
+    assert np.array_equal(vb, wv), first_mismatch(vb, wv)
 
 
 def test_prefill_workload_full_size(K, orc):
-    """16 x 8192 tokens, HND, int64 table, fp16 out: the sampled requests'
-    pages hold the oracle's quantization of bf16 N(0,1); the rest are random
-    bytes (dequant does not depend on how a page was written)."""
+    """16 x 8192 tokens, HND, int64 table, fp16 out: every page holds the
+    oracle's quantization of bf16 N(0,1); one request is shorter (its tail
+    stays untouched); all 16 requests are compared."""
     rng = np.random.default_rng(1003)
     B, T, ps, H, D = 16, 8192, 32, 8, 128
     n_pages = B * T // ps
     perm = rng.permutation(n_pages)
     bt = perm.reshape(B, T // ps).astype(np.int64)
-    cache = W.make_cache(rng, n_pages, ps, H, D, W.HND)
-    sample = [0, 9]
-    rows = len(sample) * T
-    xk = W.f32_to_bits(W.normal_rows(rng, (rows, H, D)), True)
-    xv = W.f32_to_bits(W.normal_rows(rng, (rows, H, D)), True)
+    cache = W.make_cache(rng, n_pages, ps, H, D, W.HND, fill="zero")
+    xk = W.f32_to_bits(W.normal_rows(rng, (B * T, H, D)), True)
+    xv = W.f32_to_bits(W.normal_rows(rng, (B * T, H, D)), True)
     gk, gv = orc.global_scale(xk, True), orc.global_scale(xv, True)
-    sub_indices = np.concatenate([perm[b * (T // ps):(b + 1) * (T // ps)] for b in sample]).astype(np.int32)
-    sub_indptr = (np.arange(len(sample) + 1) * (T // ps)).astype(np.int32)
-    bi, pos = W.rows_for_positions(np.zeros(len(sample), np.int64), np.full(len(sample), T))
-    say("prefill full size: oracle quantization of the sampled requests")
-    orc.quantize_append(cache, xk, xv, True, bi, pos, sub_indices, sub_indptr, np.full(len(sample), ps, np.int32),
-                        gk, gv, threads=oracle_threads())
+    bi, pos = W.rows_for_positions(np.zeros(B, np.int64), np.full(B, T))
+    say("prefill full size: oracle quantization of all 16 requests")
+    orc.quantize_append(cache, xk, xv, True, bi, pos, perm.astype(np.int32), (np.arange(B + 1) * (T // ps)).astype(np.int32),
+                        np.full(B, ps, np.int32), gk, gv, threads=oracle_threads())
+    del xk, xv
     dev = DeviceCache(cache)
     ok = torch.full((B, T, H, D), W.SENTINEL_16 - 65536, dtype=torch.int16, device="cuda").view(torch.float16)
     ov = ok.clone()
@@ -120,16 +109,18 @@ def test_prefill_workload_full_size(K, orc):
     K.kv_dequantize_paged(dev.cache, torch.from_numpy(bt).cuda(), i32(lens), torch.tensor([gk], device="cuda"),
                           torch.tensor([gv], device="cuda"), ok, ov)
     torch.cuda.synchronize()
-    kb, vb = tensor_bits(ok), tensor_bits(ov)
-    assert np.all(kb[3, 5000:] == W.SENTINEL_16) and np.all(vb[3, 5000:] == W.SENTINEL_16)
-    sl = np.zeros(B, np.int32)
-    sl[sample] = lens[sample]
+    del dev
+    say("prefill full size: oracle dequant of all 16 requests")
     wk = np.full((B, T, H, D), W.SENTINEL_16, np.uint16)
     wv = wk.copy()
-    orc.dequantize_paged(cache, bt, sl, gk, gv, wk, wv, False, threads=oracle_threads())
-    for b in sample:
-        assert np.array_equal(kb[b], wk[b]), (b, first_mismatch(kb[b], wk[b]))
-        assert np.array_equal(vb[b], wv[b]), (b, first_mismatch(vb[b], wv[b]))
+    orc.dequantize_paged(cache, bt, lens, gk, gv, wk, wv, False, threads=oracle_threads())
+    kb = tensor_bits(ok)
+    del ok
+    assert np.all(kb[3, 5000:] == W.SENTINEL_16)
+    assert np.array_equal(kb, wk), first_mismatch(kb, wk)
+    del kb, wk
+    vb = tensor_bits(ov)
+    assert np.array_equal(vb, wv), first_mismatch(vb, wv)
 
 
 def test_materialize_workload_full_size(K, orc):
@@ -156,21 +147,13 @@ def test_materialize_workload_full_size(K, orc):
         n = need[b]
         assert np.array_equal(gtab[b, :n], wl.kv_page_indptr[b] + np.arange(n) + 1)
         assert np.all(gtab[b, n:] == -1)
-    # the shortest request and the two nearest the median length (the oracle
-    # converts one element at a time; the longest request alone is ~66M)
-    order = np.argsort(wl.seq_lens)
-    sample = sorted({int(order[0]), int(order[15]), int(order[16])})
-    sl = np.zeros(32, np.int32)
-    sl[sample] = wl.seq_lens[sample]
     want = np.full_like(got, W.SENTINEL_FP8)
     wtab = np.full_like(gtab, -1)
-    say(f"materialize full size: oracle for requests {sample} ({int(need[sample].sum())} pages)")
-    orc.materialize_fp8(c, wl.block_tables, sl, wl.kv_page_indptr, want, wtab, shared=False,
+    say(f"materialize full size: oracle for all 32 requests ({int(need.sum())} pages)")
+    orc.materialize_fp8(c, wl.block_tables, wl.seq_lens, wl.kv_page_indptr, want, wtab, shared=False,
                         v_sf_interleaved=True, threads=oracle_threads())
-    for b in sample:
-        pages = wl.kv_page_indptr[b] + np.arange(need[b]) + 1
-        assert np.array_equal(got[pages], want[pages]), b
-        assert np.array_equal(gtab[b], wtab[b])
+    assert np.array_equal(got, want), first_mismatch(got, want)
+    assert np.array_equal(gtab, wtab)
 
 
 @pytest.mark.parametrize("mode", ["MSE", "MAE"])
@@ -202,12 +185,10 @@ def test_four_over_six_workload_full_size(K, orc, mode):
     got = dev.to_host()
     for name, a, b in zip(("k_data", "v_data", "k_sf", "v_sf"), got.bases, host.bases):
         assert np.array_equal(a, b), (name, first_mismatch(a, b))
-    sample = [2, 11]
-    sl = np.zeros(B, np.int32)
-    sl[sample] = T
+    say(f"4over6 {mode} full size: oracle dequant of all 16 requests")
     wk = np.full((B, T, H, D), W.SENTINEL_16, np.uint16)
     wv = wk.copy()
-    orc.dequantize_paged(host, wl.block_tables, sl, gk, gv, wk, wv, True, threads=oracle_threads())
+    orc.dequantize_paged(host, wl.block_tables, wl.seq_lens, gk, gv, wk, wv, True, threads=oracle_threads())
     kb, vb = tensor_bits(ok), tensor_bits(ov)
-    for b in sample:
-        assert np.array_equal(kb[b], wk[b]) and np.array_equal(vb[b], wv[b]), b
+    assert np.array_equal(kb, wk), first_mismatch(kb, wk)
+    assert np.array_equal(vb, wv), first_mismatch(vb, wv)
