@@ -5,7 +5,8 @@
 // flashinfer.quantization page).
 //
 // fp32 order (bit-exact with the reference reading):
-//   sf  = amax / fp32(C * g)                 (IEEE division)
+//   sf  = amax / fp32(C * g)                 (IEEE division; scale_code
+//                                             reaches the same code faster)
 //   s   = E4M3_RNE(min(sf, clamp_C))
 //   dec = fp32(E4M3(s) * g),  inv = dec ? fp32(1 / dec) : 0
 //   c_i = E2M1_RNE_sat(fp32(x_i * inv))
@@ -78,6 +79,64 @@ __device__ __forceinline__ float block_error(const float x[16], uint2 codes, flo
     return t[0] + t[1];
 }
 
+// A quick stand-in for a candidate's error, to decide the 4over6 choice
+// without the exact tree in almost every block: each difference is one fused
+// x_i - dec * e2m1_i (rounded once) and the terms (its square for MSE, its
+// magnitude for MAE) are accumulated by a chain of fused multiply-adds /
+// adds. With u = 2^-24, S the exact sum of the exact terms and q_i = dec *
+// e2m1_i (|q_i| <= 6 dec):
+//   MSE: pairwise tree vs S within 5.0001u S; the fused differences move the
+//        sum by at most 10.001u S + 1.0001u sum(q_i^2) <= ... + 576.06u dec^2;
+//        the chain adds 16.0001u S': in all within 31.01u S + 577u dec^2.
+//   MAE: tree within 4.0001u S, the differences within 2.0001u S + 96.01u
+//        dec, the chain 15.001u S': in all within 21.01u S + 97u dec.
+// Results in fp32's subnormal range add at most 2^-140 of absolute error.
+template <bool MSE>
+__device__ __forceinline__ float error_chain(const float x[16], uint2 codes, float dec)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const uint32_t w = half ? codes.y : codes.x;
+        const f32x2 v0 = fp4x2_to_f32x2<0>(w), v1 = fp4x2_to_f32x2<1>(w);
+        const f32x2 v2 = fp4x2_to_f32x2<2>(w), v3 = fp4x2_to_f32x2<3>(w);
+        const float v[8] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float d = __builtin_fmaf(-dec, v[i], x[8 * half + i]);
+            acc = MSE ? __builtin_fmaf(d, d, acc) : acc + fabsf(d);
+        }
+    }
+    return acc;
+}
+
+// 4over6 choice for the fp32 MSE / MAE recipes: amax/4 iff its pairwise-tree
+// error is strictly lower. The chains decide it whenever they are further
+// apart than m, which is at least the sum of both chains' worst distances to
+// their trees above (the constants are generous: 2^-18 >= 64u covers 31.01u
+// with room for m's own roundings, 2^-14 >= 1024u covers 577u, 2^-19 >= 32u
+// covers 21.01u, 2^-17 >= 128u covers 97u; the 2^-126 floor covers the
+// subnormal term). Both chains zero means every difference is zero, so both
+// trees are zero: a tie, amax/6 stays. Anything closer, and an inf on either
+// side (m is then inf or NaN and neither test passes), is decided by the
+// trees themselves, so the choice is always the trees' choice.
+template <bool MSE>
+__device__ __forceinline__ bool chain_takes_amax4(const float x[16], uint2 codes6, float dec6, uint2 codes4,
+                                                  float dec4)
+{
+    const float f6 = error_chain<MSE>(x, codes6, dec6);
+    const float f4 = error_chain<MSE>(x, codes4, dec4);
+    if (f4 == 0.0f && f6 == 0.0f)
+        return false;
+    const float m = MSE ? fmaxf(0x1p-18f * (f4 + f6) + 0x1p-14f * (dec4 * dec4 + dec6 * dec6), 0x1p-126f)
+                        : fmaxf(0x1p-19f * (f4 + f6) + 0x1p-17f * (dec4 + dec6), 0x1p-126f);
+    if (f6 - f4 > m)
+        return true;
+    if (f4 - f6 > m)
+        return false;
+    return block_error<MSE>(x, codes4, dec4) < block_error<MSE>(x, codes6, dec6);
+}
+
 // fp32 value -> nearest fp16 value (ties to even), back in fp32 (exact)
 __device__ __forceinline__ float round_f16(float v) { return (float)(_Float16)v; }
 
@@ -144,31 +203,50 @@ __device__ __forceinline__ float block_error_fp16(const f16x2 xh[8], uint2 codes
 // RECIPE: 0 standard, 1 4over6 MSE, 2 4over6 MAE, 3 MSE in fp16, 4 MAE in
 // fp16. x holds the block, amax its largest magnitude; returns the packed
 // codes and sets the scale byte.
+// E4M3_RNE(min(fp32(amax / t), clamp)), the block-scale code, for amax >= 0
+// and t = fp32(C * g) > 0 (rt = fp32(1 / t)). q = fp32(amax * rt) is within
+// 3.0001u (amax / t) of the quotient, so fp32(amax / t) and q are at most 4
+// bit patterns apart, and they round to the same E4M3 code unless an E4M3
+// rounding midpoint lies between them. Normal E4M3 midpoints (1.mmm1 x 2^e)
+// have bit 19 set and bits 18..0 clear in fp32, so a q whose low 20 bits are
+// more than 16 away from 0x80000 has none within reach; below 2^-6 (the
+// subnormal E4M3 range, where midpoints fall elsewhere) only q < 2^-11, where
+// both give code 0, is taken directly. Everything else divides in IEEE fp32,
+// which is then exactly the quotient the arithmetic defines. Clamping cannot
+// separate the two either: the clamp is itself an E4M3 value.
+__device__ __forceinline__ uint32_t scale_code(float amax, float t, float rt, float clamp)
+{
+    const float q = amax * rt;
+    const uint32_t low = __float_as_uint(q) & 0xFFFFFu;
+    const bool direct = q < 0x1p-11f || (q >= 0x1p-6f && low - 0x7FFF0u > 32u);
+    float sf = q;
+    if (__builtin_expect(!direct, 0))
+        sf = amax / t;
+    return f32_to_e4m3_hw(fminf(sf, clamp));
+}
+
 template <int RECIPE>
 __device__ __forceinline__ uint2 quantize_block(const float x[16], float amax, float g, float clamp6,
                                                 const float *dec_tab, const float *inv_tab, uint32_t &s_out)
 {
-    const float sf6 = amax / (6.0f * g);
-    uint32_t s = f32_to_e4m3_hw(fminf(sf6, clamp6));
+    const float t6 = 6.0f * g, t4 = 4.0f * g;
+    uint32_t s = scale_code(amax, t6, 1.0f / t6, clamp6);
     uint2 codes = encode16(x, inv_tab[s]);
     if (RECIPE != 0) {
         const float dec = dec_tab[s];
-        const float sf4 = amax / (4.0f * g);
-        const uint32_t s4 = f32_to_e4m3_hw(fminf(sf4, 448.0f));
+        const uint32_t s4 = scale_code(amax, t4, 1.0f / t4, 448.0f);
         const float dec4 = dec_tab[s4];
         const uint2 codes4 = encode16(x, inv_tab[s4]);
         constexpr bool kMse = RECIPE == 1 || RECIPE == 3;
-        float e6, e4;
+        bool take4;
         if (RECIPE >= 3) {
             f16x2 xh[8];
             inputs_fp16(x, xh);
-            e6 = block_error_fp16<kMse>(xh, codes, dec);
-            e4 = block_error_fp16<kMse>(xh, codes4, dec4);
+            take4 = block_error_fp16<kMse>(xh, codes4, dec4) < block_error_fp16<kMse>(xh, codes, dec);
         } else {
-            e6 = block_error<kMse>(x, codes, dec);
-            e4 = block_error<kMse>(x, codes4, dec4);
+            take4 = chain_takes_amax4<kMse>(x, codes, dec, codes4, dec4);
         }
-        if (e4 < e6) {                     // an inf or NaN error never wins
+        if (take4) {                       // an inf or NaN error never wins
             s = s4;
             codes = codes4;
         }
