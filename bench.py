@@ -288,17 +288,25 @@ def leg_prefill_dequant(env, iters, warmup, samples):
                 "8 heads, head_dim 128, HND, int64 block table, fp16 out", bytes=nbytes, **rates(nbytes, r))
 
 
-def materialize_replica(env, seed=1004, samples=None):
+def materialize_replica(env, seed=1004, samples=None, placement="shuffled"):
+    """The materialize workload. `placement` "shuffled" (the workload): K and
+    V pages from independent permutations of the pool, separate tables;
+    "shuffled_shared": one permutation and one shared table for K and V;
+    "request_order": request b's pages are consecutive ids (shared table)."""
     torch, K = env.torch, env.K
     import workloads as W
     ps, H, D = 16, 8, 128
     rng = np.random.default_rng(seed)
-    lens, P, maxp, bt, indptr = W.materialize_tables(rng, 32, 128, 32768, ps, shared=False, compact=True)
+    shared = placement != "shuffled"
+    lens, P, maxp, bt, indptr = W.materialize_tables(rng, 32, 128, 32768, ps, shared=shared, compact=True)
+    if placement == "request_order":
+        bt = np.where(np.arange(maxp)[None, :] < np.diff(indptr)[:, None],
+                      indptr[:-1, None] + np.arange(maxp)[None, :], 0).astype(np.int32)
     cache, keep = env.cache(P, ps, H, D, K.KVFP4_HND, seed, data_pad=256)
     out = torch.empty((P + 1, 2, H, ps, D), dtype=torch.float8_e4m3fn, device=env.dev)
     tab = torch.zeros((32, maxp), dtype=torch.int32, device=env.dev)
     bt_t, sl, ip = env.i32(bt), env.i32(lens), env.i32(indptr)
-    mat = K.NVFP4KVMaterializer(H, ps, D, env.dev, uses_shared_paged_kv_idx=False)
+    mat = K.NVFP4KVMaterializer(H, ps, D, env.dev, uses_shared_paged_kv_idx=shared)
     kd, vd, ks, vs = cache.tensors
     nbytes = materialize_bytes(lens, ps, H, D, 32)
     fn = lambda: mat.run(kd, vd, ks, vs, bt_t, sl, ip, out=out, fp8_block_tables=tab)   # noqa: E731
@@ -312,12 +320,13 @@ def materialize_replica(env, seed=1004, samples=None):
         reqs = []
         for b in picks:
             n = int((lens[b] + ps - 1) // ps)
-            pages = np.concatenate([bt[b, 0, :n], bt[b, 1, :n]])
+            pages = np.concatenate([bt[b, :n], bt[b, :n]] if shared else [bt[b, 0, :n], bt[b, 1, :n]])
             dst = int(indptr[b]) + 1
             reqs.append(SimpleNamespace(b=b, n=n, cache=gather_pages(cache, pages), len=int(lens[b]),
                                         out=out.view(torch.uint8)[dst:dst + n].cpu().numpy(),
                                         table=tab[b].cpu().numpy(), dst=dst))
-        samples.add("materialize", "materialize workload: shortest, median and longest requests", reqs=reqs,
+        what = "materialize workload" if placement == "shuffled" else f"materialize page-order context ({placement})"
+        samples.add("materialize", f"{what}: shortest, median and longest requests", reqs=reqs,
                     page0=out.view(torch.uint8)[0].cpu().numpy(), H=H, ps=ps, D=D, maxp=maxp)
     return fn, nbytes, (cache, keep, out)
 
@@ -332,6 +341,27 @@ def leg_materialize(env, iters, warmup, samples):
     return dict(kernel="kv_materialize_fp8", workload="materialize_fp8: 32 requests, lengths log-uniform "
                 "[128, 32768], page_size 16, 8 heads, head_dim 128, HND, data page stride 8448 B, separate K/V "
                 "tables, compact kv_page_indptr, interleaved V scales", bytes=nbytes, **rates(nbytes, r))
+
+
+def leg_materialize_page_order(env, iters, warmup, samples):
+    """Context, not a workload of the method: the materialize workload's
+    lengths and bytes with three page placements (separate shuffled K and V
+    tables, as timed above; one shuffled table shared by K and V; pages in
+    request order). The spread is what placement costs at the DRAM level."""
+    torch = env.torch
+    res = {"workload": "materialize_fp8 lengths and geometry; pages shuffled with separate K/V tables, shuffled "
+                       "with a shared table, or in request order"}
+    for placement in ("shuffled", "shuffled_shared", "request_order"):
+        fns, keep = [], []
+        for i in range(replicas_for(222_000_000)):
+            fn, nbytes, k = materialize_replica(env, 1004, samples if i == 0 else None, placement)
+            fns.append(fn)
+            keep.append(k)
+        res[placement] = dict(kernel="kv_materialize_fp8", bytes=nbytes,
+                              **rates(nbytes, env.steady(fns, iters, warmup)))
+        del fns, keep
+        torch.cuda.empty_cache()
+    return res
 
 
 def four_over_six_replica(env, seed=1005):
@@ -989,7 +1019,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--leg-iters", type=int, default=50)
     ap.add_argument("--legs", default="prefill,materialize,four_over_six,contiguous,pool_quantize,attention,"
-                                      "page_order,copy,host_cost",
+                                      "page_order,materialize_page_order,copy,host_cost",
                     help="comma list of legs to run after the headline step (empty: none)")
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle's timing (parity still runs)")
@@ -1075,6 +1105,8 @@ def main():
         legs["decode_attention"] = leg_attention(env, args.leg_iters, 5, samples)
     if "page_order" in chosen:
         legs["page_order_context"] = leg_page_order(env, args.leg_iters, 5, samples)
+    if "materialize_page_order" in chosen:
+        legs["materialize_page_order_context"] = leg_materialize_page_order(env, args.leg_iters, 5, samples)
     if "copy" in chosen:
         # also the known-size copy that calibrates the byte counters
         legs["copy_context"] = leg_copy(env, 1 << 29, args.leg_iters, 5)

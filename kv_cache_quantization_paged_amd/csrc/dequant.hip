@@ -42,6 +42,13 @@ constexpr int kBatchHnd = 8;
 template <bool HND>
 constexpr int batch_of() { return HND ? kBatchHnd : kBatchNhd; }
 constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (grid size in work-items stays below 2^32)
+// Workgroups are dealt to the 8 XCDs in turn. Giving each XCD runs of 4
+// consecutive pages (all their parts) instead of spreading a page's parts
+// over 4 XCDs measured 4-5% faster on 64 full 4096-token requests with
+// shuffled pages (228 vs 238 us) and the same on the decode workload.
+// Ordering the items page-major (page j of every request, then page j + 1)
+// was 30% slower: the output is written best in request order.
+constexpr int kXcdChunk = 4;
 
 struct DequantArgs {
     const uint8_t *data[2];
@@ -54,9 +61,24 @@ struct DequantArgs {
     int32_t pages_per_req;   // ceil(T / ps)
     int32_t parts;           // work items per page: ceil(ps * H * D / 8 / (kBatch * kThreads))
     int32_t num_items;       // B * pages_per_req * parts
+    int32_t xcd_chunk;       // items per XCD run (0: workgroup i takes item i)
 };
 
-// 4 code bytes (8 values) -> 4 packed 16-bit pairs
+// workgroup -> first item. Workgroups are dealt to the 8 XCDs in turn (XCD
+// = blockIdx % 8); with xcd_chunk C, the k-th workgroup of XCD x takes item
+// (k / C) * 8C + x * C + k % C, so each XCD works through runs of C
+// consecutive items. A bijection on [0, grid) when the grid is a multiple of
+// 8C.
+__device__ __forceinline__ int first_item(int chunk)
+{
+    const int bid = (int)blockIdx.x;
+    if (chunk == 0)
+        return bid;
+    const int x = bid & 7, k = bid >> 3;
+    return (k / chunk) * 8 * chunk + x * chunk + k % chunk;
+}
+
+
 template <bool BF16>
 __device__ __forceinline__ u32x4 decode_chunk(uint32_t codes, float dec)
 {
@@ -109,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const 
     const uint32_t page_sf_bytes = (uint32_t)(a.ps * a.H * nb);
 
     // one item per workgroup (the loop only repeats for more than kMaxGrid)
-    for (int item = blockIdx.x; item < a.num_items; item += gridDim.x) {
+    for (int item = first_item(a.xcd_chunk); item < a.num_items; item += gridDim.x) {
         const int pair = item / a.parts;
         const int part = item - pair * a.parts;
         const int b = pair / a.pages_per_req;
@@ -332,7 +354,13 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
         return hipErrorInvalidValue;
     a.num_items = (int32_t)items;
     const DequantPtrs p = {block_tables, seq_lens, k_scale, v_scale};
-    const int grid = (int)(items < kMaxGrid ? items : kMaxGrid);
+    a.xcd_chunk = 0;
+    int grid = (int)(items < kMaxGrid ? items : kMaxGrid);
+    if (kXcdChunk > 0 && items < kMaxGrid) {
+        const int64_t run = 8 * (int64_t)kXcdChunk * a.parts;
+        a.xcd_chunk = kXcdChunk * a.parts;
+        grid = (int)((items + run - 1) / run * run);
+    }
     const bool hnd = c.layout == KVFP4_HND;
     if (hnd) {
         // the LDS path: chunks per token a power of two dividing the item,

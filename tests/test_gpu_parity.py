@@ -247,6 +247,33 @@ def test_dequant_stacked_padded_and_empty(K, orc, geom):
     assert np.all(tensor_bits(zk) == 7) and np.all(tensor_bits(zv) == 7)
 
 
+@pytest.mark.parametrize("layout,geom", [(W.NHD, (16, 2, 64)), (W.HND, (8, 2, 256)), (W.NHD, (5, 3, 48))])
+def test_dequant_many_requests(K, orc, layout, geom):
+    """more requests than a wavefront has lanes (the kernel finds each
+    work item's request with a scan over per-lane request groups), with empty,
+    clamped and single-token requests among them"""
+    ps, H, D = geom
+    seed = 1300 + ps + H
+    cache, bt, lens, T = dequant_case(seed, layout, ps, H, D, B=150, pool=40)
+    rng = np.random.default_rng(seed + 1)
+    lens[rng.integers(3, 150, 30)] = 0
+    lens[rng.integers(3, 150, 10)] = T + 3
+    B = len(lens)
+    ok = np.full((B, T, H, D), W.SENTINEL_16, np.uint16)
+    ov = ok.copy()
+    orc.dequantize_paged(cache, bt, lens, 0.5, 0.125, ok, ov, True, threads=oracle_threads())
+    dev = DeviceCache(cache)
+    dk = torch.full((B, T, H, D), W.SENTINEL_16 - 65536, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dv = dk.clone()
+    one = lambda v: torch.tensor([v], dtype=torch.float32, device="cuda")  # noqa: E731
+    say(f"dequant many requests layout={layout} geom={geom} seed={seed} B={B} T={T}")
+    K.kv_dequantize_paged(dev.cache, i32(bt), i32(lens), one(0.5), one(0.125), dk, dv)
+    torch.cuda.synchronize()
+    gk_bits, gv_bits = tensor_bits(dk), tensor_bits(dv)
+    assert np.array_equal(gk_bits, ok), first_mismatch(gk_bits, ok)
+    assert np.array_equal(gv_bits, ov), first_mismatch(gv_bits, ov)
+
+
 def test_append_then_dequant_round_trip(K, orc):
     """Tiny round trip workload: append every token, then dequantize into
     sentinel-filled outputs; both stages bit-exact against the oracle."""
