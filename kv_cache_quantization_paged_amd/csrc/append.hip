@@ -161,11 +161,9 @@ __global__ __launch_bounds__(kThreads, row_workgroups_per_cu(RECIPE)) void appen
         int slot, hc;
         u32x4 in[2][2];
     };
+    // the input loads first: they need only the row, so they are in flight
+    // while the request -> indptr -> page chain of scalar loads resolves
     auto fetch = [&](int64_t r, int slice, Slice &sl) {
-        const int b = batch_indices[r];
-        const int p = positions[r];
-        sl.page = kv_indices[kv_indptr[b] + p / a.ps];
-        sl.slot = p % a.ps;
         sl.hc = slice * 64 + lane;                           // this lane's block of the row
 #pragma unroll
         for (int kv = 0; kv < 2; ++kv) {
@@ -173,6 +171,10 @@ __global__ __launch_bounds__(kThreads, row_workgroups_per_cu(RECIPE)) void appen
             sl.in[kv][0] = buf_load_u32x4(in, (uint32_t)sl.hc * 32u);
             sl.in[kv][1] = buf_load_u32x4(in, (uint32_t)sl.hc * 32u + 16u);
         }
+        const int b = batch_indices[r];
+        const int p = positions[r];
+        sl.page = kv_indices[kv_indptr[b] + p / a.ps];
+        sl.slot = p % a.ps;
     };
     auto quantize = [&](const Slice &cur) {
         const int h = cur.hc / nb, c = cur.hc - (cur.hc / nb) * nb;
