@@ -27,6 +27,8 @@ the host's full core count and at one thread.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import json
 import os
 import statistics
@@ -122,16 +124,32 @@ class Env:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sizes]
         torch.cuda.synchronize()
         i = 0
-        for (ev0, ev1), n in zip(evs, sizes):
-            ev0.record()
-            for _ in range(n):
-                fns[i % len(fns)]()
-                i += 1
-            ev1.record()
-        torch.cuda.synchronize()
+        with quiet_host():
+            for (ev0, ev1), n in zip(evs, sizes):
+                ev0.record()
+                for _ in range(n):
+                    fns[i % len(fns)]()
+                    i += 1
+                ev1.record()
+            torch.cuda.synchronize()
         per = [a.elapsed_time(b) / n for (a, b), n in zip(evs, sizes)]
         total = sum(a.elapsed_time(b) for a, b in evs)
         return total / iters, statistics.median(per)
+
+
+@contextlib.contextmanager
+def quiet_host():
+    """Python's cyclic garbage collector off (after one collection) while
+    launches are being timed: a collection inside a timed batch stalls the
+    host that enqueues the launches, and the GPU idles for it (seen as one
+    batch of a leg taking 20-40 ms longer right after another leg's buffers
+    were freed)."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 
 def student_t3(env, shape, gen):
@@ -1058,11 +1076,12 @@ def main():
     # kernels adds a few microseconds of gap to every step (measured: 127 vs
     # 121 us per step), which no serving loop has
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with quiet_host():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     # the dequant's own launch time, for the roofline: as many dequant
     # launches as timed steps, over the same replicas, back to back in three
