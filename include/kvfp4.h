@@ -314,11 +314,12 @@ kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const v
  * length to the bt_cols * page_size tokens its table row addresses and treat
  * a negative one as 0, so no access leaves the caller's buffers and a bad
  * length changes only its own request's output.
- * q and out are [batch_size, num_qo_heads, 128] of q_dtype (bf16 or fp16),
- * contiguous, 16-byte aligned; block_tables and seq_lens int32. head_dim
- * must be 128 and num_qo_heads / num_kv_heads at most 16
+ * q and out are [batch_size, num_qo_heads, head_dim] of q_dtype (bf16 or
+ * fp16), contiguous, 16-byte aligned; block_tables and seq_lens int32.
+ * head_dim must be 64, 128 or 256 and num_qo_heads / num_kv_heads at most 16
  * (KVFP4_EUNSUPPORTED otherwise); scale bases and scale page strides must be
- * even. Scores and the softmax are fp32. The products run in fp16: decoded
+ * even for head_dim 128 and multiples of 4 for head_dim 256. Scores and the
+ * softmax are fp32. The products run in fp16: decoded
  * K and V are exact there; a bf16 query row is scaled by a power of two that
  * puts its largest magnitude in [2^14, 2^15) and converted (exact except for
  * components more than 2^38 below that largest one); the probabilities are
@@ -326,7 +327,7 @@ kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const v
  * The sequence is split into 256-token pieces whose partial softmax results
  * go to `workspace` (caller-owned device memory, 16-byte aligned, at least
  * kv_decode_attention_workspace_size(batch_size, num_kv_heads, num_qo_heads,
- * bt_cols, page_size) bytes, no initial contents needed; it is scratch for the
+ * bt_cols, page_size, head_dim) bytes, no initial contents needed; it is scratch for the
  * duration of the call's stream work, so concurrent calls need their own).
  */
 kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void *q, int32_t q_dtype,
@@ -336,9 +337,10 @@ kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void 
                                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Bytes of workspace kv_decode_attention needs for these sizes (-1 for
- * invalid sizes). */
+ * invalid sizes): batch_size * num_kv_heads * ceil(bt_cols * page_size / 256)
+ * partials of (2 + head_dim) * (num_qo_heads / num_kv_heads) floats. */
 int64_t kv_decode_attention_workspace_size(int32_t batch_size, int32_t num_kv_heads, int32_t num_qo_heads,
-                                           int32_t bt_cols, int32_t page_size);
+                                           int32_t bt_cols, int32_t page_size, int32_t head_dim);
 
 /*
  * kv_decode_attention_noalloc - kv_decode_attention for callers that cannot

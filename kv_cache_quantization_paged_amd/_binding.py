@@ -97,7 +97,7 @@ def load_library():
     lib.kv_decode_attention_noalloc.argtypes = [C.POINTER(PagedCacheDesc), P, i32, i32, P, i64, i32, P, i32, P, P,
                                                 f32, P, P]
     lib.kv_decode_attention_workspace_size.restype = i64
-    lib.kv_decode_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.kv_decode_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.kv_quantize_append_prepare.restype = i32
     lib.kv_quantize_append_prepare.argtypes = [P] + lib.kv_quantize_append.argtypes[:-1]
     lib.kv_dequantize_paged_prepare.restype = i32
@@ -470,9 +470,9 @@ def kv_quantize_paged_cache(cache: PagedCache, k_in, v_in, k_scale, v_scale, rec
 
 
 def kv_decode_attention_workspace_size(batch: int, num_kv_heads: int, num_qo_heads: int, max_pages: int,
-                                       page_size: int) -> int:
+                                       page_size: int, head_dim: int = 128) -> int:
     return int(load_library().kv_decode_attention_workspace_size(batch, num_kv_heads, num_qo_heads, max_pages,
-                                                                 page_size))
+                                                                 page_size, head_dim))
 
 
 def _attention_args(cache: PagedCache, q, block_tables, seq_lens, k_scale, v_scale, out):

@@ -522,7 +522,8 @@ kvfp4_status_t check_attention(const kvfp4_paged_cache_t *cache, const void *q, 
         return KVFP4_EINVAL;
     if (bt_cols < 0 || bt_row_stride < bt_cols || !isfinite(sm_scale))
         return KVFP4_EINVAL;
-    if (cache->head_dim != 128 || num_qo_heads / cache->num_kv_heads > 16)
+    const int D = cache->head_dim;
+    if ((D != 64 && D != 128 && D != 256) || num_qo_heads / cache->num_kv_heads > 16)
         return KVFP4_EUNSUPPORTED;
     if (batch_size == 0) {
         *nothing_to_do = true;
@@ -534,8 +535,11 @@ kvfp4_status_t check_attention(const kvfp4_paged_cache_t *cache, const void *q, 
         return KVFP4_EUNSUPPORTED;
     if (!aligned16(q) || !aligned16(out))
         return KVFP4_EALIGN;
-    if ((((uintptr_t)cache->k_sf | (uintptr_t)cache->v_sf) & 1u) ||
-        ((cache->k_sf_page_stride | cache->v_sf_page_stride) & 1))
+    // a lane reads D / 64 K scale bytes of a row at once (head_dim 128: 2,
+    // 256: 4)
+    const uint64_t sf_align = D >= 128 ? (uint64_t)D / 64 - 1 : 0;
+    if ((((uintptr_t)cache->k_sf | (uintptr_t)cache->v_sf) & sf_align) ||
+        ((uint64_t)(cache->k_sf_page_stride | cache->v_sf_page_stride) & sf_align))
         return KVFP4_EALIGN;
     return KVFP4_OK;
 }
@@ -558,7 +562,7 @@ kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void 
     if (!workspace)
         return KVFP4_EINVAL;
     if (workspace_bytes < decode_attention_workspace_bytes(batch_size, cache->num_kv_heads, num_qo_heads, bt_cols,
-                                                           cache->page_size))
+                                                           cache->page_size, cache->head_dim))
         return KVFP4_EINVAL;
     if (!aligned16(workspace))
         return KVFP4_EALIGN;
@@ -578,8 +582,8 @@ kvfp4_status_t kv_decode_attention_noalloc(const kvfp4_paged_cache_t *cache, con
                                        seq_lens, batch_size, k_scale, v_scale, sm_scale, out, &empty);
     if (s != KVFP4_OK || empty)
         return s;
-    if (decode_attention_workspace_bytes(batch_size, cache->num_kv_heads, num_qo_heads, bt_cols,
-                                         cache->page_size) > kNoAllocScratchBytes)
+    if (decode_attention_workspace_bytes(batch_size, cache->num_kv_heads, num_qo_heads, bt_cols, cache->page_size,
+                                         cache->head_dim) > kNoAllocScratchBytes)
         return KVFP4_ESCRATCH;
     void *ws = nullptr;
     hipError_t e = noalloc_scratch(&ws);
@@ -591,12 +595,12 @@ kvfp4_status_t kv_decode_attention_noalloc(const kvfp4_paged_cache_t *cache, con
 }
 
 int64_t kv_decode_attention_workspace_size(int32_t batch_size, int32_t num_kv_heads, int32_t num_qo_heads,
-                                           int32_t bt_cols, int32_t page_size)
+                                           int32_t bt_cols, int32_t page_size, int32_t head_dim)
 {
     if (batch_size < 0 || num_kv_heads <= 0 || num_qo_heads <= 0 || num_qo_heads % num_kv_heads != 0 ||
-        bt_cols < 0 || page_size <= 0)
+        bt_cols < 0 || page_size <= 0 || head_dim <= 0)
         return -1;
-    return decode_attention_workspace_bytes(batch_size, num_kv_heads, num_qo_heads, bt_cols, page_size);
+    return decode_attention_workspace_bytes(batch_size, num_kv_heads, num_qo_heads, bt_cols, page_size, head_dim);
 }
 
 const char *kvfp4_status_string(kvfp4_status_t status)

@@ -56,7 +56,7 @@ namespace kvfp4 {
 
 namespace {
 
-constexpr int kD = 128;                     // head_dim
+constexpr int kD = 128;                     // head_dim of the LDS-staged loader
 constexpr int kTile = 32;                   // tokens per MFMA tile
 constexpr int kWaves = 4;                   // wavefronts per workgroup
 constexpr int kWaveTiles = 2;               // tiles per wave
@@ -75,7 +75,7 @@ struct AttnArgs {
     int64_t sf_stride[2];
     const uint16_t *q;
     uint16_t *out;
-    float *ws;                // [B][H][splits] partials: m[G], l[G], o[G][128]
+    float *ws;                // [B][H][splits] partials: m[G], l[G], o[G][head_dim]
     int64_t bt_row_stride;
     int32_t ps, H, G, Hq;
     int32_t tok_rows;         // rows between consecutive tokens of a page (HND 1, NHD H)
@@ -92,8 +92,23 @@ struct AttnArgs {
 __device__ __forceinline__ int clamp_len(int len, int max_len) { return max(0, min(len, max_len)); }
 
 // floats per partial result of a split: max and sum per query head, then the
-// unnormalised output rows [G][128]
-__host__ __device__ constexpr int partial_floats(int G) { return 2 * G + G * kD; }
+// unnormalised output rows [G][D]
+__host__ __device__ constexpr int partial_floats(int G, int D) { return 2 * G + G * D; }
+
+// The lane maps for head_dim D (64, 128 or 256). Scores: lane group qg of a
+// 16-token MFMA block takes channels (D / 4) qg .. + D / 4 of its token, D / 32
+// code dwords, one MFMA each (dword kappa holds channels (D / 4) qg + 8 kappa
+// .. + 8), with D / 64 block-scale bytes. Output: D / 16 MFMAs, MFMA j covering
+// channels (D / 16) m + j, so lane n holds channels (D / 16) n .. + D / 16 of
+// its 8 tokens: D / 32 code bytes and one scale byte per token.
+template <int D>
+struct Shape {
+    static_assert(D == 64 || D == 128 || D == 256, "head_dim 64, 128 or 256");
+    static constexpr int kKDw = D / 32;          // K code dwords per lane and token = score MFMAs per block
+    static constexpr int kVBytes = D / 32;       // V code bytes per lane and token
+    static constexpr int kVDw = (D / 32 + 3) / 4;  // ... in dwords
+    static constexpr int kVMfma = D / 16;        // output MFMAs
+};
 
 __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c)
 {
@@ -156,13 +171,62 @@ __device__ __forceinline__ uint32_t max4_u32(uint32_t v)
     return max(s[0], s[1]);
 }
 
-// raw bytes of one 32-token tile for one lane
+// raw bytes of one 32-token tile for one lane (D = 128: kc 16 bytes, ks 2,
+// vc 4 per token)
+template <int D>
 struct TileLoads {
-    u32x4 kc[2];      // K codes: token 16 eta + n, channels 32 q .. 32 q + 31
-    uint32_t ks[2];   // their two scale bytes (blocks 2q, 2q + 1)
-    uint32_t vc[8];   // V codes: channels 8n .. 8n + 7 of token 16 (i / 4) + 4 q + i % 4
-    uint32_t vs[8];   // its scale byte (block n / 2)
+    uint32_t kc[2][Shape<D>::kKDw];     // K codes: token 16 eta + n, channels (D / 4) q ..
+    uint32_t ks[2];                     // their D / 64 scale bytes, low byte first
+    uint32_t vc[8][Shape<D>::kVDw];     // V codes: channels (D / 16) n .. of token 16 (i / 4) + 4 q + i % 4
+    uint32_t vs[8];                     // its scale byte (block D n / 256)
 };
+
+// K codes of one lane and token (D / 8 bytes at p)
+template <int D>
+__device__ __forceinline__ void load_kc(const uint8_t *p, uint32_t (&kc)[Shape<D>::kKDw])
+{
+    if constexpr (D == 64) {
+        const u32x2 w = *(const u32x2 *)p;
+        kc[0] = w.x;
+        kc[1] = w.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < D / 128; ++i) {
+            const u32x4 w = *(const u32x4 *)(p + 16 * i);
+            kc[4 * i] = w.x;
+            kc[4 * i + 1] = w.y;
+            kc[4 * i + 2] = w.z;
+            kc[4 * i + 3] = w.w;
+        }
+    }
+}
+
+// K scale bytes of one lane and token (D / 64 bytes at p)
+template <int D>
+__device__ __forceinline__ uint32_t load_ks(const uint8_t *p)
+{
+    if constexpr (D == 64)
+        return *p;
+    else if constexpr (D == 128)
+        return *(const uint16_t *)p;
+    else
+        return *(const uint32_t *)p;
+}
+
+// V codes of one lane and token (D / 32 bytes at p)
+template <int D>
+__device__ __forceinline__ void load_vc(const uint8_t *p, uint32_t (&vc)[Shape<D>::kVDw])
+{
+    if constexpr (D == 64) {
+        vc[0] = *(const uint16_t *)p;
+    } else if constexpr (D == 128) {
+        vc[0] = *(const uint32_t *)p;
+    } else {
+        const u32x2 w = *(const u32x2 *)p;
+        vc[0] = w.x;
+        vc[1] = w.y;
+    }
+}
 
 // per-lane byte offsets inside a page for the fast loader
 struct LaneOffsets {
@@ -224,12 +288,12 @@ __device__ __forceinline__ void stage_tile(const RawTile &r, uint8_t *vt, int l)
     *(uint32_t *)(vt + kKOff + 32 * kVPitch + 4 * l) = r.ksw;
     asm volatile("" ::: "memory");
 }
-__device__ __forceinline__ void read_v(const uint8_t *vt, int n, int qg, uint32_t vc[8], uint32_t vsp[4])
+__device__ __forceinline__ void read_v(const uint8_t *vt, int n, int qg, uint32_t (&vc)[8][1], uint32_t vsp[4])
 {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int T = 16 * (i >> 2) + 4 * qg + (i & 3);
-        vc[i] = *(const uint32_t *)(vt + T * kVPitch + 4 * n);
+        vc[i][0] = *(const uint32_t *)(vt + T * kVPitch + 4 * n);
     }
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2)
@@ -240,27 +304,29 @@ __device__ __forceinline__ void read_v(const uint8_t *vt, int n, int qg, uint32_
 
 // page size a multiple of 16: each 16-token half of a tile lies in one page,
 // so a half is a scalar base (page, first slot) plus per-lane constants.
+template <int D>
 __device__ __forceinline__ void load_half_fast(const AttnArgs &a, int64_t page, int row0, const LaneOffsets &o,
-                                               int eta, TileLoads &r)
+                                               int eta, TileLoads<D> &r)
 {
-    const uint8_t *kd = a.data[0] + page * a.stride[0] + (int64_t)row0 * (kD / 2);
-    const uint8_t *ksf = a.sf[0] + page * a.sf_stride[0] + (int64_t)row0 * (kD / 16);
-    const uint8_t *vd = a.data[1] + page * a.stride[1] + (int64_t)row0 * (kD / 2);
-    const uint8_t *vsf = a.sf[1] + page * a.sf_stride[1] + (int64_t)row0 * (kD / 16);
-    r.kc[eta] = *(const u32x4 *)(kd + o.k);
-    r.ks[eta] = *(const uint16_t *)(ksf + o.ks);
-    const int64_t tc = (int64_t)a.tok_rows * (kD / 2), ts = (int64_t)a.tok_rows * (kD / 16);
+    const uint8_t *kd = a.data[0] + page * a.stride[0] + (int64_t)row0 * (D / 2);
+    const uint8_t *ksf = a.sf[0] + page * a.sf_stride[0] + (int64_t)row0 * (D / 16);
+    const uint8_t *vd = a.data[1] + page * a.stride[1] + (int64_t)row0 * (D / 2);
+    const uint8_t *vsf = a.sf[1] + page * a.sf_stride[1] + (int64_t)row0 * (D / 16);
+    load_kc<D>(kd + o.k, r.kc[eta]);
+    r.ks[eta] = load_ks<D>(ksf + o.ks);
+    const int64_t tc = (int64_t)a.tok_rows * (D / 2), ts = (int64_t)a.tok_rows * (D / 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        r.vc[4 * eta + i] = *(const uint32_t *)(vd + i * tc + o.v);
+        load_vc<D>(vd + i * tc + o.v, r.vc[4 * eta + i]);
         r.vs[4 * eta + i] = vsf[i * ts + o.vs];
     }
 }
 
 // any page size: per-token page ids from the split's LDS copy; a token past
 // the end reads the split's first token (always valid) and is masked later
+template <int D>
 __device__ __forceinline__ void load_tile_any(const AttnArgs &a, const int *pages, int h, int t0, int t_base,
-                                              int len, int n, int qg, TileLoads &r)
+                                              int len, int n, int qg, TileLoads<D> &r)
 {
     auto addr = [&](int t, int &row) -> int64_t {
         t = t < len ? t : t_base;
@@ -273,22 +339,38 @@ __device__ __forceinline__ void load_tile_any(const AttnArgs &a, const int *page
     for (int eta = 0; eta < 2; ++eta) {
         int row;
         const int64_t page = addr(t0 + 16 * eta + n, row);
-        r.kc[eta] = *(const u32x4 *)(a.data[0] + page * a.stride[0] + (int64_t)row * (kD / 2) + 16 * qg);
-        r.ks[eta] = *(const uint16_t *)(a.sf[0] + page * a.sf_stride[0] + (int64_t)row * (kD / 16) + 2 * qg);
+        load_kc<D>(a.data[0] + page * a.stride[0] + (int64_t)row * (D / 2) + (D / 8) * qg, r.kc[eta]);
+        r.ks[eta] = load_ks<D>(a.sf[0] + page * a.sf_stride[0] + (int64_t)row * (D / 16) + (D / 64) * qg);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         int row;
         const int64_t page = addr(t0 + 16 * (i >> 2) + 4 * qg + (i & 3), row);
-        r.vc[i] = *(const uint32_t *)(a.data[1] + page * a.stride[1] + (int64_t)row * (kD / 2) + 4 * n);
-        r.vs[i] = a.sf[1][page * a.sf_stride[1] + (int64_t)row * (kD / 16) + (n >> 1)];
+        load_vc<D>(a.data[1] + page * a.stride[1] + (int64_t)row * (D / 2) + (D / 32) * n, r.vc[i]);
+        r.vs[i] = a.sf[1][page * a.sf_stride[1] + (int64_t)row * (D / 16) + (D * n) / 256];
     }
 }
 
+// MFMA J of the value product and those after it: channels (D / 16) m + J
+// come from code byte J / 2 of each token (even channel in the low nibble)
+template <int D, int J>
+__device__ __forceinline__ void pv_mfma(const uint32_t (&ev)[4][Shape<D>::kVDw],
+                                        const uint32_t (&od)[4][Shape<D>::kVDw], const uint32_t (&ss)[4], f16x8 pv,
+                                        f32x4 *o)
+{
+    constexpr int byte = J >> 1, dw = byte >> 2, sel = byte & 3;
+    const uint32_t(&src)[4][Shape<D>::kVDw] = (J & 1) ? od : ev;
+    o[J] = mfma(as_f16x8(mul_f16x2(fp4x2_f16<sel>(src[0][dw]), ss[0]), mul_f16x2(fp4x2_f16<sel>(src[1][dw]), ss[1]),
+                         mul_f16x2(fp4x2_f16<sel>(src[2][dw]), ss[2]), mul_f16x2(fp4x2_f16<sel>(src[3][dw]), ss[3])),
+                pv, o[J]);
+    if constexpr (J + 1 < Shape<D>::kVMfma)
+        pv_mfma<D, J + 1>(ev, od, ss, pv, o);
+}
+
 // one 32-token tile: scores, online softmax update, value product
-template <bool first, class VFetch>
-__device__ __forceinline__ void attend_tile(TileLoads cur, VFetch fetch_v, const f16x8 qv[4], int t0, int len, int qg, float c,
-                                            float &m_run, float &l_run, f32x4 o[8])
+template <int D, bool first, class VFetch>
+__device__ __forceinline__ void attend_tile(TileLoads<D> cur, VFetch fetch_v, const f16x8 *qv, int t0, int len, int qg,
+                                            float c, float &m_run, float &l_run, f32x4 *o)
 {
     const bool partial = t0 + kTile > len;           // wave-uniform
 
@@ -296,14 +378,17 @@ __device__ __forceinline__ void attend_tile(TileLoads cur, VFetch fetch_v, const
     float s[8];
 #pragma unroll
     for (int eta = 0; eta < 2; ++eta) {
-        const uint32_t sc = fp8x2_f16(cur.ks[eta]);
-        const uint32_t s_lo = __builtin_amdgcn_perm(sc, sc, 0x01000100u);   // (s_lo, s_lo)
-        const uint32_t s_hi = __builtin_amdgcn_perm(sc, sc, 0x03020302u);   // (s_hi, s_hi)
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma(decode8(cur.kc[eta].x, s_lo), qv[0], acc);
-        acc = mfma(decode8(cur.kc[eta].y, s_lo), qv[1], acc);
-        acc = mfma(decode8(cur.kc[eta].z, s_hi), qv[2], acc);
-        acc = mfma(decode8(cur.kc[eta].w, s_hi), qv[3], acc);
+#pragma unroll
+        for (int kap = 0; kap < Shape<D>::kKDw; ++kap) {
+            // two code dwords per 16-channel block: scale byte kap / 2,
+            // doubled into (s, s)
+            const int blk = kap >> 1;
+            const uint32_t sc = fp8x2_f16(cur.ks[eta] >> (16 * (blk >> 1)));
+            const uint32_t sp = (blk & 1) ? __builtin_amdgcn_perm(sc, sc, 0x03020302u)
+                                          : __builtin_amdgcn_perm(sc, sc, 0x01000100u);
+            acc = mfma(decode8(cur.kc[eta][kap], sp), qv[kap], acc);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[4 * eta + i] = acc[i] * c;
     }
@@ -341,7 +426,7 @@ __device__ __forceinline__ void attend_tile(TileLoads cur, VFetch fetch_v, const
                               pack_f16x2(p[6], p[7]));
     // token pair i2 = (2 i2, 2 i2 + 1): byte b of ev[i2] holds channel 2b of both
     // tokens (low nibble: the first), od[i2] channel 2b + 1; ss[i2] = their scales
-    uint32_t vc[8], vsp[4];
+    uint32_t vc[8][Shape<D>::kVDw], vsp[4];
     fetch_v(vc, vsp);
     if (partial) {
         // a masked token's V scale becomes 0 so that its (finite) codes add
@@ -352,28 +437,19 @@ __device__ __forceinline__ void attend_tile(TileLoads cur, VFetch fetch_v, const
             vsp[i2] = (T < len ? vsp[i2] & 0xFFu : 0u) | (T + 1 < len ? vsp[i2] & 0xFF00u : 0u);
         }
     }
-    uint32_t ev[4], od[4], ss[4];
+    uint32_t ev[4][Shape<D>::kVDw], od[4][Shape<D>::kVDw], ss[4];
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) {
-        const uint32_t wa = vc[2 * i2], wb = vc[2 * i2 + 1];
-        ev[i2] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
-        od[i2] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+#pragma unroll
+        for (int dw = 0; dw < Shape<D>::kVDw; ++dw) {
+            const uint32_t wa = vc[2 * i2][dw], wb = vc[2 * i2 + 1][dw];
+            ev[i2][dw] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
+            od[i2][dw] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+        }
         ss[i2] = fp8x2_f16(vsp[i2]);
     }
     // one channel (MFMA) at a time keeps few decoded words live
-#define KVFP4_PV(J, SRC, SEL)                                                                                   \
-    o[J] = mfma(as_f16x8(mul_f16x2(fp4x2_f16<SEL>(SRC[0]), ss[0]), mul_f16x2(fp4x2_f16<SEL>(SRC[1]), ss[1]),        \
-                         mul_f16x2(fp4x2_f16<SEL>(SRC[2]), ss[2]), mul_f16x2(fp4x2_f16<SEL>(SRC[3]), ss[3])),       \
-                pv, o[J])
-    KVFP4_PV(0, ev, 0);
-    KVFP4_PV(1, od, 0);
-    KVFP4_PV(2, ev, 1);
-    KVFP4_PV(3, od, 1);
-    KVFP4_PV(4, ev, 2);
-    KVFP4_PV(5, od, 2);
-    KVFP4_PV(6, ev, 3);
-    KVFP4_PV(7, od, 3);
-#undef KVFP4_PV
+    pv_mfma<D, 0>(ev, od, ss, pv, o);
 }
 
 // bf16 bits -> fp32 (exact)
@@ -383,7 +459,7 @@ __device__ __forceinline__ float bf16_bits_hi(uint32_t w) { return __uint_as_flo
 // one work item: kv head h of request b over tokens [split * kSplitTokens,
 // + kSplitTokens) (len > split * kSplitTokens). All waves of the workgroup
 // call it together; it ends with the partial result in the workspace.
-template <bool BF16, bool FAST16>
+template <int D, bool BF16, bool FAST16>
 __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__restrict__ bt,
                                             const float *__restrict__ k_scale, int b, int h, int split, int len,
                                             int *pages, float (*red_m)[16], float (*red_l)[16], float *red_o)
@@ -392,13 +468,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform by construction
 
     // the query rows first: their loads need no sequence length
-    // Q^T operands: head n of this kv head's group, channels 32 qg + 8 kappa .. +8
-    u32x4 qraw[4];
+    // Q^T operands: head n of this kv head's group, channels (D / 4) qg + 8 kappa .. +8
+    constexpr int kQ = Shape<D>::kKDw;
+    u32x4 qraw[kQ];
     {
         const bool live = n < a.G;
-        const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.G + (live ? n : 0)) * kD + 32 * qg;
+        const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.G + (live ? n : 0)) * D + (D / 4) * qg;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) qraw[k] = *(const u32x4 *)(qrow + 8 * k);
+        for (int k = 0; k < kQ; ++k) qraw[k] = *(const u32x4 *)(qrow + 8 * k);
     }
 
     const int t_split = split * kSplitTokens;
@@ -416,12 +493,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
     }
 
     float m_run = -INFINITY, l_run = 0.0f;
-    f32x4 o[8];
+    f32x4 o[Shape<D>::kVMfma];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < Shape<D>::kVMfma; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (t_w < len) {
-        TileLoads ld[2];
+        TileLoads<D> ld[2];
         // fast loader state: the page index and slot of the next half to load
         int pi = 0, slot = 0, pi_w = 0, slot_w = 0;
         LaneOffsets lo;
@@ -431,10 +508,10 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
             pi = pi_w;
             slot = slot_w;
             const uint32_t tr = (uint32_t)a.tok_rows;
-            lo.k = n * tr * (kD / 2) + 16 * qg;
-            lo.ks = n * tr * (kD / 16) + 2 * qg;
-            lo.v = 4 * qg * tr * (kD / 2) + 4 * n;
-            lo.vs = 4 * qg * tr * (kD / 16) + (n >> 1);
+            lo.k = n * tr * (D / 2) + (D / 8) * qg;
+            lo.ks = n * tr * (D / 16) + (D / 64) * qg;
+            lo.v = 4 * qg * tr * (D / 2) + (D / 32) * n;
+            lo.vs = 4 * qg * tr * (D / 16) + (D * n) / 256;
         }
         auto issue = [&](int k) {
             const int t0 = t_w + kTile * k;
@@ -446,7 +523,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
                     // a half past the end reads the wave's first half
                     const bool valid = t0 + 16 * eta < len;
                     const int ppi = valid ? pi : pi_w, pslot = valid ? slot : slot_w;
-                    load_half_fast(a, row_bt[ppi], pslot * a.tok_rows + h * a.head_rows, lo, eta, ld[k & 1]);
+                    load_half_fast<D>(a, row_bt[ppi], pslot * a.tok_rows + h * a.head_rows, lo, eta, ld[k & 1]);
                     slot += 16;
                     if (slot == a.ps) {
                         slot = 0;
@@ -454,7 +531,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
                     }
                 }
             } else {
-                load_tile_any(a, pages, h, t0, t_split, len, n, qg, ld[k & 1]);
+                load_tile_any<D>(a, pages, h, t0, t_split, len, n, qg, ld[k & 1]);
             }
         };
         issue(0);
@@ -462,17 +539,17 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
             issue(1);
 
         // the query rows into fp16 while the tiles load
-        f16x8 qv[4];
+        f16x8 qv[kQ];
         float c = a.sm_scale_log2 * *k_scale;         // scores to log2 units
         if (n >= a.G) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) qraw[k] = u32x4{0u, 0u, 0u, 0u};
+            for (int k = 0; k < kQ; ++k) qraw[k] = u32x4{0u, 0u, 0u, 0u};
         }
         if (BF16) {
             // largest magnitude of the row (bf16 magnitudes order as integers)
             uint32_t mx = 0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < kQ; ++k)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t v = qraw[k][e] & 0x7FFF7FFFu;
@@ -486,7 +563,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
             // c 2^-kk stays a normal fp32 number
             const int kk = min(max(141 - E, ec - 126), ec + 125);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < kQ; ++k) {
                 u32x4 o16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -496,49 +573,52 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
             c = ldexpf(c, -kk);
         } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) qv[k] = __builtin_bit_cast(f16x8, qraw[k]);
+            for (int k = 0; k < kQ; ++k) qv[k] = __builtin_bit_cast(f16x8, qraw[k]);
         }
 
 #pragma unroll
         for (int k = 0; k < kWaveTiles; ++k) {
             const int t0 = t_w + kTile * k;
             if (t0 < len) {
-                const TileLoads &tl = ld[k & 1];
-                auto fv = [&](uint32_t *vc, uint32_t *vsp) {
+                const TileLoads<D> &tl = ld[k & 1];
+                auto fv = [&](uint32_t (&vc)[8][Shape<D>::kVDw], uint32_t *vsp) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) vc[i] = tl.vc[i];
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int dw = 0; dw < Shape<D>::kVDw; ++dw) vc[i][dw] = tl.vc[i][dw];
 #pragma unroll
                     for (int i2 = 0; i2 < 4; ++i2) vsp[i2] = tl.vs[2 * i2] | (tl.vs[2 * i2 + 1] << 8);
                 };
                 if (k == 0)
-                    attend_tile<true>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o);
+                    attend_tile<D, true>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o);
                 else
-                    attend_tile<false>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o);
+                    attend_tile<D, false>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o);
             }
             if (k + 2 < kWaveTiles)
                 issue(k + 2);
         }
     }
 
-    // ---- merge the waves: lane (qg, n) holds O^T[8 (4 qg + i) + j][n], that
-    // is channels 32 qg + 8 i .. + 8 of head n
+    // ---- merge the waves: lane (qg, n) holds O^T[(D / 16) (4 qg + i) + j][n],
+    // that is channels (D / 4) qg + (D / 16) i .. + D / 16 of head n
     if (qg == 0) {
         red_m[w][n] = m_run;
         red_l[w][n] = l_run;
     }
     if (n < a.G) {
-        float *orow = red_o + (w * a.G + n) * kD + 32 * qg;
+        float *orow = red_o + (w * a.G + n) * D + (D / 4) * qg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *(f32x4 *)(orow + 8 * i) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
-            *(f32x4 *)(orow + 8 * i + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < D / 64; ++jj)
+                *(f32x4 *)(orow + (D / 16) * i + 4 * jj) =
+                    f32x4{o[4 * jj][i], o[4 * jj + 1][i], o[4 * jj + 2][i], o[4 * jj + 3][i]};
     }
     __syncthreads();
-    const int pf = partial_floats(a.G);
+    const int pf = partial_floats(a.G, D);
     float *ws = a.ws + (((int64_t)b * a.H + h) * a.splits + split) * pf;
-    for (int idx = tid; idx < a.G * (kD / 4); idx += 64 * kWaves) {
-        const int g = idx / (kD / 4), d0 = (idx - g * (kD / 4)) * 4;
+    for (int idx = tid; idx < a.G * (D / 4); idx += 64 * kWaves) {
+        const int g = idx / (D / 4), d0 = (idx - g * (D / 4)) * 4;
         float M = -INFINITY;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) M = fmaxf(M, red_m[v][g]);
@@ -548,13 +628,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
         for (int v = 0; v < kWaves; ++v) {
             const float f = __builtin_amdgcn_exp2f(red_m[v][g] - M);   // 0 for a wave without tokens
             L += red_l[v][g] * f;
-            acc += *(const f32x4 *)(red_o + (v * a.G + g) * kD + d0) * f;
+            acc += *(const f32x4 *)(red_o + (v * a.G + g) * D + d0) * f;
         }
         if (d0 == 0) {
             ws[g] = M;
             ws[a.G + g] = L;
         }
-        *(f32x4 *)(ws + 2 * a.G + g * kD + d0) = acc;
+        *(f32x4 *)(ws + 2 * a.G + g * D + d0) = acc;
     }
     __syncthreads();                                   // LDS is reused by the next item
 }
@@ -660,15 +740,19 @@ __device__ __forceinline__ void attend_item_staged(const AttnArgs &a, const int3
 
     bool have_next = false;
     auto issue_next = [&]() { have_next = has_next && issue_staged(a, bt, next, w, 0, lo, l, pre); };
-    auto stage_k = [&](const RawTile &r, TileLoads &cur) {
+    auto stage_k = [&](const RawTile &r, TileLoads<kD> &cur) {
         stage_tile(r, vt, l);
 #pragma unroll
         for (int eta = 0; eta < 2; ++eta) {
-            cur.kc[eta] = *(const u32x4 *)(vt + kKOff + (16 * eta + n) * kVPitch + 16 * qg);
+            const u32x4 kw = *(const u32x4 *)(vt + kKOff + (16 * eta + n) * kVPitch + 16 * qg);
+            cur.kc[eta][0] = kw.x;
+            cur.kc[eta][1] = kw.y;
+            cur.kc[eta][2] = kw.z;
+            cur.kc[eta][3] = kw.w;
             cur.ks[eta] = *(const uint16_t *)(vt + kKOff + 32 * kVPitch + (16 * eta + n) * (kD / 16) + 2 * qg);
         }
     };
-    auto fv = [&](uint32_t *vc, uint32_t *vs) { read_v(vt, n, qg, vc, vs); };
+    auto fv = [&](uint32_t (&vc)[8][1], uint32_t *vs) { read_v(vt, n, qg, vc, vs); };
 
     if (t_w < len) {
         if (!have_pre)
@@ -678,17 +762,17 @@ __device__ __forceinline__ void attend_item_staged(const AttnArgs &a, const int3
         f16x8 qv[4];
         const float c = load_query<BF16>(a, k_scale, b, h, n, qg, qv);
         {
-            TileLoads cur;
+            TileLoads<kD> cur;
             stage_k(pre, cur);
             if (!two)
                 issue_next();
-            attend_tile<true>(cur, fv, qv, t_w, len, qg, c, m_run, l_run, o);
+            attend_tile<kD, true>(cur, fv, qv, t_w, len, qg, c, m_run, l_run, o);
         }
         if (two) {
-            TileLoads cur;
+            TileLoads<kD> cur;
             stage_k(r1, cur);
             issue_next();
-            attend_tile<false>(cur, fv, qv, t_w + kTile, len, qg, c, m_run, l_run, o);
+            attend_tile<kD, false>(cur, fv, qv, t_w + kTile, len, qg, c, m_run, l_run, o);
         }
     } else {
         issue_next();
@@ -708,7 +792,7 @@ __device__ __forceinline__ void attend_item_staged(const AttnArgs &a, const int3
         }
     }
     __syncthreads();
-    const int pf = partial_floats(a.G);
+    const int pf = partial_floats(a.G, kD);
     float *ws = a.ws + (((int64_t)b * a.H + h) * a.splits + split) * pf;
     for (int idx = tid; idx < a.G * (kD / 4); idx += 64 * kWaves) {
         const int g = idx / (kD / 4), d0 = (idx - g * (kD / 4)) * 4;
@@ -772,8 +856,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot, int &t
 // 3.5% faster than kDirect on NHD pools and 8% slower on HND pools, whose
 // head runs the direct gathers already read contiguously).
 constexpr int kAnyPage = 0, kDirect = 1, kStaged = 2;
-template <bool BF16, int LOADER>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void attention_split_kernel(AttnArgs a, const int32_t *__restrict__ bt,
+template <int D, bool BF16, int LOADER>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : 4))) void attention_split_kernel(AttnArgs a, const int32_t *__restrict__ bt,
                                                                       const int32_t *__restrict__ seq_lens,
                                                                       const float *__restrict__ k_scale)
 {
@@ -784,7 +868,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
     __shared__ int4 items[64 * kWaves];              // (b, split, h, len)
     extern __shared__ float dyn[];                   // red_o [kWaves][G][128], then cum [batch + 1]
     float *red_o = dyn;
-    int *cum = (int *)(dyn + kWaves * a.G * kD);
+    int *cum = (int *)(dyn + kWaves * a.G * D);
     const int tid = threadIdx.x, nthr = 64 * kWaves;
 
     // ---- cum[b]: live splits of the requests before b
@@ -830,7 +914,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
         }
         __syncthreads();
         const int count = (int)min((int64_t)nthr, (nix - base + per_xcd - 1) / per_xcd);
-        if constexpr (LOADER == kStaged) {
+        if constexpr (LOADER == kStaged && D == kD) {
             RawTile pre;                                 // this wave's first tile of the next item
             bool have_pre = false;
             for (int t = 0; t < count; ++t) {
@@ -841,8 +925,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
         } else {
             for (int t = 0; t < count; ++t) {
                 const int4 it = items[t];
-                attend_item<BF16, LOADER == kDirect>(a, bt, k_scale, it.x, it.z, it.y, it.w, pages, red_m, red_l,
-                                                     red_o);
+                attend_item<D, BF16, LOADER == kDirect>(a, bt, k_scale, it.x, it.z, it.y, it.w, pages, red_m, red_l,
+                                                        red_o);
             }
         }
     }
@@ -851,17 +935,17 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
 // merge the live splits of one (request, kv head); thread -> (head g, 4
 // channels). Splits are taken 8 at a time, all their loads in flight, with
 // a running (max, sum, output) rescaled per group.
-template <bool BF16>
-__global__ __launch_bounds__(512) void attention_merge_kernel(AttnArgs a, const int32_t *__restrict__ seq_lens,
-                                                              const float *__restrict__ v_scale)
+template <int D, bool BF16>
+__global__ __launch_bounds__(1024) void attention_merge_kernel(AttnArgs a, const int32_t *__restrict__ seq_lens,
+                                                               const float *__restrict__ v_scale)
 {
     constexpr int kGroup = 8;
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-    const int g = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
+    const int g = threadIdx.x / (D / 4), d0 = (threadIdx.x % (D / 4)) * 4;
     const int len = clamp_len(seq_lens[b], a.max_len);
     const int live = (len + kSplitTokens - 1) / kSplitTokens;
-    const int pf = partial_floats(a.G);
+    const int pf = partial_floats(a.G, D);
     const float *ws = a.ws + (int64_t)bh * a.splits * pf;
     float M = -INFINITY, L = 0.0f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -873,7 +957,7 @@ __global__ __launch_bounds__(512) void attention_merge_kernel(AttnArgs a, const 
             const float *p = ws + min(s0 + u, live - 1) * pf;   // a repeat of the last split is dropped below
             ms[u] = p[g];
             ls[u] = p[a.G + g];
-            os[u] = *(const f32x4 *)(p + 2 * a.G + g * kD + d0);
+            os[u] = *(const f32x4 *)(p + 2 * a.G + g * D + d0);
         }
         float mx = M;
 #pragma unroll
@@ -895,7 +979,7 @@ __global__ __launch_bounds__(512) void attention_merge_kernel(AttnArgs a, const 
     const float scale = L > 0.0f ? *v_scale / L : 0.0f;        // an empty request gives zeros
     const uint32_t w0 = BF16 ? pack_bf16x2(acc[0] * scale, acc[1] * scale) : pack_f16x2(acc[0] * scale, acc[1] * scale);
     const uint32_t w1 = BF16 ? pack_bf16x2(acc[2] * scale, acc[3] * scale) : pack_f16x2(acc[2] * scale, acc[3] * scale);
-    *(u32x2 *)(a.out + ((int64_t)b * a.Hq + h * a.G + g) * kD + d0) = u32x2{w0, w1};
+    *(u32x2 *)(a.out + ((int64_t)b * a.Hq + h * a.G + g) * D + d0) = u32x2{w0, w1};
 }
 
 }  // namespace
@@ -940,11 +1024,34 @@ int64_t decode_attention_splits(int32_t bt_cols, int32_t page_size)
 }
 
 int64_t decode_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_qo_heads, int32_t bt_cols,
-                                         int32_t page_size)
+                                         int32_t page_size, int32_t head_dim)
 {
     const int G = num_qo_heads / num_kv_heads;
-    return (int64_t)batch * num_kv_heads * decode_attention_splits(bt_cols, page_size) * partial_floats(G) * 4;
+    return (int64_t)batch * num_kv_heads * decode_attention_splits(bt_cols, page_size) * partial_floats(G, head_dim) *
+           4;
 }
+
+namespace {
+
+typedef void (*split_fn)(AttnArgs, const int32_t *, const int32_t *, const float *);
+typedef void (*merge_fn)(AttnArgs, const int32_t *, const float *);
+
+// the split kernel for (head_dim, query dtype, loader); the LDS-staged
+// loader is built for head_dim 128 only, other sizes read NHD pages directly
+template <int D>
+split_fn split_kernel_of(bool bf16, int loader)
+{
+    if (D != kD && loader == kStaged)
+        loader = kDirect;
+    const split_fn kernels[2][3] = {
+        {attention_split_kernel<D, false, kAnyPage>, attention_split_kernel<D, false, kDirect>,
+         attention_split_kernel<D, false, D == kD ? kStaged : kDirect>},
+        {attention_split_kernel<D, true, kAnyPage>, attention_split_kernel<D, true, kDirect>,
+         attention_split_kernel<D, true, D == kD ? kStaged : kDirect>}};
+    return kernels[bf16 ? 1 : 0][loader];
+}
+
+}  // namespace
 
 hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, bool bf16, int32_t num_qo_heads,
                                    const int32_t *bt, int64_t bt_row_stride, int32_t bt_cols,
@@ -980,27 +1087,27 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
     const int64_t bh = (int64_t)batch * c.num_kv_heads;
     if (bh == 0)
         return hipSuccess;
-    typedef void (*split_fn)(AttnArgs, const int32_t *, const int32_t *, const float *);
+    const int D = c.head_dim;
     const int loader = c.page_size % 16 != 0 ? kAnyPage : (c.layout == KVFP4_NHD ? kStaged : kDirect);
-    const split_fn kernels[2][3] = {
-        {attention_split_kernel<false, kAnyPage>, attention_split_kernel<false, kDirect>,
-         attention_split_kernel<false, kStaged>},
-        {attention_split_kernel<true, kAnyPage>, attention_split_kernel<true, kDirect>,
-         attention_split_kernel<true, kStaged>}};
-    const split_fn kernel = kernels[bf16 ? 1 : 0][loader];
+    const split_fn kernel = D == 64    ? split_kernel_of<64>(bf16, loader)
+                            : D == 256 ? split_kernel_of<256>(bf16, loader)
+                                       : split_kernel_of<128>(bf16, loader);
+    const merge_fn merge = D == 64    ? (bf16 ? attention_merge_kernel<64, true> : attention_merge_kernel<64, false>)
+                           : D == 256 ? (bf16 ? attention_merge_kernel<256, true> : attention_merge_kernel<256, false>)
+                                      : (bf16 ? attention_merge_kernel<128, true> : attention_merge_kernel<128, false>);
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess)
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess)
         return e;
-    const int64_t pf = partial_floats(a.G);
+    const int64_t pf = partial_floats(a.G, D);
     for (int64_t b0 = 0; b0 < batch; b0 += kMaxBatchPerLaunch) {
         AttnArgs ac = a;
         ac.batch = (int32_t)(batch - b0 < kMaxBatchPerLaunch ? batch - b0 : kMaxBatchPerLaunch);
-        ac.q = a.q + b0 * a.Hq * kD;
+        ac.q = a.q + b0 * a.Hq * D;
         ac.ws = a.ws + b0 * a.H * a.splits * pf;
-        const size_t lds = (size_t)kWaves * a.G * kD * sizeof(float) + (size_t)(ac.batch + 1) * sizeof(int);
+        const size_t lds = (size_t)kWaves * a.G * D * sizeof(float) + (size_t)(ac.batch + 1) * sizeof(int);
         // as many workgroups as stay resident, a multiple of the 8 XCDs, and
         // no more than there can be items
         int occ = 0;
@@ -1013,13 +1120,8 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * kWaves), lds, st, ac, bt + b0 * bt_row_stride,
                            seq_lens + b0, k_scale);
     }
-    const dim3 merge_threads((unsigned)(32 * a.G));           // one thread per (query head, 4 channels)
-    if (bf16)
-        hipLaunchKernelGGL((attention_merge_kernel<true>), dim3((unsigned)bh), merge_threads, 0, st, a, seq_lens,
-                           v_scale);
-    else
-        hipLaunchKernelGGL((attention_merge_kernel<false>), dim3((unsigned)bh), merge_threads, 0, st, a, seq_lens,
-                           v_scale);
+    const dim3 merge_threads((unsigned)(D / 4 * a.G));        // one thread per (query head, 4 channels)
+    hipLaunchKernelGGL(merge, dim3((unsigned)bh), merge_threads, 0, st, a, seq_lens, v_scale);
     return hipGetLastError();
 }
 

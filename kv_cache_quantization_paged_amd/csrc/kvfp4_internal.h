@@ -53,6 +53,6 @@ int64_t decode_attention_splits(int32_t bt_cols, int32_t page_size);
 constexpr int64_t kNoAllocScratchBytes = KVFP4_NOALLOC_SCRATCH_BYTES;
 hipError_t noalloc_scratch(void **addr);
 int64_t decode_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_qo_heads, int32_t bt_cols,
-                                         int32_t page_size);
+                                         int32_t page_size, int32_t head_dim);
 
 }  // namespace kvfp4

@@ -193,17 +193,28 @@ def test_decode_attention_rejects_bad_arguments(B):
     assert call(_cache(B), dt=4) == B.KVFP4_EINVAL
     assert call(_cache(B), hq=12) == B.KVFP4_EINVAL                           # not a multiple of 8 kv heads
     assert call(_cache(B), hq=8 * 17) == B.KVFP4_EUNSUPPORTED                 # group of 17
+    # head_dim 64, 128 and 256 run; other multiples of 16 are refused
+    assert call(_cache(B, head_dim=96, k_page_stride=6144, v_page_stride=6144, k_sf_page_stride=768,
+                       v_sf_page_stride=768)) == B.KVFP4_EUNSUPPORTED
+    assert call(_cache(B, head_dim=512, k_page_stride=32768, v_page_stride=32768, k_sf_page_stride=4096,
+                       v_sf_page_stride=4096)) == B.KVFP4_EUNSUPPORTED
     assert call(_cache(B, head_dim=64, k_page_stride=4096, v_page_stride=4096, k_sf_page_stride=512,
-                       v_sf_page_stride=512)) == B.KVFP4_EUNSUPPORTED
+                       v_sf_page_stride=512), out=P(8200)) == B.KVFP4_EALIGN      # past the head_dim check
+    assert call(_cache(B, head_dim=256, k_page_stride=16384, v_page_stride=16384, k_sf_page_stride=2048,
+                       v_sf_page_stride=2048, k_sf=50)) == B.KVFP4_EALIGN          # 4-byte scale loads
+    assert call(_cache(B, head_dim=64, k_page_stride=4096, v_page_stride=4096, k_sf_page_stride=512,
+                       v_sf_page_stride=512, k_sf=49), out=P(8200)) == B.KVFP4_EALIGN
     assert call(_cache(B), sm=float("nan")) == B.KVFP4_EINVAL
     assert call(_cache(B), row=4) == B.KVFP4_EINVAL
     assert call(_cache(B), batch=0, q=None, bt=None, sl=None, out=None) == B.KVFP4_OK
     assert call(_cache(B), vs=None) == B.KVFP4_EINVAL
     assert call(_cache(B), out=P(8200)) == B.KVFP4_EALIGN
     assert call(_cache(B, k_sf=49)) == B.KVFP4_EALIGN                          # 2-byte scale loads
-    need = lib.kv_decode_attention_workspace_size(2, 8, 16, 8, 16)
-    assert need > 0 and lib.kv_decode_attention_workspace_size(-1, 8, 16, 8, 16) == -1
-    assert lib.kv_decode_attention_workspace_size(2, 8, 12, 8, 16) == -1
+    need = lib.kv_decode_attention_workspace_size(2, 8, 16, 8, 16, 128)
+    assert need == 2 * 8 * 1 * (2 + 128) * 2 * 4           # one 256-token split of (2 + 128) G floats
+    assert lib.kv_decode_attention_workspace_size(2, 8, 16, 8, 16, 256) == 2 * 8 * 1 * (2 + 256) * 2 * 4
+    assert lib.kv_decode_attention_workspace_size(-1, 8, 16, 8, 16, 128) == -1
+    assert lib.kv_decode_attention_workspace_size(2, 8, 12, 8, 16, 128) == -1
     assert call(_cache(B), wsb=need - 1) == B.KVFP4_EINVAL                     # workspace too small
     assert call(_cache(B), ws=None) == B.KVFP4_EINVAL
     assert call(_cache(B), ws=P((1 << 20) + 8)) == B.KVFP4_EALIGN
@@ -224,7 +235,7 @@ def test_noalloc_attention_rejects_bad_arguments_and_oversized_calls(B):
     assert call(_cache(B), out=P(8200)) == B.KVFP4_EALIGN
     assert call(_cache(B), batch=0) == B.KVFP4_OK
     # 4096 requests x 8 kv heads x 16 splits of 16 query heads: ~2 GiB of partials
-    big = lib.kv_decode_attention_workspace_size(4096, 8, 128, 256, 16)
+    big = lib.kv_decode_attention_workspace_size(4096, 8, 128, 256, 16, 128)
     assert big > B.NOALLOC_SCRATCH_BYTES
     assert call(_cache(B), hq=128, cols=256, batch=4096) == B.KVFP4_ESCRATCH
 

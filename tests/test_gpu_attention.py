@@ -58,9 +58,8 @@ def max_abs_v(cache, bt, lens, gv, b, h):
     return m
 
 
-def run_case(K, orc, seed, layout, ps, H, G, lens, bf16, spread=1.0, sm=None, check=None, q_exp=None):
+def run_case(K, orc, seed, layout, ps, H, G, lens, bf16, spread=1.0, sm=None, check=None, q_exp=None, D=128):
     rng = np.random.default_rng(seed)
-    D = 128
     B = len(lens)
     maxp = max(1, max((l + ps - 1) // ps for l in lens))
     P = B * maxp + 3
@@ -73,10 +72,11 @@ def run_case(K, orc, seed, layout, ps, H, G, lens, bf16, spread=1.0, sm=None, ch
         qf = (qf * np.exp2(q_exp.astype(np.float64))).astype(np.float32)
     q = W.f32_to_bits(qf, bf16)
     sm = float(np.float32(1.0 / np.sqrt(D) if sm is None else sm))
-    say(f"attention layout={layout} ps={ps} H={H} G={G} bf16={bf16} lens={list(lens)[:8]}")
+    say(f"attention layout={layout} ps={ps} H={H} G={G} D={D} bf16={bf16} lens={list(lens)[:8]}")
     dev = DeviceCache(cache)
     out = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16 if bf16 else torch.float16, device="cuda")
-    ws = torch.full((K.kv_decode_attention_workspace_size(B, H, Hq, maxp, ps),), 0xFF, dtype=torch.uint8, device="cuda")
+    ws = torch.full((K.kv_decode_attention_workspace_size(B, H, Hq, maxp, ps, D),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
     K.kv_decode_attention(dev.cache, bits_tensor(q, bf16), i32(bt), i32(lens), torch.tensor([gk], device="cuda"),
                           torch.tensor([gv], device="cuda"), sm, out, ws)
     got = out.float().cpu().numpy().astype(np.float64)
@@ -107,6 +107,30 @@ def test_attention_parity(K, orc, layout, bf16, G):
 @pytest.mark.parametrize("ps", [1, 5, 8, 32, 64])
 def test_attention_page_sizes(K, orc, ps):
     run_case(K, orc, 600 + ps, W.HND, ps, 3, 3, [7, 70, 300, 1], True)
+
+
+# head_dim 64 and 256: the lane maps scale with D (D / 32 score MFMAs per
+# 16 tokens, D / 16 output MFMAs); NHD pools read directly at these sizes
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("layout", [W.NHD, W.HND])
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("G", [1, 4, 16])
+def test_attention_head_dims(K, orc, D, layout, bf16, G):
+    lens = [1, 0, 31, 32, 33, 100, 257, 16, 5, 64]
+    run_case(K, orc, zlib.crc32(repr(("hd", D, layout, bf16, G)).encode()), layout, 16, 2, G, lens, bf16, D=D)
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("ps", [5, 32])
+def test_attention_head_dims_page_sizes(K, orc, D, ps):
+    """page sizes that are not multiples of 16 take the per-token loader"""
+    run_case(K, orc, 700 + ps + D, W.NHD if ps == 5 else W.HND, ps, 3, 2, [7, 70, 600, 1], True, D=D)
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_attention_head_dims_long_requests(K, orc, D):
+    """many 256-token splits per request, merged by the second kernel"""
+    run_case(K, orc, 800 + D, W.HND, 16, 2, 4, [4099, 1000, 2047, 3], False, D=D)
 
 
 def test_attention_peaked_scores(K, orc):
