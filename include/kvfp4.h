@@ -316,8 +316,9 @@ kvfp4_status_t kv_quantize_paged_cache(const kvfp4_paged_cache_t *cache, const v
  * length changes only its own request's output.
  * q and out are [batch_size, num_qo_heads, head_dim] of q_dtype (bf16 or
  * fp16), contiguous, 16-byte aligned; block_tables and seq_lens int32.
- * head_dim must be 64, 128 or 256 and num_qo_heads / num_kv_heads at most 16
- * (KVFP4_EUNSUPPORTED otherwise); scale bases and scale page strides must be
+ * head_dim must be 64, 128 or 256 (KVFP4_EUNSUPPORTED otherwise); any number
+ * of query heads per kv head (beyond 16 they run in passes of 16, each
+ * reading the cache again); scale bases and scale page strides must be
  * even for head_dim 128 and multiples of 4 for head_dim 256. Scores and the
  * softmax are fp32. The products run in fp16: decoded
  * K and V are exact there; a bf16 query row is scaled by a power of two that
@@ -338,7 +339,7 @@ kvfp4_status_t kv_decode_attention(const kvfp4_paged_cache_t *cache, const void 
 
 /* Bytes of workspace kv_decode_attention needs for these sizes (-1 for
  * invalid sizes): batch_size * num_kv_heads * ceil(bt_cols * page_size / 256)
- * partials of (2 + head_dim) * (num_qo_heads / num_kv_heads) floats. */
+ * partials of (2 + head_dim) * min(num_qo_heads / num_kv_heads, 16) floats. */
 int64_t kv_decode_attention_workspace_size(int32_t batch_size, int32_t num_kv_heads, int32_t num_qo_heads,
                                            int32_t bt_cols, int32_t page_size, int32_t head_dim);
 

@@ -523,7 +523,7 @@ kvfp4_status_t check_attention(const kvfp4_paged_cache_t *cache, const void *q, 
     if (bt_cols < 0 || bt_row_stride < bt_cols || !isfinite(sm_scale))
         return KVFP4_EINVAL;
     const int D = cache->head_dim;
-    if ((D != 64 && D != 128 && D != 256) || num_qo_heads / cache->num_kv_heads > 16)
+    if (D != 64 && D != 128 && D != 256)
         return KVFP4_EUNSUPPORTED;
     if (batch_size == 0) {
         *nothing_to_do = true;

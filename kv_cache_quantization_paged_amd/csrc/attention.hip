@@ -64,6 +64,7 @@ constexpr int kSplitTokens = kTile * kWaveTiles * kWaves;
 constexpr int kMaxPagesPerSplit = kSplitTokens + 1;
 constexpr float kSlack = 8.0f;              // log2 headroom of the softmax reference
 constexpr int kMaxBatchPerLaunch = 2048;    // requests whose split counts one workgroup keeps in LDS
+constexpr int kMaxG = 16;                   // query heads per pass: the MFMA's 16 columns
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -77,7 +78,8 @@ struct AttnArgs {
     uint16_t *out;
     float *ws;                // [B][H][splits] partials: m[G], l[G], o[G][head_dim]
     int64_t bt_row_stride;
-    int32_t ps, H, G, Hq;
+    int32_t ps, H, G, Hq;     // G: query heads of each kv head in this pass (<= 16)
+    int32_t Gtot, gq0;        // query heads per kv head; the pass's first one
     int32_t tok_rows;         // rows between consecutive tokens of a page (HND 1, NHD H)
     int32_t head_rows;        // rows between consecutive kv heads of a page (HND ps, NHD 1)
     int32_t splits;           // per (request, kv head)
@@ -473,7 +475,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
     u32x4 qraw[kQ];
     {
         const bool live = n < a.G;
-        const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.G + (live ? n : 0)) * D + (D / 4) * qg;
+        const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.Gtot + a.gq0 + (live ? n : 0)) * D + (D / 4) * qg;
 #pragma unroll
         for (int k = 0; k < kQ; ++k) qraw[k] = *(const u32x4 *)(qrow + 8 * k);
     }
@@ -670,7 +672,7 @@ __device__ __forceinline__ float load_query(const AttnArgs &a, const float *__re
 {
     u32x4 qraw[4];
     const bool live = n < a.G;
-    const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.G + (live ? n : 0)) * kD + 32 * qg;
+    const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.Gtot + a.gq0 + (live ? n : 0)) * kD + 32 * qg;
 #pragma unroll
     for (int k = 0; k < 4; ++k) qraw[k] = live ? *(const u32x4 *)(qrow + 8 * k) : u32x4{0u, 0u, 0u, 0u};
     float c = a.sm_scale_log2 * *k_scale;
@@ -979,7 +981,7 @@ __global__ __launch_bounds__(1024) void attention_merge_kernel(AttnArgs a, const
     const float scale = L > 0.0f ? *v_scale / L : 0.0f;        // an empty request gives zeros
     const uint32_t w0 = BF16 ? pack_bf16x2(acc[0] * scale, acc[1] * scale) : pack_f16x2(acc[0] * scale, acc[1] * scale);
     const uint32_t w1 = BF16 ? pack_bf16x2(acc[2] * scale, acc[3] * scale) : pack_f16x2(acc[2] * scale, acc[3] * scale);
-    *(u32x2 *)(a.out + ((int64_t)b * a.Hq + h * a.G + g) * D + d0) = u32x2{w0, w1};
+    *(u32x2 *)(a.out + ((int64_t)b * a.Hq + h * a.Gtot + a.gq0 + g) * D + d0) = u32x2{w0, w1};
 }
 
 }  // namespace
@@ -1026,7 +1028,9 @@ int64_t decode_attention_splits(int32_t bt_cols, int32_t page_size)
 int64_t decode_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_qo_heads, int32_t bt_cols,
                                          int32_t page_size, int32_t head_dim)
 {
-    const int G = num_qo_heads / num_kv_heads;
+    // the query heads of a kv head run in passes of up to 16, one after the
+    // other on the stream, each reusing the workspace
+    const int G = min(num_qo_heads / num_kv_heads, kMaxG);
     return (int64_t)batch * num_kv_heads * decode_attention_splits(bt_cols, page_size) * partial_floats(G, head_dim) *
            4;
 }
@@ -1075,7 +1079,7 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
     a.ps = c.page_size;
     a.H = c.num_kv_heads;
     a.Hq = num_qo_heads;
-    a.G = num_qo_heads / c.num_kv_heads;
+    a.Gtot = num_qo_heads / c.num_kv_heads;
     a.tok_rows = c.layout == KVFP4_HND ? 1 : c.num_kv_heads;
     a.head_rows = c.layout == KVFP4_HND ? c.page_size : 1;
     a.splits = (int32_t)decode_attention_splits(bt_cols, c.page_size);
@@ -1101,27 +1105,33 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess)
         return e;
-    const int64_t pf = partial_floats(a.G, D);
-    for (int64_t b0 = 0; b0 < batch; b0 += kMaxBatchPerLaunch) {
-        AttnArgs ac = a;
-        ac.batch = (int32_t)(batch - b0 < kMaxBatchPerLaunch ? batch - b0 : kMaxBatchPerLaunch);
-        ac.q = a.q + b0 * a.Hq * D;
-        ac.ws = a.ws + b0 * a.H * a.splits * pf;
-        const size_t lds = (size_t)kWaves * a.G * D * sizeof(float) + (size_t)(ac.batch + 1) * sizeof(int);
-        // as many workgroups as stay resident, a multiple of the 8 XCDs, and
-        // no more than there can be items
-        int occ = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 64 * kWaves, lds);
-        if (e != hipSuccess)
-            return e;
-        const int64_t most = ((int64_t)ac.batch * a.H * a.splits + 7) / 8 * 8;
-        int64_t grid = (int64_t)(occ > 0 ? occ : 1) * cus / 8 * 8;
-        grid = grid < 8 ? 8 : (grid > most ? most : grid);
-        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * kWaves), lds, st, ac, bt + b0 * bt_row_stride,
-                           seq_lens + b0, k_scale);
+    // query heads beyond the MFMA's 16 columns: passes over blocks of 16
+    // query heads (each pass reads K and V again)
+    for (int g0 = 0; g0 < a.Gtot; g0 += kMaxG) {
+        a.gq0 = g0;
+        a.G = a.Gtot - g0 < kMaxG ? a.Gtot - g0 : kMaxG;
+        const int64_t pf = partial_floats(a.G, D);
+        for (int64_t b0 = 0; b0 < batch; b0 += kMaxBatchPerLaunch) {
+            AttnArgs ac = a;
+            ac.batch = (int32_t)(batch - b0 < kMaxBatchPerLaunch ? batch - b0 : kMaxBatchPerLaunch);
+            ac.q = a.q + b0 * a.Hq * D;
+            ac.ws = a.ws + b0 * a.H * a.splits * pf;
+            const size_t lds = (size_t)kWaves * a.G * D * sizeof(float) + (size_t)(ac.batch + 1) * sizeof(int);
+            // as many workgroups as stay resident, a multiple of the 8 XCDs,
+            // and no more than there can be items
+            int occ = 0;
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 64 * kWaves, lds);
+            if (e != hipSuccess)
+                return e;
+            const int64_t most = ((int64_t)ac.batch * a.H * a.splits + 7) / 8 * 8;
+            int64_t grid = (int64_t)(occ > 0 ? occ : 1) * cus / 8 * 8;
+            grid = grid < 8 ? 8 : (grid > most ? most : grid);
+            hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * kWaves), lds, st, ac, bt + b0 * bt_row_stride,
+                               seq_lens + b0, k_scale);
+        }
+        const dim3 merge_threads((unsigned)(D / 4 * a.G));    // one thread per (query head, 4 channels)
+        hipLaunchKernelGGL(merge, dim3((unsigned)bh), merge_threads, 0, st, a, seq_lens, v_scale);
     }
-    const dim3 merge_threads((unsigned)(D / 4 * a.G));        // one thread per (query head, 4 channels)
-    hipLaunchKernelGGL(merge, dim3((unsigned)bh), merge_threads, 0, st, a, seq_lens, v_scale);
     return hipGetLastError();
 }
 

@@ -192,7 +192,7 @@ def test_decode_attention_rejects_bad_arguments(B):
                                        None)
     assert call(_cache(B), dt=4) == B.KVFP4_EINVAL
     assert call(_cache(B), hq=12) == B.KVFP4_EINVAL                           # not a multiple of 8 kv heads
-    assert call(_cache(B), hq=8 * 17) == B.KVFP4_EUNSUPPORTED                 # group of 17
+    assert call(_cache(B), hq=8 * 17, out=P(8200)) == B.KVFP4_EALIGN         # a group of 17 passes the checks
     # head_dim 64, 128 and 256 run; other multiples of 16 are refused
     assert call(_cache(B, head_dim=96, k_page_stride=6144, v_page_stride=6144, k_sf_page_stride=768,
                        v_sf_page_stride=768)) == B.KVFP4_EUNSUPPORTED
@@ -215,6 +215,8 @@ def test_decode_attention_rejects_bad_arguments(B):
     assert lib.kv_decode_attention_workspace_size(2, 8, 16, 8, 16, 256) == 2 * 8 * 1 * (2 + 256) * 2 * 4
     assert lib.kv_decode_attention_workspace_size(-1, 8, 16, 8, 16, 128) == -1
     assert lib.kv_decode_attention_workspace_size(2, 8, 12, 8, 16, 128) == -1
+    # more than 16 query heads per kv head run in passes of 16 over one workspace
+    assert lib.kv_decode_attention_workspace_size(2, 1, 40, 8, 16, 128) == 2 * 1 * 1 * (2 + 128) * 16 * 4
     assert call(_cache(B), wsb=need - 1) == B.KVFP4_EINVAL                     # workspace too small
     assert call(_cache(B), ws=None) == B.KVFP4_EINVAL
     assert call(_cache(B), ws=P((1 << 20) + 8)) == B.KVFP4_EALIGN
@@ -230,7 +232,7 @@ def test_noalloc_attention_rejects_bad_arguments_and_oversized_calls(B):
         return lib.kv_decode_attention_noalloc(C.byref(cache), P(4096), dt, hq, P(64), cols, cols, P(64), batch,
                                                P(64), P(64), sm, out, None)
     assert call(_cache(B), dt=4) == B.KVFP4_EINVAL
-    assert call(_cache(B), hq=8 * 17) == B.KVFP4_EUNSUPPORTED
+    assert call(_cache(B), hq=8 * 17, out=P(8200)) == B.KVFP4_EALIGN
     assert call(_cache(B), sm=float("inf")) == B.KVFP4_EINVAL
     assert call(_cache(B), out=P(8200)) == B.KVFP4_EALIGN
     assert call(_cache(B), batch=0) == B.KVFP4_OK

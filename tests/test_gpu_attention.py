@@ -120,6 +120,14 @@ def test_attention_head_dims(K, orc, D, layout, bf16, G):
     run_case(K, orc, zlib.crc32(repr(("hd", D, layout, bf16, G)).encode()), layout, 16, 2, G, lens, bf16, D=D)
 
 
+@pytest.mark.parametrize("D,G,H", [(128, 17, 2), (128, 32, 1), (64, 40, 2), (256, 24, 1)])
+@pytest.mark.parametrize("layout", [W.NHD, W.HND])
+def test_attention_many_query_heads_per_kv_head(K, orc, D, G, H, layout):
+    """more query heads per kv head than the MFMA's 16 columns: passes of 16"""
+    lens = [1, 0, 31, 300, 33, 257]
+    run_case(K, orc, zlib.crc32(repr(("mq", D, G, H, layout)).encode()), layout, 16, H, G, lens, True, D=D)
+
+
 @pytest.mark.parametrize("D", [64, 256])
 @pytest.mark.parametrize("ps", [5, 32])
 def test_attention_head_dims_page_sizes(K, orc, D, ps):
