@@ -12,8 +12,9 @@
 // quant_block.h's quantize_block.
 // dec and inv depend only on (tensor, scale byte): each workgroup tabulates
 // them for the 127 finite non-negative scale bytes in LDS at start, so a block
-// pays one IEEE division (for sf) per candidate and two LDS reads. The E2M1
-// encode / decode and the E4M3 encode use gfx950's conversion instructions.
+// pays two LDS reads per candidate, and its scale code a multiply (an IEEE
+// division only near an E4M3 rounding midpoint). The E2M1 encode / decode and
+// the E4M3 encode use gfx950's conversion instructions.
 #include "kvfp4_internal.h"
 #include "nvfp4_device.h"
 #include "quant_block.h"
