@@ -420,7 +420,7 @@ __device__ __forceinline__ void attend_tile(TileLoads<D> cur, VFetch fetch_v, co
     m_run = m_new;
     if (!first && __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // o is still zero on the first tile
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] *= alpha;
+        for (int j = 0; j < Shape<D>::kVMfma; ++j) o[j] *= alpha;
     }
 
     // ---- output: O^T[8 m + j][n] += V^T[8 m + j][token] P^T[token][n]

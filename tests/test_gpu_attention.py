@@ -141,9 +141,12 @@ def test_attention_head_dims_long_requests(K, orc, D):
     run_case(K, orc, 800 + D, W.HND, 16, 2, 4, [4099, 1000, 2047, 3], False, D=D)
 
 
-def test_attention_peaked_scores(K, orc):
-    """large score spreads (keys 8x wider, sm_scale 1): near one-hot softmax"""
-    run_case(K, orc, 610, W.NHD, 16, 2, 4, [200, 45, 513], True, spread=8.0, sm=1.0)
+@pytest.mark.parametrize("D", [128, 64, 256])
+def test_attention_peaked_scores(K, orc, D):
+    """large score spreads (keys 8x wider, sm_scale 1): near one-hot softmax,
+    whose running maximum jumps by far more than the rescale slack from tile
+    to tile, so every output channel's rescale is exercised"""
+    run_case(K, orc, 610 if D == 128 else 610 + D, W.NHD, 16, 2, 4, [200, 45, 513], True, spread=8.0, sm=1.0, D=D)
 
 
 def test_attention_long_requests_many_tiles(K, orc):
@@ -161,15 +164,17 @@ def test_attention_decode_workload_full_size(K, orc):
     run_case(K, orc, 630, W.NHD, 16, 8, 4, [int(x) for x in new_len], True, check=check)
 
 
-def test_attention_query_magnitudes(K, orc):
+@pytest.mark.parametrize("D", [128, 64, 256])
+def test_attention_query_magnitudes(K, orc, D):
     """bf16 query rows from 2^-60 to 2^60 and rows spanning 2^-50..2^0 inside:
-    the power-of-two move into fp16 must keep every score"""
+    the power-of-two move into fp16 must keep every score (the row's largest
+    magnitude is found over all D / 4 channels of each lane group)"""
     lens = [40, 300, 17, 129]
     B, H, G = len(lens), 2, 4
-    rng = np.random.default_rng(640)
+    rng = np.random.default_rng(640 + D)
     row = rng.choice([-60, -30, -12, 0, 12, 30, 60], size=(B, H * G, 1))
-    wide = rng.uniform(-50, 0, size=(B, H * G, 128)) * (rng.random((B, H * G, 1)) < 0.5)
-    run_case(K, orc, 641, W.NHD, 16, H, G, lens, True, q_exp=np.floor(row + wide))
+    wide = rng.uniform(-50, 0, size=(B, H * G, D)) * (rng.random((B, H * G, 1)) < 0.5)
+    run_case(K, orc, 641 + D, W.NHD, 16, H, G, lens, True, q_exp=np.floor(row + wide), D=D)
 
 
 def test_attention_batch_beyond_one_launch(K, orc):
