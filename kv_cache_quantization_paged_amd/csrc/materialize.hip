@@ -7,7 +7,10 @@
 // element, in the same (h, t, e) order, onto the K or V half [H, ps, D] of an
 // FP8 output page, so each lane streams 16-element blocks: 8 code bytes and
 // one scale byte in, 16 FP8 bytes out, with consecutive lanes on consecutive
-// blocks (a wavefront store writes 1 KiB of contiguous output). The output
+// blocks (a wavefront store writes 1 KiB of contiguous output). A wavefront
+// fetches the scale bytes of its 128 blocks per tensor as 32 dwords and hands
+// each lane its byte with ds_bpermute: per lane and tensor one dword load
+// instead of two byte loads, measured 2.4% faster on the whole call. The output
 // byte depends only on (scale byte, code): every workgroup tabulates, in LDS,
 // the 8 output magnitudes of each of the 256 scale bytes (the product
 // E2M1 x E4M3 is exact in fp32 and is rounded once, saturating at 448); a
@@ -36,6 +39,7 @@ constexpr int kThreads = 256;
 // loads, half pages measured 1.3% faster than whole pages; larger pages
 // split into more items.
 constexpr int kRound = 2;
+constexpr uint32_t kSpan = kRound * 64;    // blocks per wavefront and tensor
 constexpr int64_t kMaxGrid = 1 << 20;      // work items past the grid loop round
 
 struct MatArgs {
@@ -65,9 +69,26 @@ __device__ __forceinline__ uint2 convert8(uint32_t w, u32x2 lut, uint32_t smask)
     return make_uint2(perm(odd, even, 0x05010400u), perm(odd, even, 0x07030602u));
 }
 
+// byte offset of block q's V scale in a page whose scales are 4-token
+// interleaved: block q is (row, c) with row = q / nb = h ps + t (ps % 4 == 0,
+// so row % 4 = t % 4), and its scale sits at (row - row % 4) nb + 4 c + row % 4.
+// When nb divides 32, these offsets for a wavefront's kSpan blocks (whole
+// groups of 4 rows) are the same kSpan bytes as for linear scales; nb is then
+// a power of two (2^nbs).
+__device__ __forceinline__ uint32_t v_scale_index(uint32_t q, uint32_t nb)
+{
+    const uint32_t row = q / nb, c = q - row * nb;
+    return (row & ~3u) * nb + 4u * c + (row & 3u);
+}
+__device__ __forceinline__ uint32_t v_scale_index_pow2(uint32_t q, uint32_t nbs)
+{
+    const uint32_t row = q >> nbs, c = q & ((1u << nbs) - 1u);
+    return ((row & ~3u) << nbs) + 4u * c + (row & 3u);
+}
+
 // the index arrays are read-only for the whole launch: as __restrict__ kernel
 // parameters their wave-uniform reads are scalar loads
-template <bool INTERLEAVED, bool SHARED>
+template <bool INTERLEAVED, bool SHARED, bool V_BYTES>
 __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const int32_t *__restrict__ bt,
                                                                const int32_t *__restrict__ seq_lens,
                                                                const int32_t *__restrict__ indptr)
@@ -83,12 +104,6 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const 
         for (uint32_t i = tid; i < 2u * (uint32_t)bph; i += kThreads)
             buf_store_u32x4(u32x4{0u, 0u, 0u, 0u}, z, i * 16u);
     }
-
-    // block q of a half page is (h, t, c) with q = (h * ps + t) * nb + c; the
-    // lane advances it by kThreads blocks
-    const int c_step = kThreads % nb;
-    const int t_all = kThreads / nb;
-    const int t_step = t_all % a.ps, h_step = t_all / a.ps;
 
     bool have_lut = false;
     const int64_t n_work = a.batch > 0 ? indptr[a.batch] : 0;
@@ -121,33 +136,29 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const 
             sfs[kv] = make_rsrc(a.sf[kv] + pg[kv] * a.sf_stride[kv], (uint32_t)bph);
             dsts[kv] = make_rsrc(a.out + (dst * 2 + kv) * (int64_t)half_bytes, half_bytes);
         }
+        // a wavefront takes kSpan consecutive blocks of each tensor, 64 per round
         const int base = part * kRound * kThreads;
-        const int q0 = base + tid;
-        int c = q0 % nb, t = (q0 / nb) % a.ps, h = q0 / (nb * a.ps);
+        const int lane = tid & 63;
+        const uint32_t nbs = (uint32_t)__builtin_ctz((unsigned)nb);
+        const uint32_t qw = (uint32_t)base + (uint32_t)(tid >> 6) * kSpan;
         // every load of the item first: a wait for a load also waits for all
         // earlier stores. Blocks past the page read zeros and their stores
-        // are dropped by the range checks.
+        // are dropped by the range checks. The wavefront's kSpan scale bytes
+        // of a tensor come in as one dword per lane (lanes past kSpan / 4
+        // fetch the same dwords again) and reach their blocks' lanes by
+        // ds_bpermute; the byte-wise fallback reads V scales one by one.
+        const uint32_t sdo = qw + 4u * ((uint32_t)lane % (kSpan / 4));
+        const uint32_t sdw0 = buf_load_u32_nt(sfs[0], sdo);
+        const uint32_t sdw1 = V_BYTES ? 0u : buf_load_u32_nt(sfs[1], sdo);
+        uint32_t vsb[kRound];
         u32x2 code[2][kRound];
-        uint32_t sb[2][kRound];
 #pragma unroll
         for (int u = 0; u < kRound; ++u) {
-            const uint32_t q = (uint32_t)(base + u * kThreads + tid);
-            const uint32_t vq = INTERLEAVED ? (uint32_t)((h * a.ps + (t & ~3)) * nb + c * 4 + (t & 3)) : q;
+            const uint32_t q = qw + u * 64 + lane;
+            if (V_BYTES)
+                vsb[u] = buf_load_u8_nt(sfs[1], v_scale_index(q, (uint32_t)nb));
             code[0][u] = buf_load_u32x2_nt(src[0], q * 8u);
-            sb[0][u] = buf_load_u8_nt(sfs[0], q);
             code[1][u] = buf_load_u32x2_nt(src[1], q * 8u);
-            sb[1][u] = buf_load_u8_nt(sfs[1], vq);
-            if (INTERLEAVED) {
-                c += c_step;
-                const int carry = c >= nb;
-                c -= carry ? nb : 0;
-                t += t_step + carry;
-                h += h_step;
-                if (t >= a.ps) {
-                    t -= a.ps;
-                    h += 1;
-                }
-            }
         }
         if (!have_lut) {
             // output magnitude byte for (scale byte = tid, code magnitude k),
@@ -171,8 +182,17 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const 
         for (int kv = 0; kv < 2; ++kv) {
 #pragma unroll
             for (int u = 0; u < kRound; ++u) {
-                const uint32_t q = (uint32_t)(base + u * kThreads + tid);
-                const uint32_t s = sb[kv][u];
+                const uint32_t q = qw + u * 64 + lane;
+                uint32_t s;
+                if (kv == 1 && V_BYTES) {
+                    s = vsb[u];
+                } else {
+                    // the block's scale byte, relative to the wavefront's first
+                    const uint32_t rel = (INTERLEAVED && kv == 1 ? v_scale_index_pow2(q, nbs) : q) - qw;
+                    const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(rel & ~3u),
+                                                                              (int)(kv ? sdw1 : sdw0));
+                    s = (w >> (8 * (rel & 3))) & 0xFFu;
+                }
                 const u32x2 l = lut[s];
                 const uint32_t smask = (s & 0x80u) ? 0x80808080u : 0u;
                 const uint2 lo8 = convert8(code[kv][u].x, l, smask);
@@ -184,12 +204,12 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(MatArgs a, const 
     }
 }
 
-template <bool INTERLEAVED, bool SHARED>
+template <bool INTERLEAVED, bool SHARED, bool V_BYTES = false>
 void launch2(const MatArgs &a, const int32_t *bt, const int32_t *seq_lens, const int32_t *indptr, int grid,
              hipStream_t st)
 {
-    hipLaunchKernelGGL((materialize_kernel<INTERLEAVED, SHARED>), dim3(grid), dim3(kThreads), 0, st, a, bt,
-                       seq_lens, indptr);
+    hipLaunchKernelGGL((materialize_kernel<INTERLEAVED, SHARED, V_BYTES>), dim3(grid), dim3(kThreads), 0, st, a,
+                       bt, seq_lens, indptr);
 }
 
 }  // namespace
@@ -224,7 +244,16 @@ hipError_t launch_materialize_fp8(const kvfp4_paged_cache_t &c, bool v_interleav
     a.parts = (bph + kRound * kThreads - 1) / (kRound * kThreads);
     const int64_t want = num_out_pages - 1 > 0 ? (num_out_pages - 1) * a.parts : 1;
     const int grid = (int)(want < kMaxGrid ? want : kMaxGrid);
-    if (v_interleaved) {
+    // interleaved V scales stay inside a wavefront's kSpan bytes only when
+    // D / 16 divides 32 (head_dim 64, 128, 256, 512); other head dims read
+    // them byte by byte
+    const bool v_bytes = v_interleaved && 32 % (c.head_dim / 16) != 0;
+    if (v_bytes) {
+        if (shared)
+            launch2<true, true, true>(a, bt, seq_lens, indptr, grid, st);
+        else
+            launch2<true, false, true>(a, bt, seq_lens, indptr, grid, st);
+    } else if (v_interleaved) {
         if (shared)
             launch2<true, true>(a, bt, seq_lens, indptr, grid, st);
         else

@@ -328,7 +328,7 @@ def mat_case(seed, shared, compact, ps=16, H=4, D=128, B=6, data_pad=256, extra_
 @pytest.mark.parametrize("shared", [True, False])
 @pytest.mark.parametrize("compact", [True, False])
 @pytest.mark.parametrize("interleaved", [True, False])
-@pytest.mark.parametrize("geom", [(16, 4, 128), (4, 2, 64), (32, 8, 256), (8, 1, 192)])
+@pytest.mark.parametrize("geom", [(16, 4, 128), (4, 2, 64), (32, 8, 256), (8, 1, 192), (12, 3, 128), (4, 2, 512)])
 def test_materialize_parity(K, orc, shared, compact, interleaved, geom):
     ps, H, D = geom
     seed = 600 + shared + 2 * compact + 4 * interleaved + ps
