@@ -186,12 +186,14 @@ def test_attention_batch_beyond_one_launch(K, orc):
     run_case(K, orc, 651, W.HND, 16, 1, 2, lens, True, check=check)
 
 
+@pytest.mark.parametrize("D", [128, 64, 256])
 @pytest.mark.parametrize("sm", [0.0, -0.25, 3.0])
-def test_attention_sm_scale_edge_values(K, orc, sm):
+def test_attention_sm_scale_edge_values(K, orc, sm, D):
     """sm_scale 0 (every weight equal: the plain mean of V), a negative scale
     (the softmax of reversed scores) and a large one, on fp16 and bf16"""
     for bf16 in (True, False):
-        run_case(K, orc, 660 + int(sm * 8) + bf16, W.HND, 16, 2, 4, [1, 47, 260], bf16, sm=sm)
+        seed = 660 + int(sm * 8) + bf16 + (0 if D == 128 else D)
+        run_case(K, orc, seed, W.HND, 16, 2, 4, [1, 47, 260], bf16, sm=sm, D=D)
 
 
 def test_attention_split_boundaries(K, orc):
