@@ -21,9 +21,8 @@ def K():
     return K
 
 
-def make_case(orc, seed, B, H, G, ps, layout, max_len):
+def make_case(orc, seed, B, H, G, ps, layout, max_len, D=128):
     rng = np.random.default_rng(seed)
-    D = 128
     lens = rng.integers(0, max_len + 1, size=B).astype(np.int32)
     lens[0] = max_len
     maxp = max(1, (max_len + ps - 1) // ps)
@@ -38,14 +37,14 @@ def make_case(orc, seed, B, H, G, ps, layout, max_len):
     q = W.f32_to_bits(W.normal_rows(rng, (B, H * G, D)), True)
     return dict(dev=DeviceCache(cache), bt=i32(bt), lens=i32(lens), q=bits_tensor(q, True),
                 gk=torch.tensor([gk], device="cuda"), gv=torch.tensor([gv], device="cuda"), B=B, H=H, G=G, ps=ps,
-                maxp=maxp)
+                maxp=maxp, D=D)
 
 
 def both(K, c, sm):
     Hq = c["H"] * c["G"]
-    ref = torch.full((c["B"], Hq, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ref = torch.full((c["B"], Hq, c["D"]), float("nan"), dtype=torch.bfloat16, device="cuda")
     got = torch.full_like(ref, float("nan"))
-    ws = torch.full((K.kv_decode_attention_workspace_size(c["B"], c["H"], Hq, c["maxp"], c["ps"]),), 0xFF,
+    ws = torch.full((K.kv_decode_attention_workspace_size(c["B"], c["H"], Hq, c["maxp"], c["ps"], c["D"]),), 0xFF,
                     dtype=torch.uint8, device="cuda")
     K.kv_decode_attention(c["dev"].cache, c["q"], c["bt"], c["lens"], c["gk"], c["gv"], sm, ref, ws)
     K.kv_decode_attention_noalloc(c["dev"].cache, c["q"], c["bt"], c["lens"], c["gk"], c["gv"], sm, got)
@@ -61,6 +60,17 @@ def test_noalloc_matches_workspace_call_twice(K, orc):
         print(f"noalloc attention: {name} call, B={case['B']} H={case['H']} G={case['G']}", flush=True)
         ref, got = both(K, case, sm)
         assert np.array_equal(ref, got), name
+
+
+@pytest.mark.parametrize("D,G,layout", [(64, 20, W.NHD), (256, 4, W.HND), (128, 33, W.HND)])
+def test_noalloc_head_dims_and_query_head_passes(K, orc, D, G, layout):
+    """head_dim 64 and 256, and more than 16 query heads per kv head (passes
+    of 16 over the one scratch array), against the workspace call"""
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    case = make_case(orc, 910 + D + G, B=7, H=2, G=G, ps=16, layout=layout, max_len=700, D=D)
+    print(f"noalloc attention: D={D} G={G} layout={layout}", flush=True)
+    ref, got = both(K, case, sm)
+    assert np.array_equal(ref, got)
 
 
 def test_noalloc_refuses_calls_beyond_its_scratch(K, orc):
