@@ -177,6 +177,23 @@ def test_attention_query_magnitudes(K, orc, D):
     run_case(K, orc, 641 + D, W.NHD, 16, H, G, lens, True, q_exp=np.floor(row + wide), D=D)
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_attention_random_shapes(K, orc, case):
+    """seeded draws over head_dim, layout, page size (any-page, direct and
+    staged loaders), query dtype, kv heads, query heads per kv head (one or
+    several passes), lengths and score spread"""
+    rng = np.random.default_rng(7000 + case)
+    D = int(rng.choice([64, 128, 256]))
+    layout = W.NHD if rng.random() < 0.5 else W.HND
+    ps = int(rng.choice([1, 4, 5, 8, 16, 32, 48]))
+    bf16 = bool(rng.random() < 0.5)
+    H = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 3, 5, 8, 16, 17]))
+    lens = [int(x) for x in rng.integers(0, 600, size=int(rng.integers(1, 6)))]
+    spread = float(rng.choice([1.0, 4.0]))
+    run_case(K, orc, 7100 + case, layout, ps, H, G, lens, bf16, spread=spread, D=D)
+
+
 def test_attention_batch_beyond_one_launch(K, orc):
     """more requests than one launch's split table holds (2048): the requests
     go out in launches of 2048, each with its own slice of the workspace"""
