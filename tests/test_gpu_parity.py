@@ -151,6 +151,23 @@ def test_append_empty_is_noop(K, orc):
     assert same_bytes(dev.to_host(), cache)
 
 
+@pytest.mark.parametrize("case", range(20))
+def test_append_random_shapes(K, orc, case):
+    """seeded draws over layout, page size, heads and head_dim (rows that fill
+    whole wavefronts take the row kernel for the 4over6 recipes, the others
+    the flat kernel), input dtype, recipe and value distribution"""
+    rng = np.random.default_rng(8000 + case)
+    layout = W.NHD if rng.random() < 0.5 else W.HND
+    ps = int(rng.choice([1, 4, 5, 8, 16, 32, 64]))
+    H = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    D = int(rng.choice([16, 32, 48, 64, 80, 128, 256]))
+    in_bf16 = bool(rng.random() < 0.5)
+    recipe = str(rng.choice(["standard", "mse", "mae", "mse16", "mae16"]))
+    kind = str(rng.choice(["normal", "student_t", "special"]))
+    ro, rk = recipes(K, orc, recipe)
+    run_append_both(K, orc, 8100 + case, layout, ps, H, D, in_bf16, ro, rk, kind=kind)
+
+
 # --------------------------------------------------------------------------- dequant
 def dequant_case(seed, layout, ps, H, D, B=7, pool=60, neg_scales=True, stacked=False, data_pad=0):
     rng = np.random.default_rng(seed)
@@ -175,8 +192,25 @@ def dequant_case(seed, layout, ps, H, D, B=7, pool=60, neg_scales=True, stacked=
 @pytest.mark.parametrize("geom", [(16, 8, 128), (32, 2, 64), (5, 3, 48), (1, 16, 256), (64, 4, 128), (32, 8, 64)])
 def test_dequant_parity(K, orc, layout, out_bf16, bt64, geom):
     ps, H, D = geom
-    seed = 500 + layout + 2 * out_bf16 + 4 * bt64 + ps
-    cache, bt, lens, T = dequant_case(seed, layout, ps, H, D)
+    run_dequant(K, orc, 500 + layout + 2 * out_bf16 + 4 * bt64 + ps, layout, ps, H, D, out_bf16, bt64)
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_dequant_random_shapes(K, orc, case):
+    """seeded draws over layout, page size, heads and head_dim (HND shapes on
+    both sides of the LDS-staged path's conditions), output dtype, table
+    dtype and batch"""
+    rng = np.random.default_rng(8200 + case)
+    layout = W.NHD if rng.random() < 0.5 else W.HND
+    ps = int(rng.choice([1, 4, 5, 8, 16, 32, 64]))
+    H = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    D = int(rng.choice([16, 32, 48, 64, 128, 256]))
+    run_dequant(K, orc, 8300 + case, layout, ps, H, D, bool(rng.random() < 0.5), bool(rng.random() < 0.5),
+                B=int(rng.integers(3, 12)))
+
+
+def run_dequant(K, orc, seed, layout, ps, H, D, out_bf16, bt64, B=7):
+    cache, bt, lens, T = dequant_case(seed, layout, ps, H, D, B=B)
     bt = bt.astype(np.int64 if bt64 else np.int32)
     B = len(lens)
     gk, gv = 0.0137, 2.7e-4
@@ -187,7 +221,7 @@ def test_dequant_parity(K, orc, layout, out_bf16, bt64, geom):
     tdt = torch.bfloat16 if out_bf16 else torch.float16
     dk = torch.full((B, T, H, D), W.SENTINEL_16 - 65536, dtype=torch.int16, device="cuda").view(tdt)
     dv = dk.clone()
-    say(f"dequant seed={seed} layout={layout} geom={geom} bf16={out_bf16} bt64={bt64} B={B} T={T}")
+    say(f"dequant seed={seed} layout={layout} geom={(ps, H, D)} bf16={out_bf16} bt64={bt64} B={B} T={T}")
     K.kv_dequantize_paged(dev.cache, torch.from_numpy(bt).cuda(), i32(lens),
                           torch.tensor([gk], dtype=torch.float32, device="cuda"),
                           torch.tensor([gv], dtype=torch.float32, device="cuda"), dk, dv)
@@ -342,6 +376,37 @@ def test_materialize_parity(K, orc, shared, compact, interleaved, geom):
     d_out = torch.full((n_out, 2, H, ps, D), W.SENTINEL_FP8, dtype=torch.uint8, device="cuda")
     d_tab = torch.full((B, maxp), -1, dtype=torch.int32, device="cuda")
     say(f"materialize seed={seed} geom={geom} shared={shared} compact={compact} interleaved={interleaved}")
+    K.kv_materialize_fp8(dev.cache, torch.from_numpy(bt).cuda(), i32(lens), i32(indptr),
+                         d_out.view(torch.float8_e4m3fn), d_tab, shared, interleaved)
+    torch.cuda.synchronize()
+    got = d_out.cpu().numpy()
+    assert np.array_equal(got, out), first_mismatch(got, out)
+    assert np.array_equal(d_tab.cpu().numpy(), tab)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_materialize_random_shapes(K, orc, case):
+    """seeded draws over page size, heads, head_dim (V scales through the
+    wavefront's dwords, or byte by byte when D / 16 does not divide 32),
+    shared or separate tables, compact or padded reservations and the V
+    scale layout"""
+    rng = np.random.default_rng(8400 + case)
+    ps = int(rng.choice([4, 8, 12, 16, 32, 64]))
+    H = int(rng.choice([1, 2, 3, 4, 8]))
+    D = int(rng.choice([64, 128, 192, 256, 320, 512]))
+    shared, compact, interleaved = (bool(x) for x in rng.random(3) < 0.5)
+    seed = 8500 + case
+    cache, bt, lens, indptr, maxp, n_out = mat_case(seed, shared, compact, ps, H, D, B=int(rng.integers(3, 9)))
+    B = len(lens)
+    out = np.full((n_out, 2, H, ps, D), W.SENTINEL_FP8, np.uint8)
+    tab = np.full((B, maxp), -1, np.int32)
+    orc.materialize_fp8(cache, bt, lens, indptr, out, tab, shared=shared, v_sf_interleaved=interleaved,
+                        threads=oracle_threads())
+    dev = DeviceCache(cache)
+    d_out = torch.full((n_out, 2, H, ps, D), W.SENTINEL_FP8, dtype=torch.uint8, device="cuda")
+    d_tab = torch.full((B, maxp), -1, dtype=torch.int32, device="cuda")
+    say(f"materialize sweep seed={seed} geom={(ps, H, D)} B={B} shared={shared} compact={compact} "
+        f"interleaved={interleaved}")
     K.kv_materialize_fp8(dev.cache, torch.from_numpy(bt).cuda(), i32(lens), i32(indptr),
                          d_out.view(torch.float8_e4m3fn), d_tab, shared, interleaved)
     torch.cuda.synchronize()
