@@ -194,13 +194,15 @@ def test_attention_random_shapes(K, orc, case):
     run_case(K, orc, 7100 + case, layout, ps, H, G, lens, bf16, spread=spread, D=D)
 
 
-def test_attention_batch_beyond_one_launch(K, orc):
+@pytest.mark.parametrize("D,G", [(128, 2), (256, 16)])
+def test_attention_batch_beyond_one_launch(K, orc, D, G):
     """more requests than one launch's split table holds (2048): the requests
-    go out in launches of 2048, each with its own slice of the workspace"""
+    go out in launches of 2048, each with its own slice of the workspace;
+    head_dim 256 with 16 query heads is the largest LDS use per workgroup"""
     rng = np.random.default_rng(650)
     lens = [int(x) for x in rng.integers(0, 40, size=2100)]
     check = [0, 1, 2046, 2047, 2048, 2049, 2099]
-    run_case(K, orc, 651, W.HND, 16, 1, 2, lens, True, check=check)
+    run_case(K, orc, 651 if D == 128 else 652, W.HND, 16, 1, G, lens, True, check=check, D=D)
 
 
 @pytest.mark.parametrize("D", [128, 64, 256])
