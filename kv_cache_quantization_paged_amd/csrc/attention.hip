@@ -306,21 +306,33 @@ __device__ __forceinline__ void read_v(const uint8_t *vt, int n, int qg, uint32_
 
 // page size a multiple of 16: each 16-token half of a tile lies in one page,
 // so a half is a scalar base (page, first slot) plus per-lane constants.
-template <int D>
+// With DW (head_dim 128, scale rows 4-byte aligned) the scale bytes come in
+// as the aligned dwords that hold them and are picked out where they are
+// used: a 1- or 2-byte load is zero-extended by the compiler right after it
+// is issued, which makes the wave wait for every load in flight, including
+// the second tile's (dwords: 3-4% faster on HND pools).
+template <int D, bool DW = false>
 __device__ __forceinline__ void load_half_fast(const AttnArgs &a, int64_t page, int row0, const LaneOffsets &o,
                                                int eta, TileLoads<D> &r)
 {
+    static_assert(!DW || D == 128, "dword scale loads are laid out for head_dim 128");
     const uint8_t *kd = a.data[0] + page * a.stride[0] + (int64_t)row0 * (D / 2);
     const uint8_t *ksf = a.sf[0] + page * a.sf_stride[0] + (int64_t)row0 * (D / 16);
     const uint8_t *vd = a.data[1] + page * a.stride[1] + (int64_t)row0 * (D / 2);
     const uint8_t *vsf = a.sf[1] + page * a.sf_stride[1] + (int64_t)row0 * (D / 16);
     load_kc<D>(kd + o.k, r.kc[eta]);
-    r.ks[eta] = load_ks<D>(ksf + o.ks);
+    if constexpr (DW)
+        r.ks[eta] = *(const uint32_t *)(ksf + (o.ks & ~3u));
+    else
+        r.ks[eta] = load_ks<D>(ksf + o.ks);
     const int64_t tc = (int64_t)a.tok_rows * (D / 2), ts = (int64_t)a.tok_rows * (D / 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         load_vc<D>(vd + i * tc + o.v, r.vc[4 * eta + i]);
-        r.vs[4 * eta + i] = vsf[i * ts + o.vs];
+        if constexpr (DW)
+            r.vs[4 * eta + i] = *(const uint32_t *)(vsf + i * ts + (o.vs & ~3u));
+        else
+            r.vs[4 * eta + i] = vsf[i * ts + o.vs];
     }
 }
 
@@ -372,7 +384,7 @@ __device__ __forceinline__ void pv_mfma(const uint32_t (&ev)[4][Shape<D>::kVDw],
 // one 32-token tile: scores, online softmax update, value product
 template <int D, bool first, class VFetch>
 __device__ __forceinline__ void attend_tile(TileLoads<D> cur, VFetch fetch_v, const f16x8 *qv, int t0, int len, int qg,
-                                            float c, float &m_run, float &l_run, f32x4 *o)
+                                            float c, float &m_run, float &l_run, f32x4 *o, int ks_shift = 0)
 {
     const bool partial = t0 + kTile > len;           // wave-uniform
 
@@ -386,7 +398,7 @@ __device__ __forceinline__ void attend_tile(TileLoads<D> cur, VFetch fetch_v, co
             // two code dwords per 16-channel block: scale byte kap / 2,
             // doubled into (s, s)
             const int blk = kap >> 1;
-            const uint32_t sc = fp8x2_f16(cur.ks[eta] >> (16 * (blk >> 1)));
+            const uint32_t sc = fp8x2_f16((cur.ks[eta] >> ks_shift) >> (16 * (blk >> 1)));
             const uint32_t sp = (blk & 1) ? __builtin_amdgcn_perm(sc, sc, 0x03020302u)
                                           : __builtin_amdgcn_perm(sc, sc, 0x01000100u);
             acc = mfma(decode8(cur.kc[eta][kap], sp), qv[kap], acc);
@@ -461,7 +473,7 @@ __device__ __forceinline__ float bf16_bits_hi(uint32_t w) { return __uint_as_flo
 // one work item: kv head h of request b over tokens [split * kSplitTokens,
 // + kSplitTokens) (len > split * kSplitTokens). All waves of the workgroup
 // call it together; it ends with the partial result in the workspace.
-template <int D, bool BF16, bool FAST16>
+template <int D, bool BF16, bool FAST16, bool DW = false>
 __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__restrict__ bt,
                                             const float *__restrict__ k_scale, int b, int h, int split, int len,
                                             int *pages, float (*red_m)[16], float (*red_l)[16], float *red_o)
@@ -515,6 +527,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
             lo.v = 4 * qg * tr * (D / 2) + (D / 32) * n;
             lo.vs = 4 * qg * tr * (D / 16) + (D * n) / 256;
         }
+        // DW: the byte of each V scale dword that is this lane's (into bytes
+        // 0 and 1 of the token pair's word) and the half of the K scale
+        // dword that holds its two scale bytes
+        const uint32_t vb = DW ? lo.vs & 3u : 0u;
+        const uint32_t vsel = 0x0C0C0000u | ((vb + 4u) << 8) | vb;
+        const int ks_shift = DW ? (int)(8 * (lo.ks & 3u)) : 0;
         auto issue = [&](int k) {
             const int t0 = t_w + kTile * k;
             if (t0 >= len)
@@ -525,7 +543,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
                     // a half past the end reads the wave's first half
                     const bool valid = t0 + 16 * eta < len;
                     const int ppi = valid ? pi : pi_w, pslot = valid ? slot : slot_w;
-                    load_half_fast<D>(a, row_bt[ppi], pslot * a.tok_rows + h * a.head_rows, lo, eta, ld[k & 1]);
+                    load_half_fast<D, DW>(a, row_bt[ppi], pslot * a.tok_rows + h * a.head_rows, lo, eta, ld[k & 1]);
                     slot += 16;
                     if (slot == a.ps) {
                         slot = 0;
@@ -589,12 +607,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
 #pragma unroll
                         for (int dw = 0; dw < Shape<D>::kVDw; ++dw) vc[i][dw] = tl.vc[i][dw];
 #pragma unroll
-                    for (int i2 = 0; i2 < 4; ++i2) vsp[i2] = tl.vs[2 * i2] | (tl.vs[2 * i2 + 1] << 8);
+                    for (int i2 = 0; i2 < 4; ++i2)
+                        vsp[i2] = DW ? __builtin_amdgcn_perm(tl.vs[2 * i2 + 1], tl.vs[2 * i2], vsel)
+                                     : tl.vs[2 * i2] | (tl.vs[2 * i2 + 1] << 8);
                 };
                 if (k == 0)
-                    attend_tile<D, true>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o);
+                    attend_tile<D, true>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o, ks_shift);
                 else
-                    attend_tile<D, false>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o);
+                    attend_tile<D, false>(tl, fv, qv, t0, len, qg, c, m_run, l_run, o, ks_shift);
             }
             if (k + 2 < kWaveTiles)
                 issue(k + 2);
@@ -861,7 +881,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot, int &t
 // each item's first tile issued before the previous item's merge; measured
 // 3.5% faster than kDirect on NHD pools and 8% slower on HND pools, whose
 // head runs the direct gathers already read contiguously).
-constexpr int kAnyPage = 0, kDirect = 1, kStaged = 2;
+constexpr int kAnyPage = 0, kDirect = 1, kStaged = 2, kDirectDw = 3;
 template <int D, bool BF16, int LOADER>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : 4))) void attention_split_kernel(AttnArgs a, const int32_t *__restrict__ bt,
                                                                       const int32_t *__restrict__ seq_lens,
@@ -954,7 +974,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D =
         } else {
             for (int t = 0; t < count; ++t) {
                 const int4 it = items[t];
-                attend_item<D, BF16, LOADER == kDirect>(a, bt, k_scale, it.x, it.z, it.y, it.w, pages, red_m, red_l,
+                attend_item<D, BF16, LOADER == kDirect || LOADER == kDirectDw, LOADER == kDirectDw>(
+                    a, bt, k_scale, it.x, it.z, it.y, it.w, pages, red_m, red_l,
                                                         red_o);
             }
         }
@@ -1072,13 +1093,15 @@ typedef void (*merge_fn)(AttnArgs, const int32_t *, const float *);
 template <int D>
 split_fn split_kernel_of(bool bf16, int loader)
 {
-    if (D != kD && loader == kStaged)
+    if (D != kD && (loader == kStaged || loader == kDirectDw))
         loader = kDirect;
-    const split_fn kernels[2][3] = {
+    const split_fn kernels[2][4] = {
         {attention_split_kernel<D, false, kAnyPage>, attention_split_kernel<D, false, kDirect>,
-         attention_split_kernel<D, false, D == kD ? kStaged : kDirect>},
+         attention_split_kernel<D, false, D == kD ? kStaged : kDirect>,
+         attention_split_kernel<D, false, D == kD ? kDirectDw : kDirect>},
         {attention_split_kernel<D, true, kAnyPage>, attention_split_kernel<D, true, kDirect>,
-         attention_split_kernel<D, true, D == kD ? kStaged : kDirect>}};
+         attention_split_kernel<D, true, D == kD ? kStaged : kDirect>,
+         attention_split_kernel<D, true, D == kD ? kDirectDw : kDirect>}};
     return kernels[bf16 ? 1 : 0][loader];
 }
 
@@ -1119,7 +1142,13 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
     if (bh == 0)
         return hipSuccess;
     const int D = c.head_dim;
-    const int loader = c.page_size % 16 != 0 ? kAnyPage : (c.layout == KVFP4_NHD ? kStaged : kDirect);
+    // HND pools whose scale rows are 4-byte aligned read their scales as dwords
+    const bool sf_dw = ((uintptr_t)c.k_sf | (uintptr_t)c.v_sf | (uint64_t)c.k_sf_page_stride |
+                        (uint64_t)c.v_sf_page_stride) % 4 == 0;
+    const int loader = c.page_size % 16 != 0  ? kAnyPage
+                       : c.layout == KVFP4_NHD ? kStaged
+                       : (D == kD && sf_dw)    ? kDirectDw
+                                               : kDirect;
     const split_fn kernel = D == 64    ? split_kernel_of<64>(bf16, loader)
                             : D == 256 ? split_kernel_of<256>(bf16, loader)
                                        : split_kernel_of<128>(bf16, loader);

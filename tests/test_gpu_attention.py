@@ -33,14 +33,14 @@ def say(*a):
     print(*a, flush=True)
 
 
-def quantized_cache(orc, rng, P, ps, H, D, layout, spread=1.0):
+def quantized_cache(orc, rng, P, ps, H, D, layout, spread=1.0, sf_pad=0):
     """a pool of P pages quantized by the oracle from N(0, spread^2) K and V"""
     shape = (P, ps, H, D) if layout == W.NHD else (P, H, ps, D)
     k = W.f32_to_bits(W.normal_rows(rng, shape) * np.float32(spread), True)
     v = W.f32_to_bits(W.normal_rows(rng, shape), True)
     gk, gv = orc.global_scale(k, True), orc.global_scale(v, True)
     pad = (-(ps * H * D // 2)) % 16 + 16
-    cache = W.make_cache(rng, P, ps, H, D, layout, data_pad=pad, fill="zero")
+    cache = W.make_cache(rng, P, ps, H, D, layout, data_pad=pad, sf_pad=sf_pad, fill="zero")
     orc.quantize_paged_cache(cache, k, v, True, gk, gv, v_sf_interleaved=False, threads=oracle_threads())
     return cache, gk, gv
 
@@ -58,12 +58,13 @@ def max_abs_v(cache, bt, lens, gv, b, h):
     return m
 
 
-def run_case(K, orc, seed, layout, ps, H, G, lens, bf16, spread=1.0, sm=None, check=None, q_exp=None, D=128):
+def run_case(K, orc, seed, layout, ps, H, G, lens, bf16, spread=1.0, sm=None, check=None, q_exp=None, D=128,
+             sf_pad=0):
     rng = np.random.default_rng(seed)
     B = len(lens)
     maxp = max(1, max((l + ps - 1) // ps for l in lens))
     P = B * maxp + 3
-    cache, gk, gv = quantized_cache(orc, rng, P, ps, H, D, layout, spread)
+    cache, gk, gv = quantized_cache(orc, rng, P, ps, H, D, layout, spread, sf_pad)
     bt = rng.permutation(P)[:B * maxp].reshape(B, maxp).astype(np.int32)
     lens = np.array(lens, np.int32)
     Hq = H * G
@@ -102,6 +103,15 @@ def run_case(K, orc, seed, layout, ps, H, G, lens, bf16, spread=1.0, sm=None, ch
 def test_attention_parity(K, orc, layout, bf16, G):
     lens = [1, 0, 31, 32, 33, 100, 257, 16, 5, 64]
     run_case(K, orc, zlib.crc32(repr((layout, bf16, G)).encode()), layout, 16, 2, G, lens, bf16)
+
+
+@pytest.mark.parametrize("sf_pad", [2, 4])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_attention_scale_page_alignment(K, orc, sf_pad, bf16):
+    """HND pools read their scales as aligned dwords when every scale page
+    starts 4-byte aligned, and byte by byte otherwise (a page stride 2 past
+    a multiple of 4): both must give the same attention"""
+    run_case(K, orc, 690 + sf_pad + bf16, W.HND, 16, 2, 4, [1, 31, 300, 77], bf16, sf_pad=sf_pad)
 
 
 @pytest.mark.parametrize("ps", [1, 5, 8, 32, 64])
