@@ -533,10 +533,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
         const uint32_t vb = DW ? lo.vs & 3u : 0u;
         const uint32_t vsel = 0x0C0C0000u | ((vb + 4u) << 8) | vb;
         const int ks_shift = DW ? (int)(8 * (lo.ks & 3u)) : 0;
+        // every tile of the wave is issued, also one wholly past the end (its
+        // halves then read the wave's first half, and it is not computed):
+        // loads issued on one path only make the compiler wait for every
+        // load in flight where the paths meet
         auto issue = [&](int k) {
             const int t0 = t_w + kTile * k;
-            if (t0 >= len)
-                return;
             if (FAST16) {
 #pragma unroll
                 for (int eta = 0; eta < 2; ++eta) {
@@ -662,15 +664,24 @@ __device__ __forceinline__ void attend_item(const AttnArgs &a, const int32_t *__
 }
 
 // staged loader, one tile: tile k of wave w in item it = (b, split, h, len)
-// into r; false (nothing issued) when the wave has no tokens there. A half
-// past the end reads the wave's first half (masked later).
+// into r; false when the wave has no tokens there (and then nothing is
+// issued unless `always`). A half past the end reads the wave's first half
+// (masked later).
 __device__ __forceinline__ bool issue_staged(const AttnArgs &a, const int32_t *__restrict__ bt, int4 it, int w, int k,
-                                             const LaneOffsets &lo, int l, RawTile &r)
+                                             const LaneOffsets &lo, int l, RawTile &r, bool always = false)
 {
     const int t_w = it.y * kSplitTokens + w * (kTile * kWaveTiles);
-    const int t0 = t_w + kTile * k;
-    if (t0 >= it.w)
-        return false;
+    int t0 = t_w + kTile * k;
+    const bool has = t0 < it.w;
+    if (!has) {
+        // with `always` (a wave whose first tile exists), the wave's first
+        // tile is read again and not used: loads issued on one path only
+        // make the compiler wait for every load in flight where the paths
+        // meet
+        if (!always)
+            return false;
+        t0 = t_w;
+    }
     const int32_t *row_bt = bt + (int64_t)it.x * a.bt_row_stride;
     int64_t pg[2];
     int rw[2];
@@ -682,19 +693,24 @@ __device__ __forceinline__ bool issue_staged(const AttnArgs &a, const int32_t *_
         rw[eta] = (t - pi * a.ps) * a.tok_rows + it.z * a.head_rows;
     }
     load_tile_staged(a, pg, rw, lo, l, r);
-    return true;
+    return has;
 }
 
 // the query rows of item it into fp16 MFMA operands and the score factor
-template <bool BF16>
-__device__ __forceinline__ float load_query(const AttnArgs &a, const float *__restrict__ k_scale, int b, int h, int n,
-                                            int qg, f16x8 qv[4])
+// the raw query rows of head n of kv head h (zeros for n >= G), issued
+// before a wave's second tile so that converting them waits for no tile
+__device__ __forceinline__ void query_raw(const AttnArgs &a, int b, int h, int n, int qg, u32x4 qraw[4])
 {
-    u32x4 qraw[4];
     const bool live = n < a.G;
     const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h * a.Gtot + a.gq0 + (live ? n : 0)) * kD + 32 * qg;
 #pragma unroll
     for (int k = 0; k < 4; ++k) qraw[k] = live ? *(const u32x4 *)(qrow + 8 * k) : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_query(const AttnArgs &a, const float *__restrict__ k_scale, u32x4 qraw[4],
+                                            f16x8 qv[4])
+{
     float c = a.sm_scale_log2 * *k_scale;
     if (BF16) {
         uint32_t mx = 0;
@@ -779,10 +795,12 @@ __device__ __forceinline__ void attend_item_staged(const AttnArgs &a, const int3
     if (t_w < len) {
         if (!have_pre)
             issue_staged(a, bt, it, w, 0, lo, l, pre);
+        u32x4 qraw[4];
+        query_raw(a, b, h, n, qg, qraw);
         RawTile r1;
-        const bool two = issue_staged(a, bt, it, w, 1, lo, l, r1);
+        const bool two = issue_staged(a, bt, it, w, 1, lo, l, r1, true);
         f16x8 qv[4];
-        const float c = load_query<BF16>(a, k_scale, b, h, n, qg, qv);
+        const float c = load_query<BF16>(a, k_scale, qraw, qv);
         {
             TileLoads<kD> cur;
             stage_k(pre, cur);
