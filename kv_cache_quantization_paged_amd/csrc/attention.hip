@@ -306,16 +306,15 @@ __device__ __forceinline__ void read_v(const uint8_t *vt, int n, int qg, uint32_
 
 // page size a multiple of 16: each 16-token half of a tile lies in one page,
 // so a half is a scalar base (page, first slot) plus per-lane constants.
-// With DW (head_dim 128, scale rows 4-byte aligned) the scale bytes come in
-// as the aligned dwords that hold them and are picked out where they are
-// used: a 1- or 2-byte load is zero-extended by the compiler right after it
-// is issued, which makes the wave wait for every load in flight, including
-// the second tile's (dwords: 3-4% faster on HND pools).
+// With DW (scale rows 4-byte aligned) the scale bytes come in as the
+// aligned dwords that hold them and are picked out where they are used: a
+// 1- or 2-byte load is zero-extended by the compiler right after it is
+// issued, which makes the wave wait for every load in flight, including the
+// second tile's (dwords: 3-4% faster on HND pools at head_dim 128).
 template <int D, bool DW = false>
 __device__ __forceinline__ void load_half_fast(const AttnArgs &a, int64_t page, int row0, const LaneOffsets &o,
                                                int eta, TileLoads<D> &r)
 {
-    static_assert(!DW || D == 128, "dword scale loads are laid out for head_dim 128");
     const uint8_t *kd = a.data[0] + page * a.stride[0] + (int64_t)row0 * (D / 2);
     const uint8_t *ksf = a.sf[0] + page * a.sf_stride[0] + (int64_t)row0 * (D / 16);
     const uint8_t *vd = a.data[1] + page * a.stride[1] + (int64_t)row0 * (D / 2);
@@ -1111,15 +1110,13 @@ typedef void (*merge_fn)(AttnArgs, const int32_t *, const float *);
 template <int D>
 split_fn split_kernel_of(bool bf16, int loader)
 {
-    if (D != kD && (loader == kStaged || loader == kDirectDw))
+    if (D != kD && loader == kStaged)
         loader = kDirect;
     const split_fn kernels[2][4] = {
         {attention_split_kernel<D, false, kAnyPage>, attention_split_kernel<D, false, kDirect>,
-         attention_split_kernel<D, false, D == kD ? kStaged : kDirect>,
-         attention_split_kernel<D, false, D == kD ? kDirectDw : kDirect>},
+         attention_split_kernel<D, false, D == kD ? kStaged : kDirect>, attention_split_kernel<D, false, kDirectDw>},
         {attention_split_kernel<D, true, kAnyPage>, attention_split_kernel<D, true, kDirect>,
-         attention_split_kernel<D, true, D == kD ? kStaged : kDirect>,
-         attention_split_kernel<D, true, D == kD ? kDirectDw : kDirect>}};
+         attention_split_kernel<D, true, D == kD ? kStaged : kDirect>, attention_split_kernel<D, true, kDirectDw>}};
     return kernels[bf16 ? 1 : 0][loader];
 }
 
@@ -1165,7 +1162,7 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
                         (uint64_t)c.v_sf_page_stride) % 4 == 0;
     const int loader = c.page_size % 16 != 0  ? kAnyPage
                        : c.layout == KVFP4_NHD ? kStaged
-                       : (D == kD && sf_dw)    ? kDirectDw
+                       : sf_dw                 ? kDirectDw
                                                : kDirect;
     const split_fn kernel = D == 64    ? split_kernel_of<64>(bf16, loader)
                             : D == 256 ? split_kernel_of<256>(bf16, loader)
