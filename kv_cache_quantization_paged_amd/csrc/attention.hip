@@ -6,7 +6,7 @@
 //
 // out[b, hq, :] = softmax_t(sm_scale * q[b, hq] . K[b, t]) V[b, t] over
 // t < seq_lens[b], with kv head h = hq / G (G = Hq / H query heads per kv
-// head), head_dim 128.
+// head), head_dim 64, 128 or 256.
 //
 // Split over the sequence: a work item is (request, kv head, split of
 // kSplitTokens tokens), handled by one workgroup of kWaves wavefronts. The
@@ -26,11 +26,14 @@
 // issue the next item's first tile before the merge.
 //
 // Both products run on v_mfma_f32_16x16x32_f16 (A 16x32, B 32x16; lane l
-// holds A[l%16][8(l/16)..+8], B[8(l/16)..+8][l%16], D[4(l/16)..+4][l%16]):
+// holds A[l%16][8(l/16)..+8], B[8(l/16)..+8][l%16], D[4(l/16)..+4][l%16]);
+// the counts below are head_dim 128's (Shape<D> scales them for 64 and 256):
 //  * scores, S^T[token][g] = K[token][d] . Q^T[d][g]: 16 tokens per MFMA
 //    row block, the 128 channels in 4 MFMAs of 32. Lane group q = l/16
-//    takes channels 32q..32q+31 (one 16-byte code load and one 2-byte scale
-//    load per lane and token), and Q^T follows the same channel map.
+//    takes channels 32q..32q+31 (one 16-byte code load per lane and token;
+//    its two scale bytes come from a 2-byte load, or from the aligned dword
+//    that holds them when the pool's scale rows are 4-byte aligned), and Q^T
+//    follows the same channel map.
 //  * output, O^T[d][g] += V^T[d][token] . P^T[token][g]: the 32 tokens of a
 //    tile in one MFMA, 8 MFMAs for the 128 channels, MFMA j covering
 //    channels 8m + j. The lane that holds P for tokens {4q + i, 16 + 4q + i}
