@@ -188,7 +188,7 @@ def test_attention_query_magnitudes(K, orc, D):
     run_case(K, orc, 641 + D, W.NHD, 16, H, G, lens, True, q_exp=np.floor(row + wide), D=D)
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(96))
 def test_attention_random_shapes(K, orc, case):
     """seeded draws over head_dim, layout, page size (any-page, direct and
     staged loaders), query dtype, kv heads, query heads per kv head (one or

@@ -151,7 +151,7 @@ def test_append_empty_is_noop(K, orc):
     assert same_bytes(dev.to_host(), cache)
 
 
-@pytest.mark.parametrize("case", range(20))
+@pytest.mark.parametrize("case", range(100))
 def test_append_random_shapes(K, orc, case):
     """seeded draws over layout, page size, heads and head_dim (rows that fill
     whole wavefronts take the row kernel for the 4over6 recipes, the others
@@ -195,7 +195,7 @@ def test_dequant_parity(K, orc, layout, out_bf16, bt64, geom):
     run_dequant(K, orc, 500 + layout + 2 * out_bf16 + 4 * bt64 + ps, layout, ps, H, D, out_bf16, bt64)
 
 
-@pytest.mark.parametrize("case", range(20))
+@pytest.mark.parametrize("case", range(100))
 def test_dequant_random_shapes(K, orc, case):
     """seeded draws over layout, page size, heads and head_dim (HND shapes on
     both sides of the LDS-staged path's conditions), output dtype, table
@@ -384,7 +384,7 @@ def test_materialize_parity(K, orc, shared, compact, interleaved, geom):
     assert np.array_equal(d_tab.cpu().numpy(), tab)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(64))
 def test_materialize_random_shapes(K, orc, case):
     """seeded draws over page size, heads, head_dim (V scales through the
     wavefront's dwords, or byte by byte when D / 16 does not divide 32),
