@@ -3,7 +3,9 @@
 Headline step (the decode workload): quantize-append one new token for each
 of 64 requests (bf16 K/V, 8 KV heads, head_dim 128, page_size 16, NHD pages
 shuffled across a 20,000-page pool), then gather-dequantize every request's
-full context (lengths U{1..4096} + 1) into bf16 [64, max_len, 8, 128].
+full context (lengths U{1..4096} + 1) into bf16 [64, max_len, 8, 128], as one
+kv_append_dequantize_paged call per step (the same step as the two calls
+kv_quantize_append and kv_dequantize_paged is timed as a leg).
 value = algorithmic bytes of the step / wall time of the step, with all
 inputs resident in HBM; replicas of the workload in disjoint memory rotate so
 that no step finds its inputs in the 256 MB Infinity Cache.
@@ -227,6 +229,13 @@ class Decode:
                                                        self.out_k, self.out_v)
         self.append = self.append_call.launch
         self.dequant = self.dequant_call.launch
+        # the same step as one call: the append's rows and the dequant of
+        # every request (with its newest token) in one launch
+        self.step_call = K.prepare_append_dequantize_paged(self.cache, self.key, self.value, self.bi, self.pos,
+                                                           self.indices, self.indptr, self.last, self.gk, self.gv,
+                                                           self.bt, self.seq_lens, self.gk_t, self.gv_t, self.out_k,
+                                                           self.out_v)
+        self.step = self.step_call.launch
 
     def append_eager(self):
         """the functional call: every tensor checked again"""
@@ -242,14 +251,14 @@ class Decode:
         before and after, the new rows, and the picked requests' outputs"""
         torch = self.env.torch
         pre = whole_cache(self.cache)
-        self.append()
-        self.dequant()
+        self.step()
         torch.cuda.synchronize()
         post = whole_cache(self.cache)
         outs = {b: (host_bits(self.out_k[b, :int(self.lens[b])]), host_bits(self.out_v[b, :int(self.lens[b])]))
                 for b in picks}
         indices, indptr, last, bt = self.tables
-        samples.add("decode_step", "decode workload: history quantization, append, dequant", pre=pre, post=post,
+        samples.add("decode_step", "decode workload: history quantization, then the step (append and dequant in "
+                                   "one kv_append_dequantize_paged call)", pre=pre, post=post,
                     key=host_bits(self.key), value=host_bits(self.value), bi=np.arange(64, dtype=np.int32),
                     pos=self.old.astype(np.int32), indices=indices, indptr=indptr, last=last, bt=bt,
                     lens=self.lens.astype(np.int32), old=self.old, gk=self.gk, gv=self.gv, outs=outs,
@@ -654,9 +663,10 @@ def leg_copy(env, nbytes, iters, warmup):
 
 
 DEQUANT_SOURCES = ("kv_cache_quantization_paged_amd/csrc/dequant.hip",
+                   "kv_cache_quantization_paged_amd/csrc/quant_block.h",
                    "kv_cache_quantization_paged_amd/csrc/nvfp4_device.h",
                    "kv_cache_quantization_paged_amd/csrc/kvfp4_internal.h")
-TRAFFIC_SUMMARY = "profiles/kv_dequantize_paged_decode_counters.md"
+TRAFFIC_SUMMARY = "profiles/kv_append_dequantize_paged_decode_counters.md"
 
 
 def dequant_source_hash() -> str:
@@ -669,7 +679,7 @@ def dequant_source_hash() -> str:
 
 
 def recorded_traffic():
-    """HBM bytes per launch of the decode dequant from the committed
+    """HBM bytes per launch of the decode step's kernel from the committed
     rocprofv3 counter summary, or None when the kernel's sources have
     changed since those counters were taken."""
     path = os.path.join(ROOT, TRAFFIC_SUMMARY)
@@ -1023,6 +1033,7 @@ def host_cost_leg(env, reps_n=5, calls=40):
 
     res = {"append_functional_us": host_us(r.append_eager), "append_prepared_us": host_us(r.append),
            "dequant_functional_us": host_us(r.dequant_eager), "dequant_prepared_us": host_us(r.dequant),
+           "append_dequant_prepared_us": host_us(r.step),
            "materialize_functional_us": host_us(functional_materialize),
            "materializer_run_us": host_us(fn),
            "note": "host time per eager call, decode workload (append, dequant) and materialize workload"}
@@ -1036,7 +1047,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps before each timed run (the clocks and page tables settle within a few ms)")
     ap.add_argument("--leg-iters", type=int, default=50)
     ap.add_argument("--legs", default="prefill,materialize,four_over_six,contiguous,pool_quantize,attention,"
                                       "page_order,materialize_page_order,copy,host_cost",
@@ -1066,42 +1078,58 @@ def main():
         reps[0].sample_step(samples, picks)
 
     def step(i):
+        reps[i % n_rep].step()
+
+    def step_two_calls(i):
         r = reps[i % n_rep]
         r.append()
         r.dequant()
 
+    def wall_ms(fn):
+        # the timed region holds the steps alone: an event recorded between
+        # two kernels adds a few microseconds of gap to every step (measured:
+        # 127 vs 121 us per two-call step), which no serving loop has
+        with quiet_host():
+            for i in range(args.warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                fn(i)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / args.steps
+
     log(f"bench: timing {args.steps} steps")
-    # the timed region holds the steps alone: an event recorded between two
-    # kernels adds a few microseconds of gap to every step (measured: 127 vs
-    # 121 us per step), which no serving loop has
-    with quiet_host():
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(i)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    # the dequant's own launch time, for the roofline: as many dequant
-    # launches as timed steps, over the same replicas, back to back in three
-    # batches bracketed by HIP events on the stream they are launched on
-    log(f"bench: timing {args.steps} dequant launches")
+    ms_step = wall_ms(step)
+    log(f"bench: timing {args.steps} steps as two calls (append, then dequant)")
+    ms_two = wall_ms(step_two_calls)
+    # the step kernel's own launch time, for the roofline: as many launches
+    # as timed steps, over the same replicas, back to back in three batches
+    # bracketed by HIP events on the stream they are launched on
+    log(f"bench: timing {args.steps} step launches and {args.steps} dequant launches")
+    step_avg, step_med = env.steady([r.step for r in reps], args.steps, 5)
     deq_avg, deq_med = env.steady([r.dequant for r in reps], args.steps, 5)
     step_bytes = reps[0].append_bytes + reps[0].dequant_bytes
     value = step_bytes / (ms_step * 1e6)
-    achieved = reps[0].dequant_bytes / (deq_avg * 1e6)
+    achieved = step_bytes / (step_avg * 1e6)
+    deq_rate = reps[0].dequant_bytes / (deq_avg * 1e6)
 
     # append latency of the decode step: eager launches are bound by the
     # host-side launch path at this size, so the kernel time comes from
     # replays of a HIP graph holding 20 back-to-back appends
     app_eager_ms = env.steady([r.append for r in reps], 50, 5)[0]
     app_ms = graph_latency(env, [r.append for r in reps], 20, 10)
-    legs = {"decode_append_us": app_ms * 1e3, "decode_append_us_eager": app_eager_ms * 1e3,
+    legs = {"decode_step_kernel": {"kernel": "kv_append_dequantize_paged", "bytes": step_bytes,
+                                   "us_avg": step_avg * 1e3, "us_median": step_med * 1e3,
+                                   "GBps": achieved, "frac": achieved / PEAK_GBS},
+            "decode_step_two_calls": {"calls": "kv_quantize_append, then kv_dequantize_paged", "bytes": step_bytes,
+                                      "us_per_step": ms_two * 1e3, "GBps": step_bytes / (ms_two * 1e6),
+                                      "frac": step_bytes / (ms_two * 1e6) / PEAK_GBS},
+            "decode_append_us": app_ms * 1e3, "decode_append_us_eager": app_eager_ms * 1e3,
             "decode_dequant": {"kernel": "kv_dequantize_paged", "bytes": reps[0].dequant_bytes,
                                "us_avg": deq_avg * 1e3, "us_median": deq_med * 1e3,
-                               "GBps": achieved, "frac": achieved / PEAK_GBS}}
+                               "GBps": deq_rate, "frac": deq_rate / PEAK_GBS}}
     del reps
     torch.cuda.empty_cache()
     chosen = set() if args.no_legs else {x for x in args.legs.split(",") if x}
@@ -1155,12 +1183,14 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "decode_append: 64 requests x 1 new bf16 token (append) + dequantize of the full "
                                "context (124,503 tokens, bf16 out); page_size 16, 8 KV heads, head_dim 128, NHD, "
-                               "20,000-page shuffled pool, lengths U{1..4096}+1, seed 1002",
+                               "20,000-page shuffled pool, lengths U{1..4096}+1, seed 1002; one "
+                               "kv_append_dequantize_paged call per step",
                    "batch": 64, "page_size": 16, "num_kv_heads": 8, "head_dim": 128, "layout": "NHD",
                    "step_bytes": step_bytes, "peak_GBps": PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(),
-                     "kernel": "kv_dequantize_paged (dequant_kernel<NHD, bf16, int32 table>)"},
+                     "kernel": "kv_append_dequantize_paged (append_dequant_kernel<NHD, bf16 out, int32 table, "
+                               "bf16 in>)"},
         "cpu_baseline": cpu,
         "parity": parity,
         "legs": legs,

@@ -5,6 +5,7 @@
  *   kv_quantize_append   fp16/bf16 K/V rows -> packed E2M1 + E4M3 block scales
  *                        in paged NHD/HND caches addressed by a CSR page table
  *   kv_dequantize_paged  paged NVFP4 -> contiguous [B, T, H, D] fp16/bf16
+ *   kv_append_dequantize_paged  a decode step: both of the above, one launch
  *   kv_materialize_fp8   active pages -> float8_e4m3fn page copy + block table
  *   kv_global_scale      per-tensor global decode scale amax / (6 * e4m3_max)
  *   kv_quantize          contiguous fp16/bf16 -> NVFP4 with linear scales
@@ -13,7 +14,7 @@
  *                        scales optionally 4-token interleaved
  *   kv_decode_attention  one-token-per-request attention read straight
  *                        from the NVFP4 pages
- *   *_prepare + kvfp4_launch  the first three calls checked once, then
+ *   *_prepare + kvfp4_launch  the first four calls checked once, then
  *                        launched many times without re-checking
  *
  * Sources (FlashInfer 0.7.4 documentation): the API pages
@@ -162,6 +163,44 @@ kvfp4_status_t kv_dequantize_paged(const kvfp4_paged_cache_t *cache,
                                    int32_t max_seq_len, void *stream);
 
 /*
+ * kv_append_dequantize_paged - one decode step over a paged cache: the
+ * nvfp4_quantize_append_paged_kv_cache page's append of each request's newest
+ * token, then the nvfp4_kv_dequantize_paged page's dequantize of every
+ * request's context, including that token. The arguments are those of
+ * kv_quantize_append (cache through k_scale / v_scale / recipe: host global
+ * scales for the quantization) followed by those of kv_dequantize_paged
+ * (dequant_k_scale / dequant_v_scale: device fp32 scalars for the decode),
+ * with one batch_size for both and the same checks, plus nnz == batch_size
+ * (KVFP4_EINVAL otherwise). The cache and both outputs end exactly as after
+ * kv_quantize_append followed by kv_dequantize_paged on the same stream,
+ * provided the values follow the decode-step pattern (not checked, like
+ * every value): each request b has exactly one row r (batch_indices[r] ==
+ * b), at position positions[r] == seq_lens[b] - 1, and no other request of
+ * the call reaches the slot that row writes within its first seq_lens - 1
+ * tokens (requests that share pages read them, they do not append to them).
+ * For the standard recipe on layouts the gather path serves (every NHD
+ * cache; HND caches outside the LDS-staged geometry) it is one launch: the
+ * leading workgroups quantize the rows, store them in the cache and write
+ * their dequantized values into the outputs straight from the codes they
+ * computed, while the others dequantize every request without its newest
+ * token, so no workgroup reads a byte another writes. Otherwise it queues the
+ * two calls' kernels in sequence.
+ */
+kvfp4_status_t kv_append_dequantize_paged(const kvfp4_paged_cache_t *cache,
+                                          const void *append_key, const void *append_value,
+                                          int32_t in_dtype, int64_t nnz,
+                                          const int32_t *batch_indices, const int32_t *positions,
+                                          const int32_t *kv_indices, const int32_t *kv_indptr,
+                                          const int32_t *kv_last_page_len,
+                                          float k_scale, float v_scale, const kvfp4_recipe_t *recipe,
+                                          const void *block_tables, int32_t bt_dtype,
+                                          int64_t bt_row_stride, int32_t bt_cols,
+                                          const int32_t *seq_lens, int32_t batch_size,
+                                          const float *dequant_k_scale, const float *dequant_v_scale,
+                                          void *output_k, void *output_v, int32_t out_dtype,
+                                          int32_t max_seq_len, void *stream);
+
+/*
  * kv_materialize_fp8 - nvfp4_kv_materialize_fp8 / NVFP4KVMaterializer.run().
  * cache must be HND with page_size % 4 == 0 and head_dim % 64 == 0 (the
  * materializer's constraints); data page strides may exceed the compact
@@ -237,6 +276,19 @@ kvfp4_status_t kv_materialize_fp8_prepare(kvfp4_call_t *call, const kvfp4_paged_
                                           const int32_t *kv_page_indptr, int32_t batch_size, void *out_fp8,
                                           int64_t num_out_pages, int32_t *fp8_block_tables,
                                           int32_t max_pages_per_seq);
+
+kvfp4_status_t kv_append_dequantize_paged_prepare(kvfp4_call_t *call, const kvfp4_paged_cache_t *cache,
+                                                  const void *append_key, const void *append_value,
+                                                  int32_t in_dtype, int64_t nnz, const int32_t *batch_indices,
+                                                  const int32_t *positions, const int32_t *kv_indices,
+                                                  const int32_t *kv_indptr, const int32_t *kv_last_page_len,
+                                                  float k_scale, float v_scale, const kvfp4_recipe_t *recipe,
+                                                  const void *block_tables, int32_t bt_dtype,
+                                                  int64_t bt_row_stride, int32_t bt_cols,
+                                                  const int32_t *seq_lens, int32_t batch_size,
+                                                  const float *dequant_k_scale, const float *dequant_v_scale,
+                                                  void *output_k, void *output_v, int32_t out_dtype,
+                                                  int32_t max_seq_len);
 
 kvfp4_status_t kvfp4_launch(const kvfp4_call_t *call, void *stream);
 

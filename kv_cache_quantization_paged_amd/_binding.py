@@ -23,10 +23,11 @@ KVFP4_F16, KVFP4_BF16 = 0, 1
 KVFP4_I32, KVFP4_I64 = 0, 1
 KVFP4_ERR_MSE, KVFP4_ERR_MAE = 0, 1
 
-EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
-            "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
+EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_append_dequantize_paged", "kv_materialize_fp8",
+            "kv_global_scale", "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
             "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc", "kv_quantize_append_prepare",
-            "kv_dequantize_paged_prepare", "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_check_append_tables",
+            "kv_dequantize_paged_prepare", "kv_append_dequantize_paged_prepare", "kv_materialize_fp8_prepare",
+            "kvfp4_launch", "kvfp4_check_append_tables",
             "kvfp4_check_paged_tables", "kvfp4_check_materialize_tables", "kvfp4_table_problem_string",
             "kvfp4_status_string")
 
@@ -81,6 +82,10 @@ def load_library():
     lib.kv_materialize_fp8.restype = i32
     lib.kv_materialize_fp8.argtypes = [C.POINTER(PagedCacheDesc), i32, P, i32, i64, i64, i32, P, P, i32,
                                        P, i64, P, i32, P]
+    lib.kv_append_dequantize_paged.restype = i32
+    lib.kv_append_dequantize_paged.argtypes = [C.POINTER(PagedCacheDesc), P, P, i32, i64, P, P, P, P, P, f32, f32,
+                                               C.POINTER(RecipeDesc), P, i32, i64, i32, P, i32, P, P, P, P, i32,
+                                               i32, P]
     lib.kv_global_scale.restype = i32
     lib.kv_global_scale.argtypes = [P, i32, i64, f32, P, P]
     lib.kv_quantize.restype = i32
@@ -104,6 +109,8 @@ def load_library():
     lib.kv_dequantize_paged_prepare.argtypes = [P] + lib.kv_dequantize_paged.argtypes[:-1]
     lib.kv_materialize_fp8_prepare.restype = i32
     lib.kv_materialize_fp8_prepare.argtypes = [P] + lib.kv_materialize_fp8.argtypes[:-1]
+    lib.kv_append_dequantize_paged_prepare.restype = i32
+    lib.kv_append_dequantize_paged_prepare.argtypes = [P] + lib.kv_append_dequantize_paged.argtypes[:-1]
     lib.kvfp4_launch.restype = i32
     lib.kvfp4_launch.argtypes = [P, P]
     lib.kvfp4_check_append_tables.restype = i32
@@ -346,6 +353,50 @@ def prepare_dequantize_paged(cache: PagedCache, block_tables, seq_lens, k_scale,
     args = _dequant_args(cache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v)
     return _prepared("kv_dequantize_paged", lib.kv_dequantize_paged_prepare, args,
                      (cache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v), output_k.device.index)
+
+
+def _append_dequant_args(cache: PagedCache, append_key, append_value, batch_indices, positions, kv_indices,
+                         kv_indptr, kv_last_page_len, k_scale, v_scale, block_tables, seq_lens, dequant_k_scale,
+                         dequant_v_scale, output_k, output_v, recipe):
+    a = _append_args(cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                     kv_last_page_len, k_scale, v_scale, recipe)
+    d = _dequant_args(cache, block_tables, seq_lens, dequant_k_scale, dequant_v_scale, output_k, output_v)
+    nnz, batch = a[4], a[10]
+    if batch != d[6]:
+        raise ValueError("the append tables and the dequant batch disagree")
+    if nnz != batch:
+        raise ValueError("a decode step appends one row per request (nnz == batch)")
+    return a[:10] + a[11:] + d[1:]
+
+
+def kv_append_dequantize_paged(cache: PagedCache, append_key, append_value, batch_indices, positions, kv_indices,
+                               kv_indptr, kv_last_page_len, k_scale: float, v_scale: float, block_tables, seq_lens,
+                               dequant_k_scale, dequant_v_scale, output_k, output_v, recipe: Recipe | None = None,
+                               stream=None):
+    """A decode step: kv_quantize_append of each request's newest token, then
+    kv_dequantize_paged of every request (lengths including that token), in
+    one launch where the recipe and layout allow it."""
+    lib = load_library()
+    args = _append_dequant_args(cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                                kv_last_page_len, k_scale, v_scale, block_tables, seq_lens, dequant_k_scale,
+                                dequant_v_scale, output_k, output_v, recipe)
+    _check(lib.kv_append_dequantize_paged(*args, _stream(stream)), "kv_append_dequantize_paged")
+
+
+def prepare_append_dequantize_paged(cache: PagedCache, append_key, append_value, batch_indices, positions,
+                                    kv_indices, kv_indptr, kv_last_page_len, k_scale: float, v_scale: float,
+                                    block_tables, seq_lens, dequant_k_scale, dequant_v_scale, output_k, output_v,
+                                    recipe: Recipe | None = None) -> PreparedCall:
+    """kv_append_dequantize_paged checked once; ``.launch()`` runs the step
+    again with whatever the tensors hold at that time."""
+    lib = load_library()
+    args = _append_dequant_args(cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                                kv_last_page_len, k_scale, v_scale, block_tables, seq_lens, dequant_k_scale,
+                                dequant_v_scale, output_k, output_v, recipe)
+    return _prepared("kv_append_dequantize_paged", lib.kv_append_dequantize_paged_prepare, args,
+                     (cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                      kv_last_page_len, block_tables, seq_lens, dequant_k_scale, dequant_v_scale, output_k,
+                      output_v), output_k.device.index)
 
 
 def _materialize_args(cache: PagedCache, block_tables, seq_lens, kv_page_indptr, out, fp8_block_tables,

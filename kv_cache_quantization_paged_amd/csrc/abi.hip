@@ -83,7 +83,7 @@ extern "C" {
 // ---------------------------------------------------------------------------
 namespace {
 
-enum : uint32_t { kOpAppend = 1, kOpDequant = 2, kOpMaterialize = 3 };
+enum : uint32_t { kOpAppend = 1, kOpDequant = 2, kOpMaterialize = 3, kOpAppendDequant = 4 };
 
 struct AppendRec {
     kvfp4_paged_cache_t cache;
@@ -116,6 +116,23 @@ struct MaterializeRec {
     int32_t interleaved, shared, batch, max_pages_per_seq;
 };
 
+// the append and the dequantize of one decode step over one cache
+struct AppendDequantRec {
+    kvfp4_paged_cache_t cache;
+    const void *key, *value;
+    int64_t nnz;
+    const int32_t *batch_indices, *positions, *kv_indices, *kv_indptr;
+    float k_scale, v_scale;
+    int32_t in_bf16, has_recipe;
+    kvfp4_recipe_t recipe;
+    const void *block_tables;
+    int64_t bt_row_stride;
+    const int32_t *seq_lens;
+    const float *dq_k_scale, *dq_v_scale;
+    void *out_k, *out_v;
+    int32_t bt64, batch, out_bf16, max_seq_len;
+};
+
 struct CallRec {
     uint64_t seal;
     uint32_t op;
@@ -124,6 +141,7 @@ struct CallRec {
         AppendRec append;
         DequantRec dequant;
         MaterializeRec materialize;
+        AppendDequantRec append_dequant;
     } u;
 };
 static_assert(sizeof(CallRec) <= sizeof(kvfp4_call_t), "kvfp4_call_t is too small for the call records");
@@ -288,6 +306,64 @@ kvfp4_status_t prepare_materialize(CallRec *r, const kvfp4_paged_cache_t *cache,
     return KVFP4_OK;
 }
 
+// both calls' checks, exactly as each entry point runs them, plus one row per
+// request (nnz == batch_size)
+kvfp4_status_t prepare_append_dequant(CallRec *r, const kvfp4_paged_cache_t *cache, const void *append_key,
+                                      const void *append_value, int32_t in_dtype, int64_t nnz,
+                                      const int32_t *batch_indices, const int32_t *positions,
+                                      const int32_t *kv_indices, const int32_t *kv_indptr,
+                                      const int32_t *kv_last_page_len, float k_scale, float v_scale,
+                                      const kvfp4_recipe_t *recipe, const void *block_tables, int32_t bt_dtype,
+                                      int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
+                                      int32_t batch_size, const float *dq_k_scale, const float *dq_v_scale,
+                                      void *output_k, void *output_v, int32_t out_dtype, int32_t max_seq_len)
+{
+    CallRec ra, rd;
+    memset(&ra, 0, sizeof(ra));
+    memset(&rd, 0, sizeof(rd));
+    kvfp4_status_t s = prepare_append(&ra, cache, append_key, append_value, in_dtype, nnz, batch_indices, positions,
+                                      kv_indices, kv_indptr, kv_last_page_len, batch_size, k_scale, v_scale, recipe);
+    if (s != KVFP4_OK)
+        return s;
+    s = prepare_dequant(&rd, cache, block_tables, bt_dtype, bt_row_stride, bt_cols, seq_lens, batch_size, dq_k_scale,
+                        dq_v_scale, output_k, output_v, out_dtype, max_seq_len);
+    if (s != KVFP4_OK)
+        return s;
+    if (nnz != batch_size)
+        return KVFP4_EINVAL;
+    if (ra.nothing_to_do && rd.nothing_to_do) {
+        r->nothing_to_do = 1;
+        return KVFP4_OK;
+    }
+    AppendDequantRec &x = r->u.append_dequant;
+    x.cache = *cache;
+    x.key = append_key;
+    x.value = append_value;
+    x.nnz = nnz;
+    x.batch_indices = batch_indices;
+    x.positions = positions;
+    x.kv_indices = kv_indices;
+    x.kv_indptr = kv_indptr;
+    x.k_scale = k_scale;
+    x.v_scale = v_scale;
+    x.in_bf16 = in_dtype == KVFP4_BF16;
+    x.has_recipe = recipe != nullptr;
+    if (recipe)
+        x.recipe = *recipe;
+    x.block_tables = block_tables;
+    x.bt_row_stride = bt_row_stride;
+    x.seq_lens = seq_lens;
+    x.dq_k_scale = dq_k_scale;
+    x.dq_v_scale = dq_v_scale;
+    x.out_k = output_k;
+    x.out_v = output_v;
+    x.bt64 = bt_dtype == KVFP4_I64;
+    x.batch = batch_size;
+    x.out_bf16 = out_dtype == KVFP4_BF16;
+    x.max_seq_len = rd.nothing_to_do ? 0 : max_seq_len;
+    return KVFP4_OK;
+}
+
 kvfp4_status_t launch_rec(const CallRec *r, hipStream_t st)
 {
     if (r->nothing_to_do)
@@ -311,6 +387,13 @@ kvfp4_status_t launch_rec(const CallRec *r, hipStream_t st)
                                                m.bt_row_stride, m.bt_kv_stride, m.seq_lens, m.kv_page_indptr,
                                                m.batch, m.out, m.num_out_pages, m.fp8_block_tables,
                                                m.max_pages_per_seq, st));
+    }
+    case kOpAppendDequant: {
+        const AppendDequantRec &x = r->u.append_dequant;
+        return from_hip(launch_append_dequantize_paged(
+            x.cache, x.key, x.value, x.in_bf16 != 0, x.nnz, x.batch_indices, x.positions, x.kv_indices, x.kv_indptr,
+            x.k_scale, x.v_scale, x.has_recipe ? &x.recipe : nullptr, x.block_tables, x.bt64 != 0, x.bt_row_stride,
+            x.seq_lens, x.batch, x.dq_k_scale, x.dq_v_scale, x.out_k, x.out_v, x.out_bf16 != 0, x.max_seq_len, st));
     }
     default:
         return KVFP4_EINVAL;
@@ -364,6 +447,24 @@ kvfp4_status_t kv_materialize_fp8_prepare(kvfp4_call_t *call, const kvfp4_paged_
                                          out_fp8, num_out_pages, fp8_block_tables, max_pages_per_seq));
 }
 
+kvfp4_status_t kv_append_dequantize_paged_prepare(
+    kvfp4_call_t *call, const kvfp4_paged_cache_t *cache, const void *append_key, const void *append_value,
+    int32_t in_dtype, int64_t nnz, const int32_t *batch_indices, const int32_t *positions, const int32_t *kv_indices,
+    const int32_t *kv_indptr, const int32_t *kv_last_page_len, float k_scale, float v_scale,
+    const kvfp4_recipe_t *recipe, const void *block_tables, int32_t bt_dtype, int64_t bt_row_stride, int32_t bt_cols,
+    const int32_t *seq_lens, int32_t batch_size, const float *dequant_k_scale, const float *dequant_v_scale,
+    void *output_k, void *output_v, int32_t out_dtype, int32_t max_seq_len)
+{
+    if (!call)
+        return KVFP4_EINVAL;
+    CallRec *r = begin(call, kOpAppendDequant);
+    return finish(r, prepare_append_dequant(r, cache, append_key, append_value, in_dtype, nnz, batch_indices,
+                                            positions, kv_indices, kv_indptr, kv_last_page_len, k_scale, v_scale,
+                                            recipe, block_tables, bt_dtype, bt_row_stride, bt_cols, seq_lens,
+                                            batch_size, dequant_k_scale, dequant_v_scale, output_k, output_v,
+                                            out_dtype, max_seq_len));
+}
+
 kvfp4_status_t kvfp4_launch(const kvfp4_call_t *call, void *stream)
 {
     if (!call)
@@ -400,6 +501,23 @@ kvfp4_status_t kv_dequantize_paged(const kvfp4_paged_cache_t *cache, const void 
     const kvfp4_status_t s = prepare_dequant(r, cache, block_tables, bt_dtype, bt_row_stride, bt_cols, seq_lens,
                                              batch_size, k_scale, v_scale, output_k, output_v, out_dtype,
                                              max_seq_len);
+    return s != KVFP4_OK ? s : launch_rec(r, (hipStream_t)stream);
+}
+
+kvfp4_status_t kv_append_dequantize_paged(
+    const kvfp4_paged_cache_t *cache, const void *append_key, const void *append_value, int32_t in_dtype, int64_t nnz,
+    const int32_t *batch_indices, const int32_t *positions, const int32_t *kv_indices, const int32_t *kv_indptr,
+    const int32_t *kv_last_page_len, float k_scale, float v_scale, const kvfp4_recipe_t *recipe,
+    const void *block_tables, int32_t bt_dtype, int64_t bt_row_stride, int32_t bt_cols, const int32_t *seq_lens,
+    int32_t batch_size, const float *dequant_k_scale, const float *dequant_v_scale, void *output_k, void *output_v,
+    int32_t out_dtype, int32_t max_seq_len, void *stream)
+{
+    kvfp4_call_t call;
+    CallRec *r = begin(&call, kOpAppendDequant);
+    const kvfp4_status_t s = prepare_append_dequant(
+        r, cache, append_key, append_value, in_dtype, nnz, batch_indices, positions, kv_indices, kv_indptr,
+        kv_last_page_len, k_scale, v_scale, recipe, block_tables, bt_dtype, bt_row_stride, bt_cols, seq_lens,
+        batch_size, dequant_k_scale, dequant_v_scale, output_k, output_v, out_dtype, max_seq_len);
     return s != KVFP4_OK ? s : launch_rec(r, (hipStream_t)stream);
 }
 

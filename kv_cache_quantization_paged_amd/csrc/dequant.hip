@@ -24,8 +24,12 @@
 // are decoded by gfx950's conversion instructions (exact: E4M3 -> fp32, and
 // FP4 -> fp32 with a unit scale), then two fp32 multiplies in that order and
 // one round-to-nearest-even conversion per value.
+//
+// append_dequant_kernel (at the end) runs a decode step's append and this
+// gather in one launch.
 #include "kvfp4_internal.h"
 #include "nvfp4_device.h"
+#include "quant_block.h"
 
 namespace kvfp4 {
 
@@ -69,9 +73,8 @@ struct DequantArgs {
 // (k / C) * 8C + x * C + k % C, so each XCD works through runs of C
 // consecutive items. A bijection on [0, grid) when the grid is a multiple of
 // 8C.
-__device__ __forceinline__ int first_item(int chunk)
+__device__ __forceinline__ int first_item(int bid, int chunk)
 {
-    const int bid = (int)blockIdx.x;
     if (chunk == 0)
         return bid;
     const int x = bid & 7, k = bid >> 3;
@@ -101,11 +104,13 @@ __device__ __forceinline__ u32x4 decode_chunk(uint32_t codes, float dec)
     return r;
 }
 
+// the gather dequant's items item0, item0 + step, ... of the launch; a
+// request's length counts as seq_lens[b] - len_sub (len_sub 1: its last token
+// is written by someone else)
 template <bool HND, bool BF16, bool BT64>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const void *__restrict__ block_tables,
-                                                           const int32_t *__restrict__ seq_lens,
-                                                           const float *__restrict__ k_scale,
-                                                           const float *__restrict__ v_scale)
+__device__ __forceinline__ void dequant_items(const DequantArgs &a, int item0, int step,
+                                              const void *__restrict__ block_tables,
+                                              const int32_t *__restrict__ seq_lens, const float g[2], int len_sub)
 {
     constexpr int kBatch = batch_of<HND>();
     constexpr int kUnit = kBatch * kThreads;   // chunks per work item
@@ -116,7 +121,6 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const 
     // (+1 on a carry from cc), and the row's (t, h) follow
     const int r_step = kThreads / cpr, c_step = kThreads - r_step * cpr;
     const int rt_step = r_step / a.H, rh_step = r_step - rt_step * a.H;
-    const float g[2] = {*k_scale, *v_scale};
     // HND offset steps for kThreads chunks: base step, extra on a chunk-column
     // carry (next head row of the same token), extra on a head wrap (head 0 of
     // the next token)
@@ -131,12 +135,12 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const 
     const uint32_t page_sf_bytes = (uint32_t)(a.ps * a.H * nb);
 
     // one item per workgroup (the loop only repeats for more than kMaxGrid)
-    for (int item = first_item(a.xcd_chunk); item < a.num_items; item += gridDim.x) {
+    for (int item = item0; item < a.num_items; item += step) {
         const int pair = item / a.parts;
         const int part = item - pair * a.parts;
         const int b = pair / a.pages_per_req;
         const int j = pair - b * a.pages_per_req;
-        const int len = min(seq_lens[b], a.T);
+        const int len = min(seq_lens[b] - len_sub, a.T);
         const int t_first = j * a.ps;
         if (t_first >= len)
             continue;
@@ -207,6 +211,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const 
             }
         }
     }
+}
+
+template <bool HND, bool BF16, bool BT64>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, const void *__restrict__ block_tables,
+                                                           const int32_t *__restrict__ seq_lens,
+                                                           const float *__restrict__ k_scale,
+                                                           const float *__restrict__ v_scale)
+{
+    const float g[2] = {*k_scale, *v_scale};
+    dequant_items<HND, BF16, BT64>(a, first_item((int)blockIdx.x, a.xcd_chunk), (int)gridDim.x, block_tables,
+                                   seq_lens, g, 0);
 }
 
 // HND pages through LDS. When a token's H * D / 8 chunks divide the item
@@ -302,6 +317,126 @@ __global__ __launch_bounds__(kThreads) void dequant_hnd_lds_kernel(DequantArgs a
     }
 }
 
+// ------------------------------------------------ append + dequant, fused ----
+// One launch for a decode step (the append page's rows, then the dequantize
+// page over the same cache): row r of the append is request
+// batch_indices[r]'s newest token, at position seq_lens[b] - 1. The first
+// `blocks` workgroups quantize the rows exactly as the append kernel does
+// (standard recipe), store their codes and scales in the cache and write the
+// rows' dequantized values straight into the outputs (the same fp32 steps as
+// the gather, from the codes and scale just computed); the other workgroups
+// run the gather over every request with its length cut by one. No workgroup
+// reads a byte another one writes in the launch, so there is no ordering to
+// keep, and the outputs and cache equal those of the two calls in sequence.
+struct AppendPart {
+    uint8_t *data[2];
+    uint8_t *sf[2];
+    const uint8_t *in[2];
+    float g[2];          // the append's global scales (host arguments)
+    int64_t nnz;
+    int32_t batch;
+    int32_t blocks;      // leading workgroups that take the rows (a multiple of 8)
+};
+
+struct RowScaleTables {
+    float dec[2][128];
+    float inv[2][128];
+};
+
+// block c (16 elements) of head h of row r, K and V: quantized as the append
+// kernel does it, stored at the row's (page, slot), and its 16 values
+// dequantized into out[b, pos, h, 16c ..]
+template <bool HND, bool BF16_IN, bool BF16>
+__device__ __forceinline__ void append_row_block(const DequantArgs &a, const AppendPart &p, const RowScaleTables &tab,
+                                                 const float g_out[2], int64_t r, int b, int pos, int64_t page,
+                                                 int h, int c)
+{
+    const int nb = a.D >> 4;
+    const int slot = pos % a.ps;
+    const int64_t row = HND ? ((int64_t)h * a.ps + slot) : ((int64_t)slot * a.H + h);
+    // the output row exists for positions inside max_seq_len (later ones are
+    // cut, as the gather cuts them) and requests inside the batch
+    const bool out_ok = (unsigned)pos < (unsigned)a.T && (unsigned)b < (unsigned)p.batch;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+        float x[16];
+        load_block<BF16_IN>(p.in[kv] + (((r * a.H + h) * a.D) + c * 16) * 2, x);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+        uint32_t s;
+        const uint2 codes = quantize_block<0>(x, amax, p.g[kv], 448.0f, tab.dec[kv], tab.inv[kv], s);
+        const u32x2 cv = {codes.x, codes.y};
+        __builtin_nontemporal_store(cv, (u32x2 *)(p.data[kv] + page * a.stride[kv] + row * (a.D >> 1) + c * 8));
+        p.sf[kv][page * a.sf_stride[kv] + row * nb + c] = (uint8_t)s;
+        if (out_ok) {
+            const float dec = e4m3_byte_to_f32(s) * g_out[kv];
+            u32x4 *o = (u32x4 *)(a.out[kv] + (((int64_t)b * a.T + pos) * a.H + h) * a.D + c * 16);
+            o[0] = decode_chunk<BF16>(codes.x, dec);
+            o[1] = decode_chunk<BF16>(codes.y, dec);
+        }
+    }
+}
+
+// 8 waves per SIMD as the NHD gather alone reaches (the rows' scalar
+// addressing would otherwise take the SGPR count past it)
+template <bool HND, bool BF16, bool BT64, bool BF16_IN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void append_dequant_kernel(DequantArgs a, AppendPart p,
+                                                                  const void *__restrict__ block_tables,
+                                                                  const int32_t *__restrict__ seq_lens,
+                                                                  const float *__restrict__ k_scale,
+                                                                  const float *__restrict__ v_scale,
+                                                                  const int32_t *__restrict__ batch_indices,
+                                                                  const int32_t *__restrict__ positions,
+                                                                  const int32_t *__restrict__ kv_indices,
+                                                                  const int32_t *__restrict__ kv_indptr)
+{
+    __shared__ RowScaleTables tab;
+    const float g[2] = {*k_scale, *v_scale};
+    const int bid = (int)blockIdx.x;
+    if (bid >= p.blocks) {
+        // p.blocks is a multiple of 8, so each XCD keeps its runs of items
+        dequant_items<HND, BF16, BT64>(a, first_item(bid - p.blocks, a.xcd_chunk), (int)gridDim.x - p.blocks,
+                                       block_tables, seq_lens, g, 1);
+        return;
+    }
+    const int tid = threadIdx.x;
+    {
+        // the append's decode factor and its reciprocal per (tensor, scale byte)
+        const int kv = tid >> 7, s = tid & 127;
+        const float dec = e4m3_byte_to_f32((uint32_t)s) * p.g[kv];
+        tab.dec[kv][s] = dec;
+        tab.inv[kv][s] = (dec == 0.0f) ? 0.0f : 1.0f / dec;
+    }
+    __syncthreads();
+    const int nb = a.D >> 4;
+    const int bpr = a.H * nb;                         // blocks per row (all heads)
+    if (bpr <= kThreads) {
+        const int rows_per_iter = kThreads / bpr;
+        const int row_off = tid / bpr;
+        if (row_off >= rows_per_iter)
+            return;
+        const int hc = tid - row_off * bpr;
+        const int h = hc / nb, c = hc - (hc / nb) * nb;
+        for (int64_t r = (int64_t)bid * rows_per_iter + row_off; r < p.nnz; r += (int64_t)p.blocks * rows_per_iter) {
+            const int b = batch_indices[r];
+            const int pos = positions[r];
+            const int64_t page = kv_indices[kv_indptr[b] + pos / a.ps];
+            append_row_block<HND, BF16_IN, BF16>(a, p, tab, g, r, b, pos, page, h, c);
+        }
+    } else {
+        for (int64_t r = bid; r < p.nnz; r += p.blocks) {
+            const int b = batch_indices[r];
+            const int pos = positions[r];
+            const int64_t page = kv_indices[kv_indptr[b] + pos / a.ps];
+            for (int hc = tid; hc < bpr; hc += kThreads) {
+                const int h = hc / nb, c = hc - (hc / nb) * nb;
+                append_row_block<HND, BF16_IN, BF16>(a, p, tab, g, r, b, pos, page, h, c);
+            }
+        }
+    }
+}
+
 struct DequantPtrs {
     const void *block_tables;
     const int32_t *seq_lens;
@@ -320,14 +455,11 @@ hipError_t launch3(bool bt64, const DequantArgs &a, const DequantPtrs &p, int gr
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *block_tables, bool bt64,
-                                   int64_t bt_row_stride, const int32_t *seq_lens, int32_t batch,
-                                   const float *k_scale, const float *v_scale, void *out_k, void *out_v,
-                                   bool out_bf16, int32_t max_seq_len, hipStream_t st)
+// the gather's arguments (every field but the items of the LDS path) and
+// its grid; returns the item count (0: nothing to do, -1: too many)
+int64_t setup_gather(const kvfp4_paged_cache_t &c, int64_t bt_row_stride, int32_t batch, void *out_k, void *out_v,
+                     int32_t max_seq_len, DequantArgs &a, int &grid)
 {
-    DequantArgs a;
     a.data[0] = (const uint8_t *)c.k_data;
     a.data[1] = (const uint8_t *)c.v_data;
     a.sf[0] = (const uint8_t *)c.k_sf;
@@ -349,60 +481,171 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
     a.parts = (int32_t)((page_chunks + unit - 1) / unit);
     const int64_t items = (int64_t)batch * a.pages_per_req * a.parts;
     if (items == 0)
-        return hipSuccess;
+        return 0;
     if (items > INT32_MAX)
-        return hipErrorInvalidValue;
+        return -1;
     a.num_items = (int32_t)items;
-    const DequantPtrs p = {block_tables, seq_lens, k_scale, v_scale};
     a.xcd_chunk = 0;
-    int grid = (int)(items < kMaxGrid ? items : kMaxGrid);
+    grid = (int)(items < kMaxGrid ? items : kMaxGrid);
     if (kXcdChunk > 0 && items < kMaxGrid) {
         const int64_t run = 8 * (int64_t)kXcdChunk * a.parts;
         a.xcd_chunk = kXcdChunk * a.parts;
         grid = (int)((items + run - 1) / run * run);
     }
-    const bool hnd = c.layout == KVFP4_HND;
-    if (hnd) {
-        // the LDS path: chunks per token a power of two dividing the item,
-        // the item's tokens dividing the page, at most 64 heads, rows of at
-        // least 16 code bytes (16-byte aligned head runs)
-        const int64_t cpt = (int64_t)c.num_kv_heads * (c.head_dim / 8);
-        const int64_t unit_lds = (int64_t)kBatchLds * kThreads;
-        if ((cpt & (cpt - 1)) == 0 && cpt <= unit_lds && c.page_size % (unit_lds / cpt) == 0 &&
-            c.num_kv_heads <= 64 && c.head_dim >= 32) {
-            HndLdsShape sh;
-            sh.ti = (int32_t)(unit_lds / cpt);
-            a.parts = (int32_t)(c.page_size / sh.ti);
-            const int64_t items_lds = (int64_t)batch * a.pages_per_req * a.parts;
-            if (items_lds > INT32_MAX)
-                return hipErrorInvalidValue;
-            a.num_items = (int32_t)items_lds;
-            const int grid_lds = (int)(items_lds < kMaxGrid ? items_lds : kMaxGrid);
-            sh.s_cpt = __builtin_ctzll((unsigned long long)cpt);
-            sh.s_cpr = __builtin_ctz((unsigned)(c.head_dim / 8));
-            const size_t lds = (size_t)2 * c.num_kv_heads * (sh.ti * (c.head_dim / 2) + kLdsPad) +
-                               (size_t)2 * c.num_kv_heads * sh.ti * (c.head_dim / 16);
-            if (bt64) {
-                if (out_bf16)
-                    hipLaunchKernelGGL((dequant_hnd_lds_kernel<true, true>), dim3(grid_lds), dim3(kThreads), lds, st, a,
-                                       sh, block_tables, seq_lens, k_scale, v_scale);
-                else
-                    hipLaunchKernelGGL((dequant_hnd_lds_kernel<false, true>), dim3(grid_lds), dim3(kThreads), lds, st, a,
-                                       sh, block_tables, seq_lens, k_scale, v_scale);
-            } else {
-                if (out_bf16)
-                    hipLaunchKernelGGL((dequant_hnd_lds_kernel<true, false>), dim3(grid_lds), dim3(kThreads), lds, st, a,
-                                       sh, block_tables, seq_lens, k_scale, v_scale);
-                else
-                    hipLaunchKernelGGL((dequant_hnd_lds_kernel<false, false>), dim3(grid_lds), dim3(kThreads), lds, st,
-                                       a, sh, block_tables, seq_lens, k_scale, v_scale);
-            }
-            return hipGetLastError();
+    return items;
+}
+
+// the LDS path's item shape for HND pages: chunks per token a power of two
+// dividing the item, the item's tokens dividing the page, at most 64 heads,
+// rows of at least 16 code bytes (16-byte aligned head runs)
+bool hnd_lds_shape(const kvfp4_paged_cache_t &c, HndLdsShape &sh)
+{
+    if (c.layout != KVFP4_HND)
+        return false;
+    const int64_t cpt = (int64_t)c.num_kv_heads * (c.head_dim / 8);
+    const int64_t unit_lds = (int64_t)kBatchLds * kThreads;
+    if ((cpt & (cpt - 1)) != 0 || cpt > unit_lds || c.page_size % (unit_lds / cpt) != 0 || c.num_kv_heads > 64 ||
+        c.head_dim < 32)
+        return false;
+    sh.ti = (int32_t)(unit_lds / cpt);
+    sh.s_cpt = __builtin_ctzll((unsigned long long)cpt);
+    sh.s_cpr = __builtin_ctz((unsigned)(c.head_dim / 8));
+    return true;
+}
+
+}  // namespace
+
+hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *block_tables, bool bt64,
+                                   int64_t bt_row_stride, const int32_t *seq_lens, int32_t batch,
+                                   const float *k_scale, const float *v_scale, void *out_k, void *out_v,
+                                   bool out_bf16, int32_t max_seq_len, hipStream_t st)
+{
+    DequantArgs a;
+    int grid = 0;
+    const int64_t items = setup_gather(c, bt_row_stride, batch, out_k, out_v, max_seq_len, a, grid);
+    if (items == 0)
+        return hipSuccess;
+    if (items < 0)
+        return hipErrorInvalidValue;
+    const DequantPtrs p = {block_tables, seq_lens, k_scale, v_scale};
+    HndLdsShape sh;
+    if (hnd_lds_shape(c, sh)) {
+        a.parts = (int32_t)(c.page_size / sh.ti);
+        const int64_t items_lds = (int64_t)batch * a.pages_per_req * a.parts;
+        if (items_lds > INT32_MAX)
+            return hipErrorInvalidValue;
+        a.num_items = (int32_t)items_lds;
+        const int grid_lds = (int)(items_lds < kMaxGrid ? items_lds : kMaxGrid);
+        const size_t lds = (size_t)2 * c.num_kv_heads * (sh.ti * (c.head_dim / 2) + kLdsPad) +
+                           (size_t)2 * c.num_kv_heads * sh.ti * (c.head_dim / 16);
+        if (bt64) {
+            if (out_bf16)
+                hipLaunchKernelGGL((dequant_hnd_lds_kernel<true, true>), dim3(grid_lds), dim3(kThreads), lds, st, a, sh,
+                                   block_tables, seq_lens, k_scale, v_scale);
+            else
+                hipLaunchKernelGGL((dequant_hnd_lds_kernel<false, true>), dim3(grid_lds), dim3(kThreads), lds, st, a, sh,
+                                   block_tables, seq_lens, k_scale, v_scale);
+        } else {
+            if (out_bf16)
+                hipLaunchKernelGGL((dequant_hnd_lds_kernel<true, false>), dim3(grid_lds), dim3(kThreads), lds, st, a, sh,
+                                   block_tables, seq_lens, k_scale, v_scale);
+            else
+                hipLaunchKernelGGL((dequant_hnd_lds_kernel<false, false>), dim3(grid_lds), dim3(kThreads), lds, st, a,
+                                   sh, block_tables, seq_lens, k_scale, v_scale);
         }
+        return hipGetLastError();
     }
+    const bool hnd = c.layout == KVFP4_HND;
     if (hnd)
         return out_bf16 ? launch3<true, true>(bt64, a, p, grid, st) : launch3<true, false>(bt64, a, p, grid, st);
     return out_bf16 ? launch3<false, true>(bt64, a, p, grid, st) : launch3<false, false>(bt64, a, p, grid, st);
+}
+
+namespace {
+
+template <bool HND, bool BF16, bool BT64>
+hipError_t launch_fused3(bool in_bf16, const DequantArgs &a, const AppendPart &ap, const DequantPtrs &p,
+                         const int32_t *batch_indices, const int32_t *positions, const int32_t *kv_indices,
+                         const int32_t *kv_indptr, int grid, hipStream_t st)
+{
+    if (in_bf16)
+        hipLaunchKernelGGL((append_dequant_kernel<HND, BF16, BT64, true>), dim3(grid), dim3(kThreads), 0, st, a, ap,
+                           p.block_tables, p.seq_lens, p.k_scale, p.v_scale, batch_indices, positions, kv_indices,
+                           kv_indptr);
+    else
+        hipLaunchKernelGGL((append_dequant_kernel<HND, BF16, BT64, false>), dim3(grid), dim3(kThreads), 0, st, a, ap,
+                           p.block_tables, p.seq_lens, p.k_scale, p.v_scale, batch_indices, positions, kv_indices,
+                           kv_indptr);
+    return hipGetLastError();
+}
+
+template <bool HND, bool BF16>
+hipError_t launch_fused2(bool bt64, bool in_bf16, const DequantArgs &a, const AppendPart &ap, const DequantPtrs &p,
+                         const int32_t *batch_indices, const int32_t *positions, const int32_t *kv_indices,
+                         const int32_t *kv_indptr, int grid, hipStream_t st)
+{
+    return bt64 ? launch_fused3<HND, BF16, true>(in_bf16, a, ap, p, batch_indices, positions, kv_indices, kv_indptr,
+                                                 grid, st)
+                : launch_fused3<HND, BF16, false>(in_bf16, a, ap, p, batch_indices, positions, kv_indices, kv_indptr,
+                                                  grid, st);
+}
+
+constexpr int kMaxAppendWorkgroups = 1024;
+
+}  // namespace
+
+hipError_t launch_append_dequantize_paged(const kvfp4_paged_cache_t &c, const void *key, const void *value,
+                                          bool in_bf16, int64_t nnz, const int32_t *batch_indices,
+                                          const int32_t *positions, const int32_t *kv_indices,
+                                          const int32_t *kv_indptr, float k_g, float v_g,
+                                          const kvfp4_recipe_t *recipe, const void *block_tables, bool bt64,
+                                          int64_t bt_row_stride, const int32_t *seq_lens, int32_t batch,
+                                          const float *k_scale, const float *v_scale, void *out_k, void *out_v,
+                                          bool out_bf16, int32_t max_seq_len, hipStream_t st)
+{
+    // one launch for the standard recipe on the gather's layouts; the 4over6
+    // recipes and the LDS-staged HND geometry run the two calls in sequence
+    HndLdsShape sh;
+    DequantArgs a;
+    int grid = 0;
+    const int64_t items = setup_gather(c, bt_row_stride, batch, out_k, out_v, max_seq_len, a, grid);
+    if (recipe != nullptr || nnz == 0 || items <= 0 || hnd_lds_shape(c, sh)) {
+        hipError_t e = launch_quantize_append(c, key, value, in_bf16, nnz, batch_indices, positions, kv_indices,
+                                              kv_indptr, k_g, v_g, recipe, st);
+        if (e != hipSuccess)
+            return e;
+        return launch_dequantize_paged(c, block_tables, bt64, bt_row_stride, seq_lens, batch, k_scale, v_scale, out_k,
+                                       out_v, out_bf16, max_seq_len, st);
+    }
+    AppendPart ap;
+    ap.data[0] = (uint8_t *)c.k_data;
+    ap.data[1] = (uint8_t *)c.v_data;
+    ap.sf[0] = (uint8_t *)c.k_sf;
+    ap.sf[1] = (uint8_t *)c.v_sf;
+    ap.in[0] = (const uint8_t *)key;
+    ap.in[1] = (const uint8_t *)value;
+    ap.g[0] = k_g;
+    ap.g[1] = v_g;
+    ap.nnz = nnz;
+    ap.batch = batch;
+    const int64_t bpr = (int64_t)c.num_kv_heads * (c.head_dim / 16);
+    const int64_t rows_per_wg = bpr <= kThreads ? kThreads / bpr : 1;
+    int64_t wgs = (nnz + rows_per_wg - 1) / rows_per_wg;
+    wgs = wgs < kMaxAppendWorkgroups ? wgs : kMaxAppendWorkgroups;
+    ap.blocks = (int32_t)((wgs + 7) / 8 * 8);
+    if ((int64_t)grid + ap.blocks > INT32_MAX / kThreads)
+        return hipErrorInvalidValue;
+    const DequantPtrs p = {block_tables, seq_lens, k_scale, v_scale};
+    const int total = grid + ap.blocks;
+    if (c.layout == KVFP4_HND)
+        return out_bf16 ? launch_fused2<true, true>(bt64, in_bf16, a, ap, p, batch_indices, positions, kv_indices,
+                                                    kv_indptr, total, st)
+                        : launch_fused2<true, false>(bt64, in_bf16, a, ap, p, batch_indices, positions, kv_indices,
+                                                     kv_indptr, total, st);
+    return out_bf16 ? launch_fused2<false, true>(bt64, in_bf16, a, ap, p, batch_indices, positions, kv_indices,
+                                                 kv_indptr, total, st)
+                    : launch_fused2<false, false>(bt64, in_bf16, a, ap, p, batch_indices, positions, kv_indices,
+                                                  kv_indptr, total, st);
 }
 
 }  // namespace kvfp4

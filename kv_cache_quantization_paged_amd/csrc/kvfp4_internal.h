@@ -23,6 +23,18 @@ hipError_t launch_dequantize_paged(const kvfp4_paged_cache_t &c, const void *blo
                                    const float *k_scale, const float *v_scale, void *out_k, void *out_v,
                                    bool out_bf16, int32_t max_seq_len, hipStream_t st);
 
+// the append then the dequantize of a decode step (each request's newest
+// token is one appended row, at position seq_lens[b] - 1), in one launch
+// where the recipe and layout allow it
+hipError_t launch_append_dequantize_paged(const kvfp4_paged_cache_t &c, const void *key, const void *value,
+                                          bool in_bf16, int64_t nnz, const int32_t *batch_indices,
+                                          const int32_t *positions, const int32_t *kv_indices,
+                                          const int32_t *kv_indptr, float k_g, float v_g,
+                                          const kvfp4_recipe_t *recipe, const void *block_tables, bool bt64,
+                                          int64_t bt_row_stride, const int32_t *seq_lens, int32_t batch,
+                                          const float *k_scale, const float *v_scale, void *out_k, void *out_v,
+                                          bool out_bf16, int32_t max_seq_len, hipStream_t st);
+
 hipError_t launch_materialize_fp8(const kvfp4_paged_cache_t &c, bool v_interleaved, const int32_t *bt,
                                   bool shared, int64_t bt_row_stride, int64_t bt_kv_stride,
                                   const int32_t *seq_lens, const int32_t *indptr, int32_t batch,

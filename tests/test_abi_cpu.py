@@ -26,10 +26,12 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["kv_quantize_append", "kv_dequantize_paged", "kv_materialize_fp8", "kv_global_scale",
+    assert names == sorted(["kv_quantize_append", "kv_dequantize_paged", "kv_append_dequantize_paged",
+                            "kv_materialize_fp8", "kv_global_scale",
                             "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
                             "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc",
                             "kv_quantize_append_prepare", "kv_dequantize_paged_prepare",
+                            "kv_append_dequantize_paged_prepare",
                             "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_check_append_tables",
                             "kvfp4_check_paged_tables", "kvfp4_check_materialize_tables",
                             "kvfp4_table_problem_string", "kvfp4_status_string"])
@@ -104,6 +106,47 @@ def test_dequant_rejects_bad_arguments(B):
     assert call(_cache(B), batch=-1) == B.KVFP4_EINVAL
     assert call(_cache(B), batch=0, bt=None, sl=None) == B.KVFP4_OK
     assert call(_cache(B), T=0) == B.KVFP4_OK
+
+
+def _step(B, cache, prepare=False, **kw):
+    P = C.c_void_p
+    a = dict(key=P(4096), value=P(8192), dtype=1, nnz=2, bi=P(64), pos=P(64), ind=P(64), ptr=P(64), last=P(64),
+             ks=1.0, vs=1.0, recipe=None, bt=P(64), bt_dtype=0, row=4, cols=4, sl=P(64), batch=2, dks=P(64),
+             dvs=P(64), ok=P(4096), ov=P(8192), out_dtype=1, T=16)
+    a.update(kw)
+    lib = B.load_library()
+    args = (C.byref(cache), a["key"], a["value"], a["dtype"], a["nnz"], a["bi"], a["pos"], a["ind"], a["ptr"],
+            a["last"], a["ks"], a["vs"], a["recipe"], a["bt"], a["bt_dtype"], a["row"], a["cols"], a["sl"], a["batch"],
+            a["dks"], a["dvs"], a["ok"], a["ov"], a["out_dtype"], a["T"])
+    if prepare:
+        rec = (C.c_uint64 * 40)()
+        return lib.kv_append_dequantize_paged_prepare(C.addressof(rec), *args)
+    return lib.kv_append_dequantize_paged(*args, None)
+
+
+def test_append_dequant_rejects_bad_arguments(B):
+    """the fused decode step runs both calls' checks and needs one row per
+    request; its prepare returns the same statuses"""
+    P = C.c_void_p
+    for prepare in (False, True):
+        assert _step(B, _cache(B, k_data=None), prepare) == B.KVFP4_EINVAL
+        assert _step(B, _cache(B), prepare, dtype=7) == B.KVFP4_EINVAL           # append input dtype
+        assert _step(B, _cache(B), prepare, ks=0.0) == B.KVFP4_EINVAL            # append global scale
+        assert _step(B, _cache(B), prepare, key=P(4100)) == B.KVFP4_EALIGN
+        assert _step(B, _cache(B), prepare, last=None) == B.KVFP4_EINVAL
+        assert _step(B, _cache(B), prepare, bt_dtype=3) == B.KVFP4_EINVAL        # dequant table dtype
+        assert _step(B, _cache(B), prepare, out_dtype=3) == B.KVFP4_EINVAL
+        assert _step(B, _cache(B), prepare, row=2, cols=4) == B.KVFP4_EINVAL
+        assert _step(B, _cache(B), prepare, dks=None) == B.KVFP4_EINVAL
+        assert _step(B, _cache(B), prepare, ok=P(4104)) == B.KVFP4_EALIGN
+        assert _step(B, _cache(B), prepare, nnz=3) == B.KVFP4_EINVAL             # rows != requests
+        if prepare:
+            assert _step(B, _cache(B), prepare) == B.KVFP4_OK                # valid arguments prepare (no launch)
+        bad = B.RecipeDesc(300.0, 0, 0)
+        assert _step(B, _cache(B), prepare, recipe=C.byref(bad)) == B.KVFP4_EINVAL
+        # an empty step queues nothing, even with null pointers
+        assert _step(B, _cache(B), prepare, nnz=0, batch=0, key=None, value=None, bi=None, bt=None,
+                     sl=None) == B.KVFP4_OK
 
 
 def test_materialize_rejects_bad_arguments(B):
