@@ -249,3 +249,35 @@ def test_graph_decode_step(K):
         K.kv_dequantize_paged(dev.cache, bt, sl, gk, gv, ok, ov)
         K.kv_decode_attention(dev.cache, q, bt, sl, gk, gv, D ** -0.5, out, ws)
     check_replays(fn, list(dev.bases) + [ok, ov, out], "decode step")
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_graph_append_dequantize_paged(K, layout):
+    """the one-launch decode step (append, then dequantize, one kernel) and
+    the attention that reads its cache, in one graph"""
+    ps, H, D, G = 16, 4, 128, 2
+    old = np.array([0, 15, 16, 300, 77, 31], np.int64)
+    new = old + 1
+    maxp = int((new.max() + ps - 1) // ps)
+    B, P = len(old), len(old) * maxp + 4
+    lay = K.KVFP4_NHD if layout == "NHD" else K.KVFP4_HND
+    dev = random_cache(K, P, ps, H, D, lay, 91, data_pad=16, sf_hi=0x40)
+    indices, indptr, last = W.csr_for_lengths(new, ps, np.random.default_rng(92).permutation(P))
+    bt = i32(W.block_table_from_csr(indices, indptr, maxp))
+    key = rand_half((B, H, D), 93)
+    val = rand_half((B, H, D), 94)
+    sl = i32(new)
+    order = np.random.default_rng(95).permutation(B)
+    bi, pos = i32(order), i32(old[order])
+    ind, ptr, lst = i32(indices), i32(indptr), i32(last)
+    gk, gv = torch.tensor([0.5], device="cuda"), torch.tensor([0.25], device="cuda")
+    T = int(new.max())
+    ok, ov = junk((B, T, H, D), torch.bfloat16, 96), junk((B, T, H, D), torch.bfloat16, 97)
+    q = rand_half((B, H * G, D), 98)
+    out = junk(q.shape, torch.bfloat16, 99)
+    ws = junk((K.kv_decode_attention_workspace_size(B, H, H * G, maxp, ps),), torch.uint8, 100)
+
+    def fn():
+        K.kv_append_dequantize_paged(dev.cache, key, val, bi, pos, ind, ptr, lst, 0.5, 0.25, bt, sl, gk, gv, ok, ov)
+        K.kv_decode_attention(dev.cache, q, bt, sl, gk, gv, D ** -0.5, out, ws)
+    check_replays(fn, list(dev.bases) + [ok, ov, out], f"one-launch decode step ({layout})")
