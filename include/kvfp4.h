@@ -441,7 +441,8 @@ enum {
     KVFP4_TABLE_DUPLICATE_ROW = 7,   /* two rows write the same (request, position): they race */
     KVFP4_TABLE_LENGTH_RANGE = 8,    /* a length below 0 or longer than the table row addresses */
     KVFP4_TABLE_RESERVATION = 9,     /* kv_page_indptr reserves fewer pages than a request needs */
-    KVFP4_TABLE_OUT_PAGES = 10       /* out has fewer than kv_page_indptr[batch_size] + 1 pages */
+    KVFP4_TABLE_OUT_PAGES = 10,      /* out has fewer than kv_page_indptr[batch_size] + 1 pages */
+    KVFP4_TABLE_STEP_POSITION = 11   /* a decode-step row's position is not seq_lens[b] - 1 */
 };
 typedef struct {
     int32_t problem;
@@ -460,6 +461,16 @@ kvfp4_status_t kvfp4_check_append_tables(const int32_t *batch_indices, const int
                                          const int32_t *kv_indices, const int32_t *kv_indptr,
                                          const int32_t *kv_last_page_len, int32_t batch_size, int32_t page_size,
                                          int32_t num_pages, int64_t *scratch, kvfp4_table_report_t *report);
+
+/* kv_append_dequantize_paged's rows (on top of the two checks above and
+ * below, which its append and dequant tables need as well): nnz ==
+ * batch_size (KVFP4_EINVAL otherwise), every row's request in range and its
+ * position seq_lens[b] - 1, and, with `scratch` (host memory for batch_size
+ * int64 values, overwritten), no request named by two rows. Whether another
+ * request reads a row's slot is not checked. */
+kvfp4_status_t kvfp4_check_step_rows(const int32_t *batch_indices, const int32_t *positions, int64_t nnz,
+                                     const int32_t *seq_lens, int32_t batch_size, int64_t *scratch,
+                                     kvfp4_table_report_t *report);
 
 /* kv_dequantize_paged's (max_seq_len as given) and kv_decode_attention's
  * (max_seq_len = INT32_MAX, bt_dtype KVFP4_I32) tables: every length is

@@ -16,7 +16,7 @@ from ._binding import (KVFP4Error, PagedCache, Recipe, kv_dequantize, kv_dequant
                        kv_decode_attention_workspace_size, kv_decode_attention_noalloc, load_library,
                        status_string, PreparedCall, prepare_quantize_append, prepare_dequantize_paged,
                        prepare_materialize_fp8, kv_append_dequantize_paged, prepare_append_dequantize_paged,
-                       TableError, check_append_tables, check_paged_tables,
+                       TableError, check_append_tables, check_step_rows, check_paged_tables,
                        check_materialize_tables)
 from ._binding import (KVFP4_BF16, KVFP4_ERR_MAE, KVFP4_ERR_MSE, KVFP4_F16, KVFP4_HND,  # noqa: F401
                        KVFP4_I32, KVFP4_I64, KVFP4_NHD)

@@ -27,7 +27,7 @@ EXPORTED = ("kv_quantize_append", "kv_dequantize_paged", "kv_append_dequantize_p
             "kv_global_scale", "kv_quantize", "kv_dequantize", "kv_quantize_paged_cache", "kv_decode_attention",
             "kv_decode_attention_workspace_size", "kv_decode_attention_noalloc", "kv_quantize_append_prepare",
             "kv_dequantize_paged_prepare", "kv_append_dequantize_paged_prepare", "kv_materialize_fp8_prepare",
-            "kvfp4_launch", "kvfp4_check_append_tables",
+            "kvfp4_launch", "kvfp4_check_append_tables", "kvfp4_check_step_rows",
             "kvfp4_check_paged_tables", "kvfp4_check_materialize_tables", "kvfp4_table_problem_string",
             "kvfp4_status_string")
 
@@ -115,6 +115,8 @@ def load_library():
     lib.kvfp4_launch.argtypes = [P, P]
     lib.kvfp4_check_append_tables.restype = i32
     lib.kvfp4_check_append_tables.argtypes = [P, P, i64, P, P, P, i32, i32, i32, P, C.POINTER(TableReport)]
+    lib.kvfp4_check_step_rows.restype = i32
+    lib.kvfp4_check_step_rows.argtypes = [P, P, i64, P, i32, P, C.POINTER(TableReport)]
     lib.kvfp4_check_paged_tables.restype = i32
     lib.kvfp4_check_paged_tables.argtypes = [P, i32, i64, i32, P, i32, i32, i32, i32, C.POINTER(TableReport)]
     lib.kvfp4_check_materialize_tables.restype = i32
@@ -617,6 +619,20 @@ def check_append_tables(batch_indices, positions, kv_indices, kv_indptr, kv_last
                                                   _np_ptr(last), ptr.size - 1, page_size, num_pages,
                                                   None if scratch is None else _np_ptr(scratch), C.byref(rep))
     _table_result(st, rep, "append tables")
+
+
+def check_step_rows(batch_indices, positions, seq_lens, check_duplicates: bool = True):
+    """Raise TableError unless the rows follow kv_append_dequantize_paged's
+    decode-step pattern: one row per request, at position seq_lens[b] - 1."""
+    import numpy as np
+    bi, pos, sl = _host_ints(batch_indices, np.int32), _host_ints(positions, np.int32), _host_ints(seq_lens, np.int32)
+    if bi.shape != pos.shape or bi.size != sl.size:
+        raise ValueError("a decode step has one row per request")
+    scratch = np.empty(sl.size, np.int64) if check_duplicates else None
+    rep = TableReport()
+    st = load_library().kvfp4_check_step_rows(_np_ptr(bi), _np_ptr(pos), bi.size, _np_ptr(sl), sl.size,
+                                              None if scratch is None else _np_ptr(scratch), C.byref(rep))
+    _table_result(st, rep, "decode-step rows")
 
 
 def check_paged_tables(block_tables, seq_lens, page_size: int, num_pages: int, max_seq_len: int = 2 ** 31 - 1):

@@ -129,6 +129,36 @@ kvfp4_status_t kvfp4_check_append_tables(const int32_t *batch_indices, const int
     return ok(report);
 }
 
+kvfp4_status_t kvfp4_check_step_rows(const int32_t *batch_indices, const int32_t *positions, int64_t nnz,
+                                     const int32_t *seq_lens, int32_t batch_size, int64_t *scratch,
+                                     kvfp4_table_report_t *report)
+{
+    if (!report)
+        return KVFP4_EINVAL;
+    if (nnz != batch_size || batch_size < 0 || (batch_size > 0 && (!batch_indices || !positions || !seq_lens)))
+        return KVFP4_EINVAL;
+    for (int64_t r = 0; r < nnz; ++r) {
+        const int32_t b = batch_indices[r];
+        if (b < 0 || b >= batch_size)
+            return fail(report, KVFP4_TABLE_BATCH_RANGE, r, b);
+        if ((int64_t)positions[r] != (int64_t)seq_lens[b] - 1)
+            return fail(report, KVFP4_TABLE_STEP_POSITION, r, positions[r]);
+    }
+    if (scratch) {
+        // one row per request: with nnz == batch_size a request seen twice
+        // is the same as a request missing
+        for (int32_t b = 0; b < batch_size; ++b)
+            scratch[b] = -1;
+        for (int64_t r = 0; r < nnz; ++r) {
+            const int32_t b = batch_indices[r];
+            if (scratch[b] >= 0)
+                return fail(report, KVFP4_TABLE_DUPLICATE_ROW, r, b);
+            scratch[b] = r;
+        }
+    }
+    return ok(report);
+}
+
 kvfp4_status_t kvfp4_check_paged_tables(const void *block_tables, int32_t bt_dtype, int64_t bt_row_stride,
                                         int32_t bt_cols, const int32_t *seq_lens, int32_t batch_size,
                                         int32_t page_size, int32_t num_pages, int32_t max_seq_len,
@@ -211,6 +241,7 @@ const char *kvfp4_table_problem_string(int32_t problem)
     case KVFP4_TABLE_LENGTH_RANGE: return "a length below 0 or longer than its table row addresses";
     case KVFP4_TABLE_RESERVATION: return "kv_page_indptr reserves fewer pages than the request needs";
     case KVFP4_TABLE_OUT_PAGES: return "out has fewer than kv_page_indptr[batch_size] + 1 pages";
+    case KVFP4_TABLE_STEP_POSITION: return "a decode-step row's position is not its request's newest token";
     default: return "unknown problem";
     }
 }

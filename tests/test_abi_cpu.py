@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
                             "kv_quantize_append_prepare", "kv_dequantize_paged_prepare",
                             "kv_append_dequantize_paged_prepare",
                             "kv_materialize_fp8_prepare", "kvfp4_launch", "kvfp4_check_append_tables",
+                            "kvfp4_check_step_rows",
                             "kvfp4_check_paged_tables", "kvfp4_check_materialize_tables",
                             "kvfp4_table_problem_string", "kvfp4_status_string"])
 

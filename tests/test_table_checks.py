@@ -13,7 +13,7 @@ import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, EINVAL, EVALUE = 0, 1, 6
-(T_OK, T_START, T_ORDER, T_PAGE, T_BATCH, T_POS, T_LAST, T_DUP, T_LEN, T_RES, T_OUT) = range(11)
+(T_OK, T_START, T_ORDER, T_PAGE, T_BATCH, T_POS, T_LAST, T_DUP, T_LEN, T_RES, T_OUT, T_STEP) = range(12)
 
 
 class Report(C.Structure):
@@ -35,6 +35,8 @@ def lib():
     lib.kvfp4_check_materialize_tables.restype = i32
     lib.kvfp4_check_materialize_tables.argtypes = [P, i32, i64, i64, i32, P, P, i32, i32, i32, i32, i64,
                                                    C.POINTER(Report)]
+    lib.kvfp4_check_step_rows.restype = i32
+    lib.kvfp4_check_step_rows.argtypes = [P, P, i64, P, i32, P, C.POINTER(Report)]
     lib.kvfp4_table_problem_string.restype = C.c_char_p
     lib.kvfp4_table_problem_string.argtypes = [i32]
     return lib
@@ -206,3 +208,36 @@ def test_python_wrappers_raise_with_the_location():
     K.check_materialize_tables(mbt, lens, mptr, 16, P, maxp, P + 1, uses_shared_paged_kv_idx=False)
     with pytest.raises(K.TableError):
         K.check_materialize_tables(mbt, lens, mptr, 16, P, maxp, P, uses_shared_paged_kv_idx=False)
+
+
+def step_rows(lib, bi, pos, lens, dup=True, nnz=None):
+    bi, pos, lens = (np.ascontiguousarray(x, np.int32) for x in (bi, pos, lens))
+    scratch = np.zeros(len(lens), np.int64) if dup else None
+    r = Report()
+    st = lib.kvfp4_check_step_rows(ptr(bi), ptr(pos), len(bi) if nnz is None else nnz, ptr(lens), len(lens),
+                                   ptr(scratch), C.byref(r))
+    return st, (r.problem, r.index, r.value)
+
+
+def test_step_rows(lib):
+    """the one-launch decode step's rows: one per request, at its newest
+    token; the decode workload's step passes"""
+    old, new_len, *_ = decode_tables()
+    rng = np.random.default_rng(5)
+    order = rng.permutation(64)
+    assert step_rows(lib, order, old[order], new_len)[0] == OK
+    assert step_rows(lib, np.arange(64), old, new_len)[0] == OK
+    pos = old.copy()
+    pos[9] -= 1                                            # not the newest token
+    assert step_rows(lib, np.arange(64), pos, new_len) == (EVALUE, (T_STEP, 9, int(pos[9])))
+    bi = np.arange(64)
+    bi[3] = 64                                             # request out of range
+    assert step_rows(lib, bi, old, new_len)[1][:2] == (T_BATCH, 3)
+    bi = np.arange(64)
+    bi[40] = 7                                             # request 7 twice, request 40 missing
+    pos = old[bi]
+    assert step_rows(lib, bi, pos, new_len) == (EVALUE, (T_DUP, 40, 7))
+    assert step_rows(lib, bi, pos, new_len, dup=False)[0] == OK      # without scratch: not checked
+    assert step_rows(lib, np.arange(64), old, new_len, nnz=63)[0] == EINVAL   # rows != requests
+    assert step_rows(lib, np.zeros(0), np.zeros(0), np.zeros(0))[0] == OK
+    assert lib.kvfp4_table_problem_string(T_STEP).decode() != "unknown problem"
