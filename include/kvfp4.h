@@ -178,13 +178,12 @@ kvfp4_status_t kv_dequantize_paged(const kvfp4_paged_cache_t *cache,
  * b), at position positions[r] == seq_lens[b] - 1, and no other request of
  * the call reaches the slot that row writes within its first seq_lens - 1
  * tokens (requests that share pages read them, they do not append to them).
- * For the standard recipe on layouts the gather path serves (every NHD
- * cache; HND caches outside the LDS-staged geometry) it is one launch: the
- * leading workgroups quantize the rows, store them in the cache and write
- * their dequantized values into the outputs straight from the codes they
+ * For the standard recipe it is one launch, on every layout: the leading
+ * workgroups quantize the rows, store them in the cache and write their
+ * dequantized values into the outputs straight from the codes they
  * computed, while the others dequantize every request without its newest
- * token, so no workgroup reads a byte another writes. Otherwise it queues the
- * two calls' kernels in sequence.
+ * token, so no workgroup reads a byte another writes. With a 4over6 recipe it
+ * queues the two calls' kernels in sequence.
  */
 kvfp4_status_t kv_append_dequantize_paged(const kvfp4_paged_cache_t *cache,
                                           const void *append_key, const void *append_value,

@@ -25,8 +25,8 @@
 // FP4 -> fp32 with a unit scale), then two fp32 multiplies in that order and
 // one round-to-nearest-even conversion per value.
 //
-// append_dequant_kernel (at the end) runs a decode step's append and this
-// gather in one launch.
+// append_dequant_kernel and append_dequant_lds_kernel (at the end) run a
+// decode step's append and this gather in one launch.
 #include "kvfp4_internal.h"
 #include "nvfp4_device.h"
 #include "quant_block.h"
@@ -244,14 +244,13 @@ struct HndLdsShape {
     int32_t s_cpt, s_cpr;        // log2 of chunks per token (H * D / 8) and per row (D / 8)
 };
 
+// the LDS-staged items item0, item0 + step, ... (len_sub as in dequant_items)
 template <bool BF16, bool BT64>
-__global__ __launch_bounds__(kThreads) void dequant_hnd_lds_kernel(DequantArgs a, HndLdsShape sh,
-                                                                   const void *__restrict__ block_tables,
-                                                                   const int32_t *__restrict__ seq_lens,
-                                                                   const float *__restrict__ k_scale,
-                                                                   const float *__restrict__ v_scale)
+__device__ __forceinline__ void dequant_lds_items(const DequantArgs &a, const HndLdsShape &sh, int item0, int step,
+                                                  const void *__restrict__ block_tables,
+                                                  const int32_t *__restrict__ seq_lens, const float g[2],
+                                                  int len_sub, uint8_t *lds)
 {
-    extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x;
     const int ti = sh.ti, half_row = a.D >> 1, nb = a.D >> 4;
     const int code_head = ti * half_row + kLdsPad, code_tensor = a.H * code_head;
@@ -260,16 +259,15 @@ __global__ __launch_bounds__(kThreads) void dequant_hnd_lds_kernel(DequantArgs a
     const int pieces_head = ti * half_row / 16, pieces = a.H * pieces_head;   // 16-byte code pieces
     const int spieces_head = sf_head / 4, spieces = a.H * spieces_head;       // 4-byte scale pieces
     const int cpt_mask = (1 << sh.s_cpt) - 1, cpr_mask = (1 << sh.s_cpr) - 1;
-    const float g[2] = {*k_scale, *v_scale};
     const uint32_t page_bytes = (uint32_t)(a.ps * a.H * half_row);
     const uint32_t page_sf_bytes = (uint32_t)(a.ps * a.H * nb);
 
-    for (int item = blockIdx.x; item < a.num_items; item += gridDim.x) {
+    for (int item = item0; item < a.num_items; item += step) {
         const int pair = item / a.parts;
         const int part = item - pair * a.parts;
         const int b = pair / a.pages_per_req;
         const int j = pair - b * a.pages_per_req;
-        const int len = min(seq_lens[b], a.T);
+        const int len = min(seq_lens[b] - len_sub, a.T);
         const int t_a = part * ti;                        // the item's first token in the page
         const int t_first = j * a.ps + t_a;
         if (t_first >= len)
@@ -315,6 +313,18 @@ __global__ __launch_bounds__(kThreads) void dequant_hnd_lds_kernel(DequantArgs a
         }
         __syncthreads();                                  // LDS is reused by the next item of this workgroup
     }
+}
+
+template <bool BF16, bool BT64>
+__global__ __launch_bounds__(kThreads) void dequant_hnd_lds_kernel(DequantArgs a, HndLdsShape sh,
+                                                                   const void *__restrict__ block_tables,
+                                                                   const int32_t *__restrict__ seq_lens,
+                                                                   const float *__restrict__ k_scale,
+                                                                   const float *__restrict__ v_scale)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    const float g[2] = {*k_scale, *v_scale};
+    dequant_lds_items<BF16, BT64>(a, sh, (int)blockIdx.x, (int)gridDim.x, block_tables, seq_lens, g, 0, lds);
 }
 
 // ------------------------------------------------ append + dequant, fused ----
@@ -378,28 +388,16 @@ __device__ __forceinline__ void append_row_block(const DequantArgs &a, const App
     }
 }
 
-// 8 waves per SIMD as the NHD gather alone reaches (the rows' scalar
-// addressing would otherwise take the SGPR count past it)
-template <bool HND, bool BF16, bool BT64, bool BF16_IN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void append_dequant_kernel(DequantArgs a, AppendPart p,
-                                                                  const void *__restrict__ block_tables,
-                                                                  const int32_t *__restrict__ seq_lens,
-                                                                  const float *__restrict__ k_scale,
-                                                                  const float *__restrict__ v_scale,
-                                                                  const int32_t *__restrict__ batch_indices,
-                                                                  const int32_t *__restrict__ positions,
-                                                                  const int32_t *__restrict__ kv_indices,
-                                                                  const int32_t *__restrict__ kv_indptr)
+// the leading workgroups' rows (tab: their scale tables, in LDS)
+template <bool HND, bool BF16_IN, bool BF16>
+__device__ __forceinline__ void append_rows(const DequantArgs &a, const AppendPart &p, const float g[2],
+                                            RowScaleTables *tabp, const int32_t *__restrict__ batch_indices,
+                                            const int32_t *__restrict__ positions,
+                                            const int32_t *__restrict__ kv_indices,
+                                            const int32_t *__restrict__ kv_indptr)
 {
-    __shared__ RowScaleTables tab;
-    const float g[2] = {*k_scale, *v_scale};
+    RowScaleTables &tab = *tabp;
     const int bid = (int)blockIdx.x;
-    if (bid >= p.blocks) {
-        // p.blocks is a multiple of 8, so each XCD keeps its runs of items
-        dequant_items<HND, BF16, BT64>(a, first_item(bid - p.blocks, a.xcd_chunk), (int)gridDim.x - p.blocks,
-                                       block_tables, seq_lens, g, 1);
-        return;
-    }
     const int tid = threadIdx.x;
     {
         // the append's decode factor and its reciprocal per (tensor, scale byte)
@@ -435,6 +433,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
             }
         }
     }
+}
+
+// 8 waves per SIMD as the NHD gather alone reaches (the rows' scalar
+// addressing would otherwise take the SGPR count past it)
+template <bool HND, bool BF16, bool BT64, bool BF16_IN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void append_dequant_kernel(DequantArgs a, AppendPart p,
+                                                                  const void *__restrict__ block_tables,
+                                                                  const int32_t *__restrict__ seq_lens,
+                                                                  const float *__restrict__ k_scale,
+                                                                  const float *__restrict__ v_scale,
+                                                                  const int32_t *__restrict__ batch_indices,
+                                                                  const int32_t *__restrict__ positions,
+                                                                  const int32_t *__restrict__ kv_indices,
+                                                                  const int32_t *__restrict__ kv_indptr)
+{
+    __shared__ RowScaleTables tab;
+    const float g[2] = {*k_scale, *v_scale};
+    const int bid = (int)blockIdx.x;
+    if (bid >= p.blocks) {
+        // p.blocks is a multiple of 8, so each XCD keeps its runs of items
+        dequant_items<HND, BF16, BT64>(a, first_item(bid - p.blocks, a.xcd_chunk), (int)gridDim.x - p.blocks,
+                                       block_tables, seq_lens, g, 1);
+        return;
+    }
+    append_rows<HND, BF16_IN, BF16>(a, p, g, &tab, batch_indices, positions, kv_indices, kv_indptr);
+}
+
+// the same step for HND pools of the LDS-staged gather's geometry (8 waves
+// per SIMD, as that gather alone reaches)
+template <bool BF16, bool BT64, bool BF16_IN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void append_dequant_lds_kernel(DequantArgs a, HndLdsShape sh, AppendPart p,
+                                                                      const void *__restrict__ block_tables,
+                                                                      const int32_t *__restrict__ seq_lens,
+                                                                      const float *__restrict__ k_scale,
+                                                                      const float *__restrict__ v_scale,
+                                                                      const int32_t *__restrict__ batch_indices,
+                                                                      const int32_t *__restrict__ positions,
+                                                                      const int32_t *__restrict__ kv_indices,
+                                                                      const int32_t *__restrict__ kv_indptr)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    const float g[2] = {*k_scale, *v_scale};
+    const int bid = (int)blockIdx.x;
+    if (bid >= p.blocks) {
+        dequant_lds_items<BF16, BT64>(a, sh, bid - p.blocks, (int)gridDim.x - p.blocks, block_tables, seq_lens, g, 1,
+                                      lds);
+        return;
+    }
+    append_rows<true, BF16_IN, BF16>(a, p, g, (RowScaleTables *)lds, batch_indices, positions, kv_indices, kv_indptr);
 }
 
 struct DequantPtrs {
@@ -603,13 +650,13 @@ hipError_t launch_append_dequantize_paged(const kvfp4_paged_cache_t &c, const vo
                                           const float *k_scale, const float *v_scale, void *out_k, void *out_v,
                                           bool out_bf16, int32_t max_seq_len, hipStream_t st)
 {
-    // one launch for the standard recipe on the gather's layouts; the 4over6
-    // recipes and the LDS-staged HND geometry run the two calls in sequence
+    // one launch for the standard recipe; the 4over6 recipes run the two
+    // calls in sequence
     HndLdsShape sh;
     DequantArgs a;
     int grid = 0;
     const int64_t items = setup_gather(c, bt_row_stride, batch, out_k, out_v, max_seq_len, a, grid);
-    if (recipe != nullptr || nnz == 0 || items <= 0 || hnd_lds_shape(c, sh)) {
+    if (recipe != nullptr || nnz == 0 || items <= 0) {
         hipError_t e = launch_quantize_append(c, key, value, in_bf16, nnz, batch_indices, positions, kv_indices,
                                               kv_indptr, k_g, v_g, recipe, st);
         if (e != hipSuccess)
@@ -636,6 +683,39 @@ hipError_t launch_append_dequantize_paged(const kvfp4_paged_cache_t &c, const vo
     if ((int64_t)grid + ap.blocks > INT32_MAX / kThreads)
         return hipErrorInvalidValue;
     const DequantPtrs p = {block_tables, seq_lens, k_scale, v_scale};
+    if (hnd_lds_shape(c, sh)) {
+        a.parts = (int32_t)(c.page_size / sh.ti);
+        const int64_t items_lds = (int64_t)batch * a.pages_per_req * a.parts;
+        if (items_lds > INT32_MAX)
+            return hipErrorInvalidValue;
+        a.num_items = (int32_t)items_lds;
+        const int64_t grid_lds = items_lds < kMaxGrid ? items_lds : kMaxGrid;
+        if (grid_lds + ap.blocks > INT32_MAX / kThreads)
+            return hipErrorInvalidValue;
+        size_t lds = (size_t)2 * c.num_kv_heads * (sh.ti * (c.head_dim / 2) + kLdsPad) +
+                     (size_t)2 * c.num_kv_heads * sh.ti * (c.head_dim / 16);
+        lds = lds > sizeof(RowScaleTables) ? lds : sizeof(RowScaleTables);   // the rows' workgroups keep their tables there
+        const int total_lds = (int)grid_lds + ap.blocks;
+#define KVFP4_FUSED_LDS(BF, B64, BIN)                                                                                \
+    hipLaunchKernelGGL((append_dequant_lds_kernel<BF, B64, BIN>), dim3(total_lds), dim3(kThreads), lds, st, a, sh, ap, \
+                       p.block_tables, p.seq_lens, p.k_scale, p.v_scale, batch_indices, positions, kv_indices,         \
+                       kv_indptr)
+        if (out_bf16) {
+            if (bt64) {
+                if (in_bf16) KVFP4_FUSED_LDS(true, true, true); else KVFP4_FUSED_LDS(true, true, false);
+            } else {
+                if (in_bf16) KVFP4_FUSED_LDS(true, false, true); else KVFP4_FUSED_LDS(true, false, false);
+            }
+        } else {
+            if (bt64) {
+                if (in_bf16) KVFP4_FUSED_LDS(false, true, true); else KVFP4_FUSED_LDS(false, true, false);
+            } else {
+                if (in_bf16) KVFP4_FUSED_LDS(false, false, true); else KVFP4_FUSED_LDS(false, false, false);
+            }
+        }
+#undef KVFP4_FUSED_LDS
+        return hipGetLastError();
+    }
     const int total = grid + ap.blocks;
     if (c.layout == KVFP4_HND)
         return out_bf16 ? launch_fused2<true, true>(bt64, in_bf16, a, ap, p, batch_indices, positions, kv_indices,

@@ -4,9 +4,9 @@ cache and both outputs, untouched tails included. Covers both layouts, page
 sizes 1-64, head geometries whose rows take one workgroup or several,
 input / output / table dtypes, request rows in any order, lengths cut by
 max_seq_len, append and dequant global scales that differ, batches past one
-append workgroup per row group, and the cases that run the two calls in
-sequence instead (the 4over6 recipes, the HND geometry of the LDS-staged
-gather); then a prepared step launched for two consecutive decode steps."""
+append workgroup per row group, HND geometries of the LDS-staged gather, and
+the 4over6 recipes (which run the two calls in sequence instead); then a
+prepared step launched for two consecutive decode steps."""
 import numpy as np
 import pytest
 import torch
@@ -155,9 +155,12 @@ def test_append_dequant_four_over_six_runs_the_two_calls(K, orc, recipe):
     run_step(K, orc, 9300, W.NHD, 16, 8, 128, 7, recipe=recipe)
 
 
-def test_append_dequant_lds_geometry_runs_the_two_calls(K, orc):
-    """HND, 8 heads of 128, page 32: the gather would stage it through LDS"""
-    run_step(K, orc, 9400, W.HND, 32, 8, 128, 6, out_bf16=False, bt64=True)
+@pytest.mark.parametrize("ps,H,D", [(32, 8, 128), (16, 8, 128), (64, 4, 64), (4, 32, 256)])
+@pytest.mark.parametrize("in_bf16,out_bf16,bt64", [(True, True, False), (False, False, True)])
+def test_append_dequant_lds_geometry(K, orc, ps, H, D, in_bf16, out_bf16, bt64):
+    """HND geometries whose gather stages head runs through LDS: one launch
+    of the LDS-staged variant"""
+    run_step(K, orc, 9400 + ps + H + D, W.HND, ps, H, D, 9, in_bf16, out_bf16, bt64)
 
 
 @pytest.mark.parametrize("layout", [W.NHD, W.HND])
