@@ -207,3 +207,21 @@ def test_append_dequant_prepared_two_steps(K, orc, layout):
         val.copy_(bits_tensor(s.nv, True))
         pos_t.copy_(i32(s.pos))
         lens_t.copy_(i32(s.new_len))
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_append_dequant_random_shapes(K, orc, case):
+    """seeded draws over layout, page size, heads and head_dim (HND shapes on
+    both sides of the LDS-staged gather's conditions), dtypes, table dtype,
+    batch, max_seq_len cuts and the recipe"""
+    rng = np.random.default_rng(9600 + case)
+    layout = W.NHD if rng.random() < 0.5 else W.HND
+    ps = int(rng.choice([1, 4, 5, 8, 16, 32, 64]))
+    H = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    D = int(rng.choice([16, 32, 48, 64, 128, 256]))
+    in_bf16, out_bf16, bt64 = (bool(x) for x in rng.random(3) < 0.5)
+    B = int(rng.integers(1, 40))
+    T_delta = int(rng.choice([0, 3, -2]))
+    recipe = "standard" if rng.random() < 0.85 else str(rng.choice(["mse", "mae", "mse16"]))
+    run_step(K, orc, 9700 + case, layout, ps, H, D, B, in_bf16, out_bf16, bt64, T_delta=T_delta, recipe=recipe,
+             g_dq_factor=float(rng.choice([1.0, 0.5])))
