@@ -21,7 +21,8 @@ from ._binding import (KVFP4Error, PagedCache, Recipe, kv_dequantize, kv_dequant
 from ._binding import (KVFP4_BF16, KVFP4_ERR_MAE, KVFP4_ERR_MSE, KVFP4_F16, KVFP4_HND,  # noqa: F401
                        KVFP4_I32, KVFP4_I64, KVFP4_NHD)
 from .api import (NVFP44Over6Config, NVFP4KVMaterializer, make_nvfp4_global_scale,  # noqa: F401
-                  nvfp4_e4m3_max, nvfp4_kv_dequantize, nvfp4_kv_dequantize_paged, nvfp4_kv_materialize_fp8,
+                  nvfp4_append_dequantize_paged, nvfp4_e4m3_max, nvfp4_kv_dequantize, nvfp4_kv_dequantize_paged,
+                  nvfp4_kv_materialize_fp8,
                   nvfp4_kv_quantize, nvfp4_quantize_append_paged_kv_cache, nvfp4_quantize_paged_kv_cache,
                   paged_cache)
 

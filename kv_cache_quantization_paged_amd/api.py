@@ -117,6 +117,21 @@ def nvfp4_kv_dequantize_paged(paged_kv_cache: CacheArg, kv_cache_sf: CacheArg, b
     B.kv_dequantize_paged(cache, block_tables, seq_lens, k_scale, v_scale, output_k, output_v)
 
 
+def nvfp4_append_dequantize_paged(append_key, append_value, batch_indices, positions, paged_kv_cache: CacheArg,
+                                  kv_cache_sf: CacheArg, kv_indices, kv_indptr, kv_last_page_len, k_scale: float,
+                                  v_scale: float, block_tables, seq_lens, dequant_k_scale: torch.Tensor,
+                                  dequant_v_scale: torch.Tensor, output_k, output_v, kv_layout: str = "NHD",
+                                  nvfp4_4over6: Optional[NVFP44Over6Config] = None) -> None:
+    """One decode step: nvfp4_quantize_append_paged_kv_cache of each
+    request's newest token (one row per request, at position seq_lens[b] - 1),
+    then nvfp4_kv_dequantize_paged of every request, as one call."""
+    cache = paged_cache(paged_kv_cache, kv_cache_sf, kv_layout)
+    recipe = nvfp4_4over6._recipe() if nvfp4_4over6 is not None else None
+    B.kv_append_dequantize_paged(cache, append_key, append_value, batch_indices, positions, kv_indices, kv_indptr,
+                                 kv_last_page_len, k_scale, v_scale, block_tables, seq_lens, dequant_k_scale,
+                                 dequant_v_scale, output_k, output_v, recipe)
+
+
 def _hnd_cache(k_cache, v_cache, k_block_scales, v_block_scales) -> B.PagedCache:
     return B.PagedCache(k_cache, v_cache, k_block_scales, v_block_scales, B.KVFP4_HND)
 

@@ -225,3 +225,34 @@ def test_append_dequant_random_shapes(K, orc, case):
     recipe = "standard" if rng.random() < 0.85 else str(rng.choice(["mse", "mae", "mse16"]))
     run_step(K, orc, 9700 + case, layout, ps, H, D, B, in_bf16, out_bf16, bt64, T_delta=T_delta, recipe=recipe,
              g_dq_factor=float(rng.choice([1.0, 0.5])))
+
+
+def test_append_dequant_page_api_stacked_cache(K, orc):
+    """the page-style wrapper on a stacked 5-D cache ([pages, 2, ...] for the
+    codes and the scales, "HND"), against the oracle"""
+    s = Step(9900, W.HND, 16, 2, 64, 5, True)
+    P = s.cache.k_data.shape[0]
+    rng = np.random.default_rng(9901)
+    codes = torch.from_numpy(rng.integers(0, 256, (P, 2, 2, 16, 32), dtype=np.uint8)).cuda()
+    sf = torch.from_numpy(rng.integers(0, 0x7E, (P, 2, 2, 16, 4), dtype=np.uint8)).cuda()
+    host = W.make_cache(np.random.default_rng(0), P, 16, 2, 64, W.HND, fill="zero")
+    host.k_data[...] = codes[:, 0].reshape(P, -1).cpu().numpy()
+    host.v_data[...] = codes[:, 1].reshape(P, -1).cpu().numpy()
+    host.k_sf[...] = sf[:, 0].reshape(P, -1).cpu().numpy()
+    host.v_sf[...] = sf[:, 1].reshape(P, -1).cpu().numpy()
+    s.cache = host
+    bt = s.table(False)
+    T = int(s.new_len.max()) + 2
+    wk, wv = expected(orc, s, host, orc.STANDARD, (0.02, 0.003), (0.02, 0.003), T, True, bt)
+    ok = torch.full((5, T, 2, 64), W.SENTINEL_16 - 65536, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ov = ok.clone()
+    K.nvfp4_append_dequantize_paged(bits_tensor(s.nk, True), bits_tensor(s.nv, True), i32(s.bi), i32(s.pos), codes, sf,
+                                    i32(s.indices), i32(s.indptr), i32(s.last), 0.02, 0.003,
+                                    torch.from_numpy(bt).cuda(), i32(s.new_len), torch.tensor([0.02], device="cuda"),
+                                    torch.tensor([0.003], device="cuda"), ok, ov, kv_layout="HND")
+    torch.cuda.synchronize()
+    assert np.array_equal(codes[:, 0].reshape(P, -1).cpu().numpy(), host.k_data)
+    assert np.array_equal(codes[:, 1].reshape(P, -1).cpu().numpy(), host.v_data)
+    assert np.array_equal(sf[:, 0].reshape(P, -1).cpu().numpy(), host.k_sf)
+    assert np.array_equal(sf[:, 1].reshape(P, -1).cpu().numpy(), host.v_sf)
+    assert np.array_equal(tensor_bits(ok), wk) and np.array_equal(tensor_bits(ov), wv)
