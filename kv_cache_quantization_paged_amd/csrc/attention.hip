@@ -1160,13 +1160,15 @@ hipError_t launch_decode_attention(const kvfp4_paged_cache_t &c, const void *q, 
     if (bh == 0)
         return hipSuccess;
     const int D = c.head_dim;
-    // HND pools whose scale rows are 4-byte aligned read their scales as dwords
+    // pools whose scale rows are 4-byte aligned read their scales as dwords
     const bool sf_dw = ((uintptr_t)c.k_sf | (uintptr_t)c.v_sf | (uint64_t)c.k_sf_page_stride |
                         (uint64_t)c.v_sf_page_stride) % 4 == 0;
-    const int loader = c.page_size % 16 != 0  ? kAnyPage
-                       : c.layout == KVFP4_NHD ? kStaged
-                       : sf_dw                 ? kDirectDw
-                                               : kDirect;
+    // (NHD pools at head_dim 128 take the LDS-staged loader; at other head
+    // dims they read directly, with dword scale loads when aligned)
+    const int loader = c.page_size % 16 != 0            ? kAnyPage
+                       : c.layout == KVFP4_NHD && D == kD ? kStaged
+                       : sf_dw                            ? kDirectDw
+                                                          : kDirect;
     const split_fn kernel = D == 64    ? split_kernel_of<64>(bf16, loader)
                             : D == 256 ? split_kernel_of<256>(bf16, loader)
                                        : split_kernel_of<128>(bf16, loader);

@@ -105,14 +105,17 @@ def test_attention_parity(K, orc, layout, bf16, G):
     run_case(K, orc, zlib.crc32(repr((layout, bf16, G)).encode()), layout, 16, 2, G, lens, bf16)
 
 
-@pytest.mark.parametrize("D,sf_pad", [(128, 2), (128, 4), (64, 1), (64, 4), (256, 4)])
+@pytest.mark.parametrize("D,sf_pad", [(128, 2), (128, 4), (64, 1), (64, 4), (256, 4), (256, 8)])
 @pytest.mark.parametrize("bf16", [True, False])
-def test_attention_scale_page_alignment(K, orc, D, sf_pad, bf16):
-    """HND pools read their scales as aligned dwords when every scale page
-    starts 4-byte aligned, and byte by byte otherwise (a page stride 1 or 2
-    past a multiple of 4): both must give the same attention"""
-    seed = 690 + sf_pad + bf16 + (0 if D == 128 else D)
-    run_case(K, orc, seed, W.HND, 16, 2, 4, [1, 31, 300, 77], bf16, sf_pad=sf_pad, D=D)
+@pytest.mark.parametrize("layout", [W.HND, W.NHD])
+def test_attention_scale_page_alignment(K, orc, D, sf_pad, bf16, layout):
+    """pools read directly (HND at every head_dim, NHD at head_dim 64 and
+    256; NHD at 128 is staged through LDS) take their scales as aligned
+    dwords when every scale page starts 4-byte aligned, and byte by byte
+    otherwise (a page stride 1 or 2 past a multiple of 4): all must give the
+    same attention"""
+    seed = 690 + sf_pad + bf16 + (0 if D == 128 else D) + 7 * layout
+    run_case(K, orc, seed, layout, 16, 2, 4, [1, 31, 300, 77], bf16, sf_pad=sf_pad, D=D)
 
 
 @pytest.mark.parametrize("ps", [1, 5, 8, 32, 64])
