@@ -1046,7 +1046,7 @@ def host_cost_leg(env, reps_n=5, calls=40):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps before each timed run (the clocks and page tables settle within a few ms)")
     ap.add_argument("--leg-iters", type=int, default=50)
